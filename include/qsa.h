@@ -1,0 +1,239 @@
+/*
+ * qsa.h -- C ABI of libqsa, a QSA (Qwen Sparse Attention) layer step on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * One QSA layer step (sources: ariera, Qiita series part 10, sections
+ * "QSAとQSA indexerについて", "incremental pooled-key cache（COMMON-004）",
+ * "selected QSA K/V gather（COMMON-005）" and "block-domain top-k（COMMON-006）
+ * 実装は見送り"; devotd.net news on the llama.cpp CDNA sparse path, sections 2-3):
+ *   1. append the new token's indexer key; every completed 4-token block gets a
+ *      pooled summary: mean of its 4 keys -> RMS norm per head -> RoPE at the
+ *      block position -> binary16 row of the pooled-key cache;
+ *   2. score the query against every complete block;
+ *   3. keep the top-k blocks (ties to the lower block id) plus the incomplete
+ *      tail block;
+ *   4. gather the K/V of those cells;
+ *   5. attention over those cells only.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller unless the name ends in
+ *    _host.  binary16 data are passed as uint16_t (IEEE 754 binary16 bits).
+ *  - Layouts are dense, row-major, token-major:
+ *      k_raw   [cap_tokens][h_idx][d_idx]        raw indexer keys
+ *      k_pool  [cap_tokens/4][h_idx][d_idx]      pooled-key cache
+ *      k_cache [cap_tokens][hkv][d]              attention keys
+ *      v_cache [cap_tokens][hkv][dv]             attention values
+ *      q_idx   [n_q][h_idx][d_idx], q [n_q][hq][d], out [n_q][hq][dv] (fp32)
+ *    Every pointer must be 16-byte aligned.
+ *  - Token positions: a context of N tokens holds positions 0..N-1; block b
+ *    holds tokens 4b..4b+3 and is complete once 4b+3 < N.  nb = floor(N/4)
+ *    complete blocks; the tail is N mod 4 tokens; a decode step attends over
+ *    4*min(k, nb) + (N mod 4) cells, a number the host can compute.
+ *  - No entry point allocates device memory.  Scratch memory comes from a
+ *    caller workspace of qsa_workspace_size() bytes that qsa_workspace_init()
+ *    has cleared once; every call leaves the workspace cleared again.  Calls that
+ *    share one workspace must not overlap in time (same stream, or synchronised).
+ *  - Every call enqueues its kernels on `stream` and returns without waiting.
+ *    Arguments are checked on the host first; on a bad argument nothing is
+ *    enqueued and a negative status is returned.  After QSA_ERR_HIP the
+ *    workspace content is undefined: call qsa_workspace_init() again.
+ *  - qsa_last_error() returns a message for the calling thread's last failure.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_OK 0
+#define QSA_ERR_INVALID -1      /* bad shape, size, null or misaligned pointer */
+#define QSA_ERR_CAPACITY -2     /* position beyond cap_tokens, workspace too small */
+#define QSA_ERR_UNSUPPORTED -3  /* shape outside what the kernels implement, or the
+                                   list-attention preconditions fail */
+#define QSA_ERR_HIP -4          /* the HIP runtime reported an error */
+
+/* Decode-step flags. */
+#define QSA_STEP_FUSED_GATHER 0u    /* attention reads the chosen cells from the caches */
+#define QSA_STEP_COMPACT_GATHER 1u  /* copy chosen K/V to a compact buffer first, then
+                                       attend over it (the COMMON-005 arrangement) */
+
+/* A hipStream_t; NULL is the null stream. */
+typedef void *qsa_stream_t;
+
+/* Shape and constants of one QSA layer. */
+typedef struct qsa_config {
+    int32_t h_idx;       /* indexer heads (16)                                   */
+    int32_t d_idx;       /* indexer head dim (128); h_idx*d_idx/8 in {16..512},
+                            power of two; d_idx/8 a power of two <= 64            */
+    int32_t block;       /* tokens per pooled block; must be 4                   */
+    int32_t topk_blocks; /* k, blocks kept (512 = 2048 tokens / 4); 1..1024      */
+    int32_t hq;          /* attention query heads (32)                           */
+    int32_t hkv;         /* attention KV heads (4); hq/hkv in {1,2,4,8,16}       */
+    int32_t d;           /* attention key/query head dim (128)                   */
+    int32_t dv;          /* attention value head dim (128)                       */
+    int32_t cap_tokens;  /* capacity of the caches in tokens; multiple of 4,
+                            at most 2^21                                          */
+    float rope_base;     /* RoPE base (1e4)                                      */
+    float rms_eps;       /* RMS-norm epsilon, added to the mean square (1e-6)    */
+    float attn_scale;    /* softmax scale (1/sqrt(d))                            */
+} qsa_config;
+
+/* Caller-owned per-layer state (see the layouts above). */
+typedef struct qsa_layer_bufs {
+    uint16_t *k_raw;
+    uint16_t *k_pool;
+    uint16_t *k_cache;
+    uint16_t *v_cache;
+    const float *rms_w; /* [d_idx] RMS-norm weight, or NULL for all ones */
+} qsa_layer_bufs;
+
+/* Text for a status code. */
+const char *qsa_status_string(int status);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char *qsa_last_error(void);
+
+/* QSA_OK if cfg describes a shape the kernels implement. */
+int qsa_config_check(const qsa_config *cfg);
+
+/*
+ * Workspace bytes for calls with up to n_q query rows over contexts of up to
+ * n_ctx tokens (n_ctx <= cap_tokens).  Returns 0 for an invalid cfg.
+ */
+size_t qsa_workspace_size(const qsa_config *cfg, int32_t n_q, int32_t n_ctx);
+
+/* Clears a workspace (a fill kernel on `stream`).  Needed once after allocation. */
+int qsa_workspace_init(void *ws, size_t ws_bytes, qsa_stream_t stream);
+
+/*
+ * Pooled-key cache append (Qiita part 10, "QSAとQSA indexerについて" and
+ * "incremental pooled-key cache（COMMON-004）").  Copies k_new [n_new][h_idx][d_idx]
+ * to k_raw rows [n_before, n_before+n_new) and writes the pooled row of every
+ * block that completes in that range: mean of the block's 4 raw keys, RMS norm
+ * per head over d_idx (eps inside the root, times rms_w), RoPE (pair i with
+ * i+d_idx/2, angle 4b * rope_base^(-2i/d_idx)), rounded to binary16.  Other pooled
+ * rows are untouched, so one call with n_before = 0 rebuilds the whole cache and
+ * token-by-token calls give the same bits.
+ * Errors: INVALID (null, n_new < 0, n_before < 0), CAPACITY (n_before + n_new > cap_tokens).
+ */
+int qsa_pool_append(const qsa_config *cfg, const uint16_t *k_new, int32_t n_new,
+                    int32_t n_before, uint16_t *k_raw, uint16_t *k_pool, const float *rms_w,
+                    qsa_stream_t stream);
+
+/* Copies k_new/v_new [n_new][hkv][d|dv] to cache rows [n_before, n_before+n_new). */
+int qsa_kv_append(const qsa_config *cfg, const uint16_t *k_new, const uint16_t *v_new,
+                  int32_t n_new, int32_t n_before, uint16_t *k_cache, uint16_t *v_cache,
+                  qsa_stream_t stream);
+
+/*
+ * Block scores (Qiita part 10, "QSAとQSA indexerについて": the pooled summaries
+ * are scored against the query).  Query row r sits at position pos0 + r and sees
+ * nb_r = floor((pos0 + r + 1) / 4) blocks; scores[r*ld + b] for b < nb_r is
+ * sum over h, i of q_idx[r][h][i] * k_pool[b][h][i], accumulated in fp32.
+ * Entries b >= nb_r are left unspecified.  ld >= nb of the last row.
+ * n_q == 1 streams the pooled cache once (decode); n_q > 1 runs an MFMA
+ * contraction (prefill chunk).
+ */
+int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, int32_t pos0,
+                    const uint16_t *k_pool, float *scores, int32_t ld, qsa_stream_t stream);
+
+/*
+ * Top-k blocks per row (Qiita part 10, "QSAとQSA indexerについて" and the
+ * COMMON-006 section: selection in the block domain).  Row r keeps
+ * n_sel[r] = min(k, nb_r) blocks: the highest fp32 scores, equal scores to the
+ * lower block id, -0 equal to +0, NaN lowest.  blk[r*k ..] receives the chosen
+ * ids in ascending order.  Deterministic: the result depends only on the scores.
+ */
+int qsa_topk_blocks(const qsa_config *cfg, const float *scores, int32_t n_q, int32_t ld,
+                    int32_t pos0, int32_t *blk, int32_t *n_sel, void *ws, size_t ws_bytes,
+                    qsa_stream_t stream);
+
+/*
+ * Compact K/V gather for one decode query (Qiita part 10, "selected QSA K/V
+ * gather（COMMON-005）").  For n_tokens visible tokens and blk[0..n_blk) the chosen
+ * blocks, writes k_sel/v_sel rows: the 4 cells of each chosen block in order,
+ * then the tail tokens [4*floor(n_tokens/4), n_tokens).  Rows written:
+ * 4*n_blk + n_tokens mod 4.  n_blk must equal min(k, floor(n_tokens/4)).
+ */
+int qsa_gather_kv(const qsa_config *cfg, const int32_t *blk, int32_t n_blk, int32_t n_tokens,
+                  const uint16_t *k_cache, const uint16_t *v_cache, uint16_t *k_sel,
+                  uint16_t *v_sel, qsa_stream_t stream);
+
+/*
+ * Attention of one decode query over n_cells compact rows (Qiita part 10,
+ * COMMON-005: ordinary attention over the gathered cells).  out[h][j] =
+ * sum_c softmax_c(attn_scale * <q[h], k_sel[c][g]>) v_sel[c][g][j] with
+ * g = h / (hq/hkv).  Split over cells, fp32 partials, one combining pass.
+ */
+int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint16_t *k_sel,
+                    const uint16_t *v_sel, int32_t n_cells, float *out, void *ws,
+                    size_t ws_bytes, qsa_stream_t stream);
+
+/*
+ * Attention of a chunk of n_q query rows (row r at position pos0 + r), each over
+ * its own cells: the blocks blk[r*ldb .. + n_sel_r) (n_sel_r = min(k, nb_r)) and its
+ * tail, read directly from the caches.  The caches must already hold every token
+ * up to pos0 + n_q - 1.
+ */
+int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int32_t pos0,
+                     const int32_t *blk, int32_t ldb, const uint16_t *k_cache,
+                     const uint16_t *v_cache, float *out, void *ws, size_t ws_bytes,
+                     qsa_stream_t stream);
+
+/*
+ * One decode step of one layer: steps 1-5 above for the token at position
+ * n_before (the context grows to N = n_before + 1).  Appends k_idx_new [h_idx][d_idx]
+ * to the indexer caches and k_new/v_new [hkv][d|dv] to the K/V caches, then
+ * scores, selects and attends; out [hq][dv] fp32.  Optional outputs (NULL to
+ * skip): scores_out [floor(N/4)] fp32 block scores, blk_out [k] chosen blocks.
+ * flags: QSA_STEP_FUSED_GATHER or QSA_STEP_COMPACT_GATHER.
+ */
+int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
+                    const uint16_t *q_idx, const uint16_t *k_idx_new, const uint16_t *q,
+                    const uint16_t *k_new, const uint16_t *v_new, float *out, float *scores_out,
+                    int32_t *blk_out, uint32_t flags, void *ws, size_t ws_bytes,
+                    qsa_stream_t stream);
+
+/*
+ * One prefill chunk of one layer: appends n_new tokens at positions
+ * [n_before, n_before + n_new) to all four caches, then every chunk row runs
+ * steps 2-5 causally (row r sees N_r = n_before + r + 1 tokens).
+ * q_idx [n_new][h_idx][d_idx], q [n_new][hq][d], out [n_new][hq][dv].
+ * Optional outputs: scores_out [n_new][ld_scores], blk_out [n_new][k].
+ */
+int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
+                     int32_t n_new, const uint16_t *q_idx, const uint16_t *k_idx_new,
+                     const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, float *out,
+                     float *scores_out, int32_t ld_scores, int32_t *blk_out, void *ws,
+                     size_t ws_bytes, qsa_stream_t stream);
+
+/*
+ * MLA-style list attention (devotd.net news on the llama.cpp CDNA sparse path,
+ * sections 2-3).  mask [n] is additive binary16: -inf hides a position, any other
+ * value is added to its logit.  The visible positions are listed in ascending
+ * order (one 64-bit ballot per 64 positions, popcount ranks), then each of the hq
+ * query heads attends over the listed rows of one shared KV head:
+ * logit = scale * <q[h], kv[j][0:dkq]> + mask[j]; value = v[j][0:dv] if v is not
+ * NULL, else kv[j][0:dv].  q [hq][dkq], kv [n][dkq], v [n][dv], out [hq][dv] fp32.
+ * list_out [list_cap] (optional) and n_list [1] (device) receive the list and its
+ * length.  Preconditions (else QSA_ERR_UNSUPPORTED): mask != NULL, n >= 4096,
+ * n >= 2*list_cap, dkq == 576, dv == 512, hq in {1, 2, 4, 8, 16}.  If more
+ * than list_cap positions are visible, n_list receives the true count, nothing
+ * past list_cap is read and out is filled with NaN; the host learns of it by
+ * reading n_list.
+ */
+size_t qsa_mla_workspace_size(int32_t hq, int32_t dv, int32_t list_cap);
+int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const uint16_t *v,
+                        int32_t dkq, int32_t dv, const uint16_t *mask, int32_t n,
+                        int32_t list_cap, float scale, int32_t *list_out, int32_t *n_list,
+                        float *out, void *ws, size_t ws_bytes, qsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

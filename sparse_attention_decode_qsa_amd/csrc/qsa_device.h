@@ -1,0 +1,85 @@
+// Device-side helpers shared by the QSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+typedef _Float16 h16;
+typedef h16 h16x2 __attribute__((ext_vector_type(2)));
+typedef h16 h16x4 __attribute__((ext_vector_type(4)));
+typedef h16 h16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kBlockTokens = 4;
+
+// Order-preserving map of an fp32 score to uint32: a larger key is a higher
+// rank.  -0 is folded onto +0 (they tie) and NaN maps to 0, below every number.
+__device__ __forceinline__ uint32_t score_key(float s)
+{
+    uint32_t u = __float_as_uint(s);
+    if (s != s)
+        return 0u;
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float dot8(h16x8 a, h16x8 b, float acc)
+{
+    acc = __builtin_amdgcn_fdot2(h16x2{a[0], a[1]}, h16x2{b[0], b[1]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(h16x2{a[2], a[3]}, h16x2{b[2], b[3]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(h16x2{a[4], a[5]}, h16x2{b[4], b[5]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(h16x2{a[6], a[7]}, h16x2{b[6], b[7]}, acc, false);
+    return acc;
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Rank of this lane among the set lanes of a 64-bit ballot mask.
+__device__ __forceinline__ uint32_t rank_in_mask(uint64_t mask)
+{
+    const uint32_t l = lane_id();
+    const uint64_t below = (l == 0) ? 0ull : (mask & (~0ull >> (64 - l)));
+    return (uint32_t)__popcll(below);
+}
+
+// Appends from the lanes with `want` set to a global list whose length is *cnt;
+// one atomic per wave.  Returns this lane's slot (only meaningful when want).
+__device__ __forceinline__ uint32_t wave_append_slot(bool want, uint32_t *cnt)
+{
+    const uint64_t mask = __ballot(want);
+    if (mask == 0)
+        return 0;
+    const uint32_t leader = (uint32_t)(__ffsll((unsigned long long)mask) - 1);
+    uint32_t base = 0;
+    if (lane_id() == leader)
+        base = atomicAdd(cnt, (uint32_t)__popcll(mask));
+    base = __shfl(base, leader, kWave);
+    return base + rank_in_mask(mask);
+}
+
+}  // namespace qsa

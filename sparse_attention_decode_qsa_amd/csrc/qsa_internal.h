@@ -1,0 +1,102 @@
+// Host-side launchers shared between the entry points (qsa_api.hip) and the
+// kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qsa_device.h"
+
+namespace qsa {
+
+// A contiguous copy of n16 16-byte units.
+struct CopySeg {
+    const void *src;
+    void *dst;
+    int64_t n16;
+};
+
+// ---- append (k_pool.hip) ----------------------------------------------------
+struct AppendArgs {
+    CopySeg seg[3];      // raw rows, K rows, V rows (unused entries have n16 == 0)
+    const h16 *k_new;    // new raw indexer keys, token n_before first
+    int32_t n_before;
+    h16 *k_raw;
+    h16 *k_pool;
+    const float *rms_w;
+    int32_t H, d;
+    int32_t b_lo, n_blocks;  // blocks [b_lo, b_lo + n_blocks) complete in this call
+    float eps;
+    float base;
+};
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+
+// ---- scores (k_score.hip) ---------------------------------------------------
+hipError_t launch_score_decode(const h16 *q, const h16 *pool, int32_t nb, int32_t row_elems,
+                               float *scores, hipStream_t s);
+hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h16 *pool,
+                                int32_t row_elems, float *scores, int32_t ld, hipStream_t s);
+
+// ---- top-k (k_topk.hip) -----------------------------------------------------
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kCtrlWords = 64;
+
+struct TopkWs {
+    uint32_t *ctrl;  // kCtrlWords control words (tickets, counters, threshold)
+    uint32_t *hist;  // kHistBins
+    int32_t *sure;   // up to k entries
+    uint64_t *cand;  // up to nb entries (key << 32 | id)
+};
+hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_t *blk,
+                              int32_t *n_sel, TopkWs ws, hipStream_t s);
+hipError_t launch_topk_rows(const float *scores, int32_t n_q, int32_t ld, int32_t pos0,
+                            int32_t k, int32_t *blk, int32_t *n_sel, hipStream_t s);
+int32_t topk_max_blocks();
+
+// ---- gather / attention (k_attn.hip) -----------------------------------------
+hipError_t launch_gather(const int32_t *blk, int32_t n_blk, int32_t n_tokens,
+                         const h16 *k_cache, const h16 *v_cache, int32_t k_row16,
+                         int32_t v_row16, h16 *k_sel, h16 *v_sel, hipStream_t s);
+
+enum CellMode : int32_t { kCellsCompact = 0, kCellsBlocks = 1, kCellsList = 2 };
+constexpr int kAttnChunk = 64;
+
+struct AttnArgs {
+    const h16 *q;           // [rows][hq][D]
+    const h16 *kbase;       // token-major K rows
+    const h16 *vbase;       // token-major V rows
+    int64_t k_tok;          // elements per token row of K (hkv * D, or dkq for MLA)
+    int64_t v_tok;          // elements per token row of V
+    int32_t hq, hkv;
+    int32_t mode;
+    int32_t n_cells;        // compact: rows of k_sel/v_sel
+    const int32_t *blk;     // blocks: [rows][ldb] (NULL: every block, in order)
+    int32_t ldb;
+    int32_t pos0;           // blocks: row r sees pos0 + r + 1 tokens
+    int32_t topk;
+    const int32_t *list;    // list: token of cell c
+    const int32_t *n_list;  // list: device count
+    int32_t list_cap;
+    const h16 *bias;        // list: additive per-token mask (NULL: none)
+    float scale;
+    int32_t splits;         // work groups per (row, kv head)
+    int32_t chunks;         // chunks of kAttnChunk cells per work group
+    float *part;            // [rows][hq][splits][dv + 2] when splits > 1
+    uint32_t *tickets;      // [rows][hkv] when splits > 1
+    float *out;             // [rows][hq][dv]
+    int32_t rows;
+    int32_t tok_bound;      // list: tokens must be < tok_bound (the mask length)
+};
+hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s);
+
+// ---- MLA list (k_mla.hip) ---------------------------------------------------
+constexpr int kListSeg = 4096;  // positions per list-building work group
+hipError_t launch_mask_list(const h16 *mask, int32_t n, int32_t list_cap, uint32_t *seg_cnt,
+                            int32_t *list, int32_t *n_list, hipStream_t s);
+
+// ---- misc -------------------------------------------------------------------
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace qsa

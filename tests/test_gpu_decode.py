@@ -1,0 +1,278 @@
+"""GPU parity of the decode path against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_decode_qsa_amd import binding as qb
+from sparse_attention_decode_qsa_amd import synth
+from _helpers import (SCORE_ABS_REL, SCORE_REL, assert_attn_close, assert_pool_close, cfg_of,
+                      dev, host, setup_decode, shape_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def small(n_tokens, **kw):
+    base = dict(h_idx=16, d_idx=128, topk=512, hq=32, hkv=4, d=128, dv=128)
+    base.update(kw)
+    return synth.Workload(f"small_{n_tokens}", 7, "decode", n_tokens, **base)
+
+
+# ------------------------------------------------------------------ a1 pool append
+@pytest.mark.parametrize("H,d,n", [(16, 128, 4 * 700 + 3), (4, 64, 4 * 1000 + 1), (1, 128, 77),
+                                   (32, 64, 130), (8, 256, 41)])
+def test_pool_append_matches_oracle(gpu, H, d, n):
+    cfg = qb.Config(h_idx=H, d_idx=d, topk_blocks=8, hq=8, hkv=1, d=128, dv=128,
+                    cap_tokens=((n + 8) // 4) * 4)
+    raw = synth.normal_f16(11, (n, H, d))
+    w = torch.linspace(0.5, 1.5, d, dtype=torch.float32)
+    for rms in (None, w):
+        g = qb.Layer(cfg, rms_w=rms)
+        qb.qsa_pool_append(cfg, dev(raw), 0, g.k_raw, g.k_pool, g.rms_w)
+        ref = O.pool_rebuild(raw, n, w=None if rms is None else rms.numpy())
+        got = host(g.k_pool[:n // 4])
+        assert_pool_close(got, ref)
+        assert np.array_equal(host(g.k_raw[:n]).view(np.uint16), raw.view(np.uint16))
+        assert not host(g.k_pool[n // 4:]).any()  # incomplete block untouched
+
+
+def test_incremental_append_is_bitwise_chunk_append(gpu):
+    H, d, n = 16, 128, 4 * 300 + 2
+    cfg = qb.Config(h_idx=H, d_idx=d, cap_tokens=1216)
+    raw = synth.normal_f16(12, (n, H, d))
+    a = qb.Layer(cfg)
+    qb.qsa_pool_append(cfg, dev(raw), 0, a.k_raw, a.k_pool)
+    b = qb.Layer(cfg)
+    for t in range(n):
+        qb.qsa_pool_append(cfg, dev(raw[t:t + 1]), t, b.k_raw, b.k_pool)
+    c = qb.Layer(cfg)
+    r = np.random.default_rng(3)
+    t = 0
+    while t < n:
+        k = int(min(n - t, r.integers(1, 23)))
+        qb.qsa_pool_append(cfg, dev(raw[t:t + k]), t, c.k_raw, c.k_pool)
+        t += k
+    pa = host(a.k_pool).view(np.uint16)
+    assert np.array_equal(pa, host(b.k_pool).view(np.uint16))
+    assert np.array_equal(pa, host(c.k_pool).view(np.uint16))
+
+
+# ------------------------------------------------------------------ a2 scores
+@pytest.mark.parametrize("H,d,nb", [(16, 128, 3001), (4, 64, 1024), (16, 128, 1), (2, 64, 333),
+                                    (8, 128, 2047), (32, 128, 100)])
+def test_index_score_decode(gpu, H, d, nb):
+    cfg = qb.Config(h_idx=H, d_idx=d, cap_tokens=4 * nb + 64)
+    P = synth.normal_f16(20, (nb, H, d))
+    q = synth.normal_f16(21, (H, d))
+    pool = torch.zeros((cfg.cap_tokens // 4, H, d), dtype=torch.float16, device="cuda")
+    pool[:nb] = dev(P)
+    s = torch.full((nb + 7,), 12345.0, device="cuda")
+    qb.qsa_index_score(cfg, dev(q), 4 * nb + 2, pool, s, ld=nb + 7)
+    got = host(s)
+    s64, _ = O.index_score(q, P, nb)
+    bound = SCORE_ABS_REL * (np.abs(P.astype(np.float64).reshape(nb, -1)) @
+                             np.abs(q.astype(np.float64).ravel()))
+    assert np.all(np.abs(got[:nb] - s64) <= bound)
+    assert np.all(got[nb:] == 12345.0)  # nothing written past the complete blocks
+
+
+# ------------------------------------------------------------------ a3 top-k (decode form)
+def run_topk_decode(scores, k):
+    nb = scores.size
+    cfg = qb.Config(topk_blocks=k, cap_tokens=4 * nb + 64)
+    ws = qb.workspace(cfg, 1, 4 * nb + 3)
+    blk = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # the row at position 4*nb + 2 sees exactly nb complete blocks
+    qb.qsa_topk_blocks(cfg, dev(scores.astype(np.float32)), 1, nb, 4 * nb + 2, blk, nsel, ws)
+    n = int(host(nsel)[0])
+    return host(blk)[:n], n, ws
+
+
+def crafted(nb, kind, r):
+    if kind == "normal":
+        return r.standard_normal(nb).astype(np.float32) * 45
+    if kind == "all_equal":
+        return np.full(nb, 3.25, np.float32)
+    if kind == "few_values":
+        return r.integers(-3, 4, nb).astype(np.float32)
+    if kind == "zeros_signed":
+        s = np.zeros(nb, np.float32)
+        s[r.random(nb) < 0.5] = -0.0
+        s[r.random(nb) < 0.01] = 1.0
+        return s
+    if kind == "nan_inf":
+        s = r.standard_normal(nb).astype(np.float32)
+        s[r.random(nb) < 0.05] = np.nan
+        s[r.random(nb) < 0.01] = np.inf
+        s[r.random(nb) < 0.01] = -np.inf
+        return s
+    if kind == "tie_at_cut":
+        s = r.standard_normal(nb).astype(np.float32)
+        order = np.argsort(-s)
+        s[order[500:530]] = s[order[505]]
+        return s
+    if kind == "narrow":   # everything in one 12-bit bin: candidate path overflows LDS
+        return (1.0 + r.random(nb).astype(np.float32) * 1e-3).astype(np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "all_equal", "few_values", "zeros_signed", "nan_inf",
+                                  "tie_at_cut", "narrow"])
+@pytest.mark.parametrize("nb", [513, 5000, 63795])
+def test_topk_decode_bit_exact(gpu, kind, nb):
+    r = np.random.default_rng(nb + len(kind))
+    s = crafted(nb, kind, r)
+    got, n, ws = run_topk_decode(s, 512)
+    assert n == 512
+    assert np.array_equal(got, O.topk_sort(s, 512))
+    # the workspace is left cleared
+    assert not host(ws[:256 + 16384]).any()
+
+
+@pytest.mark.parametrize("nb,k", [(1, 512), (512, 512), (511, 512), (0, 4), (100, 99), (100, 1)])
+def test_topk_decode_small_and_edges(gpu, nb, k):
+    r = np.random.default_rng(nb * 7 + k)
+    s = r.standard_normal(max(nb, 1)).astype(np.float32)[:nb]
+    if nb == 0:
+        cfg = qb.Config(topk_blocks=k, cap_tokens=64)
+        ws = qb.workspace(cfg, 1, 3)
+        blk = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+        nsel = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        qb.qsa_topk_blocks(cfg, torch.zeros(4, device="cuda"), 1, 4, 2, blk, nsel, ws)
+        assert int(host(nsel)[0]) == 0
+        return
+    got, n, _ = run_topk_decode(s, k)
+    assert n == min(k, nb)
+    assert np.array_equal(got, O.topk_sort(s, k))
+
+
+def test_topk_decode_repeated_calls_share_workspace(gpu):
+    r = np.random.default_rng(5)
+    nb = 20000
+    cfg = qb.Config(topk_blocks=512, cap_tokens=4 * nb + 64)
+    ws = qb.workspace(cfg, 1, 4 * nb + 3)
+    blk = torch.zeros(512, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(6):
+        s = crafted(nb, ["normal", "few_values", "narrow"][i % 3], r)
+        qb.qsa_topk_blocks(cfg, dev(s), 1, nb, 4 * nb + 2, blk, nsel, ws)
+        assert np.array_equal(host(blk), O.topk_sort(s, 512))
+
+
+# ------------------------------------------------------------------ a4 gather + a5 attention
+@pytest.mark.parametrize("n_tokens", [4 * 3000 + 1, 4 * 3000 + 3, 4 * 3000, 4 * 100 + 2, 3])
+def test_gather_and_sparse_attn(gpu, n_tokens):
+    w = small(n_tokens)
+    cfg = cfg_of(w)
+    r = np.random.default_rng(n_tokens)
+    K = synth.normal_f16(30, (n_tokens, 4, 128))
+    V = synth.normal_f16(31, (n_tokens, 4, 128))
+    q = synth.normal_f16(32, (32, 128))
+    nb = n_tokens // 4
+    nsel = min(512, nb)
+    blk = np.sort(r.choice(nb, nsel, replace=False)).astype(np.int32) if nb else \
+        np.zeros(0, np.int32)
+    cells = O.cells(blk, n_tokens)
+    kc, vc = dev(K), dev(V)
+    ks = torch.zeros((2051, 4, 128), dtype=torch.float16, device="cuda")
+    vs = torch.zeros_like(ks)
+    qb.qsa_gather_kv(cfg, dev(blk) if nsel else torch.zeros(1, dtype=torch.int32, device="cuda"),
+                     nsel, n_tokens, kc, vc, ks, vs)
+    nc = cells.size
+    assert np.array_equal(host(ks[:nc]).view(np.uint16), K[cells].view(np.uint16))
+    assert np.array_equal(host(vs[:nc]).view(np.uint16), V[cells].view(np.uint16))
+    ws = qb.workspace(cfg, 1, n_tokens)
+    out = torch.empty((32, 128), device="cuda")
+    qb.qsa_sparse_attn(cfg, dev(q), ks, vs, nc, out, ws)
+    ref = O.attn_cells(q, K, V, cells, w.scale)
+    assert_attn_close(host(out), ref)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 1, 128), (16, 16, 64), (16, 1, 64), (4, 2, 128),
+                                      (32, 2, 128)])
+def test_sparse_attn_head_layouts(gpu, hq, hkv, d):
+    cfg = qb.Config(h_idx=16, d_idx=128, topk_blocks=64, hq=hq, hkv=hkv, d=d, dv=d,
+                    cap_tokens=1024)
+    nc = 4 * 64 + 3
+    K = synth.normal_f16(40, (nc, hkv, d))
+    V = synth.normal_f16(41, (nc, hkv, d))
+    q = synth.normal_f16(42, (hq, d))
+    ws = qb.workspace(cfg, 1, 1000)
+    out = torch.empty((hq, d), device="cuda")
+    qb.qsa_sparse_attn(cfg, dev(q), dev(K), dev(V), nc, out, ws)
+    ref = O.attn_cells(q, K, V, np.arange(nc), 1 / np.sqrt(d))
+    assert_attn_close(host(out), ref)
+
+
+# ------------------------------------------------------------------ a6 decode step
+def check_step(w, L, cfg, g, o, n_before, step, flags):
+    nb = (n_before + 1) // 4
+    out = torch.empty((w.hq, w.dv), device="cuda")
+    scores = torch.empty(max(nb, 1), device="cuda")
+    blk = torch.full((w.topk,), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, 1, w.cap_tokens)
+    qb.qsa_decode_step(cfg, g, n_before, dev(L["q_idx"]), dev(L["k_idx_new"][step]), dev(L["q"]),
+                       dev(L["k_new"][step]), dev(L["v_new"][step]), out, ws, scores_out=scores,
+                       blk_out=blk, flags=flags)
+    ref = O.decode_step(shape_of(w), o.raw, o.pooled, o.k, o.v, n_before, L["q_idx"],
+                        L["k_idx_new"][step], L["q"], L["k_new"][step], L["v_new"][step])
+    s_gpu = host(scores)[:nb]
+    if nb:
+        assert np.max(np.abs(s_gpu - ref["scores64"])) <= SCORE_REL * np.max(np.abs(ref["scores64"]))
+    nsel = min(w.topk, nb)
+    b_gpu = host(blk)[:nsel]
+    assert np.array_equal(b_gpu, O.topk_sort(s_gpu, w.topk))
+    # end to end: blocks that differ from the oracle's own choice sit at the cut
+    diff = set(b_gpu.tolist()) ^ set(ref["blk"].tolist())
+    if diff and nb > w.topk:
+        kth = np.sort(ref["scores64"])[::-1][w.topk - 1]
+        for b in diff:
+            assert abs(ref["scores64"][b] - kth) <= SCORE_REL * np.max(np.abs(ref["scores64"]))
+    cells = O.cells(b_gpu, n_before + 1)
+    ref_out = O.attn_cells(L["q"], o.k, o.v, cells, w.scale)
+    assert_attn_close(host(out), ref_out)
+    return b_gpu
+
+
+@pytest.mark.parametrize("flags", [qb.QSA_STEP_FUSED_GATHER, qb.QSA_STEP_COMPACT_GATHER])
+def test_decode_step_tiny_workload(gpu, flags):
+    w = synth.WORKLOADS["tiny_decode_4k"]
+    L, cfg, g, o = setup_decode(w)
+    check_step(w, L, cfg, g, o, L["n_prefix"], 0, flags)
+    # the step completed block 1023: the GPU's new pooled row matches the oracle's
+    assert_pool_close(host(g.k_pool[1023]), o.pooled[1023])
+
+
+@pytest.mark.parametrize("flags", [qb.QSA_STEP_FUSED_GATHER, qb.QSA_STEP_COMPACT_GATHER])
+def test_decode_step_cycle_61789(gpu, flags):
+    # the 64k workload, 4 consecutive steps: tails 1, 2, 3, then a completed block
+    w = synth.WORKLOADS["decode_61789"]
+    L, cfg, g, o = setup_decode(w)
+    n0 = L["n_prefix"]
+    for step in range(4):
+        check_step(w, L, cfg, g, o, n0 + step, step, flags)
+    nb = (n0 + 4) // 4
+    assert_pool_close(host(g.k_pool[nb - 1]), o.pooled[nb - 1])
+    assert np.array_equal(host(g.k_raw[n0:n0 + 4]).view(np.uint16),
+                          L["k_idx_new"].view(np.uint16))
+
+
+def test_decode_step_small_contexts(gpu):
+    # nb <= k (full attention), N < 4 (no complete block), k = nb - 1
+    for n_tokens, k in [(1, 512), (3, 512), (4, 512), (2049, 512), (2053, 512), (401, 99)]:
+        w = small(n_tokens, topk=k)
+        L, cfg, g, o = setup_decode(w)
+        check_step(w, L, cfg, g, o, L["n_prefix"], 0, qb.QSA_STEP_FUSED_GATHER)
+
+
+def test_decode_step_255181_planted(gpu):
+    # the 256k workload, one layer: planted blocks are chosen, full parity
+    w = synth.WORKLOADS["decode_255181"]
+    L, cfg, g, o = setup_decode(w)
+    n0 = L["n_prefix"]
+    # pooled cache built by the library vs the oracle, on 2000 sampled rows
+    rows = np.sort(np.random.default_rng(1).choice(n0 // 4, 2000, replace=False))
+    assert_pool_close(host(g.k_pool[torch.from_numpy(rows).cuda()]), o.pooled[rows])
+    b = check_step(w, L, cfg, g, o, n0, 0, qb.QSA_STEP_FUSED_GATHER)
+    assert set(L["planted"].tolist()) <= set(b.tolist())
