@@ -1,0 +1,279 @@
+"""QSA layer-step benchmark on one MI355X.
+
+Default workload: decode at N = 255,181 tokens, indexer 16 x 128, top-k 512 blocks,
+attention 32/4 x 128, 12 independent layer states stepped serially per token (a
+real model chains its layers), 8 planted blocks per layer.  One bench step is one
+token: the 12 layers one after another.  The token position cycles through
+N-1, N, N+1, N+2 (tails 1, 2, 3 and a completed block), then rewinds.
+
+Reported:
+  value        layer decode steps/s (= 12 * tokens / s)
+  roofline     the decode scoring kernel (the pooled-key scan): algorithmic bytes
+               per launch / its average duration, timed live with HIP events on the
+               stream it runs on, against 8 TB/s; plus HBM traffic per launch from
+               rocprofv3 counters when they were taken on the current kernel source
+  step_hbm     algorithmic bytes of a whole layer step / measured step time
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA layer decode steps/s at 256k ctx + achieved HBM GB/s (% of peak)"
+HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_decode_qsa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, source: str):
+    """Counter-measured HBM bytes per launch, only if taken on the current source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_hash") != src_hash(source):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def decode_bytes(w, nb, cells):
+    """Algorithmic bytes of one decode layer step (see the design notes)."""
+    row = w.h_idx * w.d_idx * 2
+    scan = nb * row
+    kv = cells * w.hkv * (w.d + w.dv) * 2
+    small = (row                      # indexer query
+             + w.hq * w.d * 2         # attention query
+             + w.hq * w.dv * 4        # fp32 output
+             + row                    # raw indexer key written
+             + w.hkv * (w.d + w.dv) * 2)  # new K/V row written
+    return scan, kv, small
+
+
+def run_cpu_baseline(w, L, budget_s):
+    """The oracle's decode step on layer 0 of the same workload, single thread."""
+    import oracle as O
+    n0 = L["n_prefix"]
+    cap = w.cap_tokens
+    raw = np.zeros((cap, w.h_idx, w.d_idx), np.float16)
+    pooled = np.zeros((cap // 4, w.h_idx, w.d_idx), np.float16)
+    kc = np.zeros((cap, w.hkv, w.d), np.float16)
+    vc = np.zeros((cap, w.hkv, w.dv), np.float16)
+    t0 = time.time()
+    O.pool_append(L["raw"], 0, raw, pooled)
+    kc[:n0], vc[:n0] = L["k"], L["v"]
+    log(f"[cpu] oracle cache build {time.time() - t0:.1f}s")
+    sh = O.Shape(w.h_idx, w.d_idx, w.topk, w.hq, w.hkv, w.d, w.dv)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        j = steps % 4
+        O.decode_step(sh, raw, pooled, kc, vc, n0 + j, L["q_idx"], L["k_idx_new"][j], L["q"],
+                      L["k_new"][j], L["v_new"][j])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 64:
+            break
+    return dict(value=steps / el, unit="layer-steps/s", cores=1, kind="oracle",
+                sample=f"{steps} oracle decode steps on layer 0 at N={w.n_tokens} "
+                       f"(positions cycling N-1..N+2), single thread, {el:.1f} s")
+
+
+def bench_decode(args):
+    import torch
+    from sparse_attention_decode_qsa_amd import binding as qb
+    from sparse_attention_decode_qsa_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    n_layers = args.layers or w.n_layers
+    dev = torch.device("cuda:0")
+    qb.load()
+    cfg = qb.Config(h_idx=w.h_idx, d_idx=w.d_idx, topk_blocks=w.topk, hq=w.hq, hkv=w.hkv, d=w.d,
+                    dv=w.dv, cap_tokens=w.cap_tokens)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    layers, host0 = [], None
+    t0 = time.time()
+    for li in range(n_layers):
+        L = synth.decode_layer(w, li)
+        g = qb.Layer(cfg, dev)
+        qb.qsa_pool_append(cfg, t(L["raw"]), 0, g.k_raw, g.k_pool)
+        g.k_cache[:L["n_prefix"]] = t(L["k"])
+        g.v_cache[:L["n_prefix"]] = t(L["v"])
+        st = dict(layer=g, q_idx=t(L["q_idx"]), q=t(L["q"]), k_idx_new=t(L["k_idx_new"]),
+                  k_new=t(L["k_new"]), v_new=t(L["v_new"]),
+                  out=torch.empty((w.hq, w.dv), dtype=torch.float32, device=dev))
+        layers.append(st)
+        if li == 0:
+            host0 = L
+        torch.cuda.synchronize()
+        log(f"[setup] layer {li} ready ({time.time() - t0:.1f}s)")
+    n0 = host0["n_prefix"]
+    ws = qb.workspace(cfg, 1, w.cap_tokens, dev)
+    flags = qb.QSA_STEP_COMPACT_GATHER if args.compact_gather else qb.QSA_STEP_FUSED_GATHER
+
+    def token(j):
+        for st in layers:
+            qb.qsa_decode_step(cfg, st["layer"], n0 + j, st["q_idx"], st["k_idx_new"][j], st["q"],
+                               st["k_new"][j], st["v_new"][j], st["out"], ws, flags=flags)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for j in range(4):
+            token(j)          # eager: also sets kernel attributes before any capture
+    stream.synchronize()
+
+    graphs = []
+    if not args.eager:
+        for j in range(4):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                token(j)
+            graphs.append(gr)
+        stream.synchronize()
+
+    def run_tokens(i0, n):
+        with torch.cuda.stream(stream):
+            for i in range(i0, i0 + n):
+                if graphs:
+                    graphs[i % 4].replay()
+                else:
+                    token(i % 4)
+
+    run_tokens(0, args.warmup)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run_tokens(args.warmup, args.steps)
+    e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    tok_s = args.steps / (ms / 1e3)
+    layer_steps_s = tok_s * n_layers
+    log(f"[time] {args.steps} tokens x {n_layers} layers in {ms:.2f} ms")
+
+    # dominant kernel: the pooled-key scan, timed alone on the same stream
+    nb = w.n_tokens // 4
+    scores = torch.empty(nb + 64, dtype=torch.float32, device=dev)
+    reps = 12 * max(1, args.kernel_reps // 12)
+    with torch.cuda.stream(stream):
+        for r in range(12):
+            st = layers[r % n_layers]
+            qb.qsa_index_score(cfg, st["q_idx"], w.n_tokens - 1, st["layer"].k_pool, scores)
+        k0 = torch.cuda.Event(enable_timing=True)
+        k1 = torch.cuda.Event(enable_timing=True)
+        k0.record(stream)
+        for r in range(reps):
+            st = layers[r % n_layers]
+            qb.qsa_index_score(cfg, st["q_idx"], w.n_tokens - 1, st["layer"].k_pool, scores)
+        k1.record(stream)
+    k1.synchronize()
+    kern_us = k0.elapsed_time(k1) * 1e3 / reps
+    row = w.h_idx * w.d_idx * 2
+    scan_bytes = nb * row
+    achieved = scan_bytes / (kern_us * 1e-6) / 1e9
+    traffic = traffic_for("score_decode_kernel", "k_score.hip")
+
+    # whole-step algorithmic bandwidth, averaged over the 4-step position cycle
+    per = []
+    for j in range(4):
+        N = w.n_tokens + j
+        nbj = N // 4
+        cells = 4 * min(w.topk, nbj) + N % 4
+        per.append(sum(decode_bytes(w, nbj, cells)))
+    step_bytes = float(np.mean(per))
+    step_s = (ms / 1e3) / (args.steps * n_layers)
+    step_gbps = step_bytes / step_s / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(layer_steps_s, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "n_tokens": w.n_tokens, "layers_per_token": n_layers,
+            "indexer": f"{w.h_idx}x{w.d_idx}", "topk_blocks": w.topk,
+            "attention": f"{w.hq}/{w.hkv}x{w.d}", "planted_blocks": w.planted,
+            "step": "one token = all layers, serially; position cycles N-1..N+2",
+            "launch": "eager" if args.eager else "hip graph per token",
+            "gather": "compact" if args.compact_gather else "fused",
+            "token_steps_per_s": round(tok_s, 2),
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "score_decode_kernel",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": scan_bytes,
+            "avg_launch_us": round(kern_us, 3),
+        },
+        "step_hbm": {
+            "algorithmic_bytes_per_layer_step": int(step_bytes),
+            "achieved": round(step_gbps, 1), "unit": "GB/s",
+            "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+            "us_per_layer_step": round(step_s * 1e6, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = run_cpu_baseline(w, host0, args.cpu_budget)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_255181",
+                    choices=["decode_255181", "decode_61789", "tiny_decode_4k"])
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count")
+    ap.add_argument("--eager", action="store_true", help="launch per call instead of graphs")
+    ap.add_argument("--compact-gather", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=240)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("this build runs on one GPU only: the QSA layer step has no multi-GPU path here "
+              "(see the sharding notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    res = bench_decode(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

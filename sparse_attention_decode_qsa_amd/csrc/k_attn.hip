@@ -42,38 +42,73 @@ struct VecH<8> {
 
 __device__ __forceinline__ float h2f(h16 x) { return (float)x; }
 
+// Cell c of row `row` -> token, or -1 (past the row's cells, or a dropped id).
+struct CellMap {
+    int32_t mode, count, nsel, nbr, tok_bound;
+    const int32_t *blkr;
+    const int32_t *list;
+
+    __device__ __forceinline__ int32_t operator()(int32_t c) const
+    {
+        if (c >= count)
+            return -1;
+        if (mode == kCellsCompact)
+            return c;
+        if (mode == kCellsBlocks) {
+            if (c < kBlockTokens * nsel) {
+                const int32_t b = blkr ? blkr[c / kBlockTokens] : c / kBlockTokens;
+                // an id outside [0, nb) can only come from a broken selection: drop
+                // the cell rather than read outside the cache
+                return ((uint32_t)b < (uint32_t)nbr) ? kBlockTokens * b + (c & 3) : -1;
+            }
+            return kBlockTokens * nbr + (c - kBlockTokens * nsel);
+        }
+        const int32_t j = list[c];
+        return ((uint32_t)j < (uint32_t)tok_bound) ? j : -1;
+    }
+};
+
 template <int G, int D, int DV>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
 {
-    constexpr int HPW = G >= 4 ? G / 4 : 1;  // query heads per wave in PV
-    constexpr int DPL = DV / kWave;          // value dims per lane
-    constexpr int QV = D / 32;               // 16-byte K pieces per lane (a quarter row)
-    static_assert(D % 32 == 0 && DV % kWave == 0, "shape");
+    constexpr int HPW = G >= 4 ? G / 4 : 1;        // query heads per wave in PV
+    constexpr int DPL = DV / kWave;                // value dims per lane in PV
+    constexpr int QV = D / 32;                     // 16-byte K pieces per lane (a quarter row)
+    constexpr int VPR = DV / 8;                    // 16-byte pieces per V row
+    constexpr int VV = kAttnChunk * VPR / kThreads;  // V pieces per thread per chunk
+    static_assert(D % 32 == 0 && DV % kWave == 0 && VV >= 1, "shape");
     typedef typename VecH<DPL>::T vtype;
 
     __shared__ __attribute__((aligned(16))) h16 qs[G * D];
+    __shared__ __attribute__((aligned(16))) h16 vs[kAttnChunk * DV];
     __shared__ float ps[G][kAttnChunk];
-    __shared__ int32_t toks[kAttnChunk];
+    __shared__ int32_t toks[2][kAttnChunk];
+    __shared__ float wts[G][kAttnMaxSplits];  // split-K merge weights, one wave per head
     __shared__ uint32_t flag;
 
     const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
 
-    int32_t count = 0, nsel = 0, nbr = 0;
+    CellMap cm;
+    cm.mode = a.mode;
+    cm.nsel = 0;
+    cm.nbr = 0;
+    cm.tok_bound = a.tok_bound;
+    cm.list = a.list;
+    cm.blkr = a.blk ? a.blk + (int64_t)row * a.ldb : nullptr;
     bool overflow = false;
     if (a.mode == kCellsCompact) {
-        count = a.n_cells;
+        cm.count = a.n_cells;
     } else if (a.mode == kCellsBlocks) {
         const int32_t N = a.pos0 + row + 1;
-        nbr = N / kBlockTokens;
-        nsel = min(a.topk, nbr);
-        count = kBlockTokens * nsel + (N - kBlockTokens * nbr);
+        cm.nbr = N / kBlockTokens;
+        cm.nsel = min(a.topk, cm.nbr);
+        cm.count = kBlockTokens * cm.nsel + (N - kBlockTokens * cm.nbr);
     } else {
         const int32_t nl = *a.n_list;
         overflow = nl > a.list_cap;
-        count = overflow ? 0 : nl;
+        cm.count = overflow ? 0 : nl;
     }
-    const int32_t *blkr = a.blk ? a.blk + (int64_t)row * a.ldb : nullptr;
 
     const h16 *qrow = a.q + ((int64_t)row * a.hq + (int64_t)g * G) * D;
     for (int i = t; i < G * D / 8; i += kThreads)
@@ -90,51 +125,65 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     }
     const float sl2 = a.scale * kLog2e;
     const int64_t kg = (int64_t)g * D, vg = (int64_t)g * DV;
+    const int cl = wave * 16 + (lane & 15);  // QK: this lane's cell in the chunk
+    const int pt = lane >> 4;                // QK: this lane's quarter of the head dim
+    const int32_t cbase = split * a.chunks * kAttnChunk;
+
+    // The first KP pieces of this lane's K quarter row and the first VP of its V
+    // pieces are loaded one chunk ahead; the rest (large head dims) when used.
+    constexpr int KP = QV < 4 ? QV : 4;
+    constexpr int VP = VV < 4 ? VV : 4;
+    h16x8 kreg[KP], vreg[VP];
+    auto kaddr = [&](int32_t tok) {
+        return a.kbase + (int64_t)max(tok, 0) * a.k_tok + kg + pt * (D / 4);
+    };
+    auto vload = [&](const int32_t *tk, int i) {
+        const int p = t + kThreads * i, c = p / VPR, pc = p - c * VPR;
+        const int32_t tv = tk[c];
+        return (tv >= 0) ? *(const h16x8 *)(a.vbase + (int64_t)tv * a.v_tok + vg + pc * 8)
+                         : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    };
+    auto issue_loads = [&](const int32_t *tk) {
+        const int32_t tok = tk[cl];
+        const h16 *kr = kaddr(tok);
+#pragma unroll
+        for (int v = 0; v < KP; v++)
+            kreg[v] = (tok >= 0) ? *(const h16x8 *)(kr + 8 * v) : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < VP; i++)
+            vreg[i] = vload(tk, i);
+    };
+
+    if (t < kAttnChunk)
+        toks[0][t] = cm(cbase + t);
+    __syncthreads();
+    issue_loads(toks[0]);
 
     for (int ch = 0; ch < a.chunks; ch++) {
-        const int32_t c0 = (split * a.chunks + ch) * kAttnChunk;
-        if (t < kAttnChunk) {
-            const int32_t c = c0 + t;
-            int32_t tok = -1;
-            if (c < count) {
-                if (a.mode == kCellsCompact) {
-                    tok = c;
-                } else if (a.mode == kCellsBlocks) {
-                    if (c < kBlockTokens * nsel) {
-                        const int32_t b = blkr ? blkr[c / kBlockTokens] : c / kBlockTokens;
-                        // an id outside [0, nb) can only come from a broken selection:
-                        // drop the cell rather than read outside the cache
-                        tok = ((uint32_t)b < (uint32_t)nbr) ? kBlockTokens * b + (c & 3) : -1;
-                    } else {
-                        tok = kBlockTokens * nbr + (c - kBlockTokens * nsel);
-                    }
-                } else {
-                    const int32_t j = a.list[c];
-                    tok = ((uint32_t)j < (uint32_t)a.tok_bound) ? j : -1;
-                }
-            }
-            toks[t] = tok;
-        }
-        __syncthreads();
+        const int cur = ch & 1;
+        const int32_t c0 = cbase + ch * kAttnChunk;
+        // ids of the next chunk: the load is issued now, the LDS store after QK
+        int32_t next_tok = -1;
+        const bool has_next = ch + 1 < a.chunks;
+        if (has_next && t < kAttnChunk)
+            next_tok = cm(c0 + kAttnChunk + t);
 
-        // ---- QK
+        // ---- QK on this lane's quarter row, reduced over the 4 quarters
         {
-            const int cl = wave * 16 + (lane & 15);
-            const int pt = lane >> 4;
-            const int32_t tok = toks[cl];
+            const int32_t tok = toks[cur][cl];
             float acc[G];
 #pragma unroll
             for (int h = 0; h < G; h++)
                 acc[h] = 0.f;
-            if (tok >= 0) {
-                const h16 *kr = a.kbase + (int64_t)tok * a.k_tok + kg + pt * (D / 4);
-#pragma unroll 2
-                for (int v = 0; v < QV; v++) {
-                    const h16x8 kv = *(const h16x8 *)(kr + 8 * v);
+            const h16 *kr = kaddr(tok);
+#pragma unroll 4
+            for (int v = 0; v < QV; v++) {
+                const h16x8 kv = (v < KP) ? kreg[v < KP ? v : 0]
+                                 : ((tok >= 0) ? *(const h16x8 *)(kr + 8 * v)
+                                               : h16x8{0, 0, 0, 0, 0, 0, 0, 0});
 #pragma unroll
-                    for (int h = 0; h < G; h++)
-                        acc[h] = dot8(*(const h16x8 *)&qs[h * D + pt * (D / 4) + 8 * v], kv, acc[h]);
-                }
+                for (int h = 0; h < G; h++)
+                    acc[h] = dot8(*(const h16x8 *)&qs[h * D + pt * (D / 4) + 8 * v], kv, acc[h]);
             }
             float bias = 0.f;
             if (a.bias && tok >= 0)
@@ -150,7 +199,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
                     ps[h][cl] = (tok >= 0) ? acc[h] * sl2 + bias : -INFINITY;
             }
         }
+#pragma unroll
+        for (int i = 0; i < VP; i++)
+            *(h16x8 *)&vs[(t + kThreads * i) * 8] = vreg[i];
+        for (int i0 = VP; i0 < VV; i0 += 4) {  // large value dims: the rest, 4 at a time
+            h16x8 tmp[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (i0 + i < VV)
+                    tmp[i] = vload(toks[cur], i0 + i);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (i0 + i < VV)
+                    *(h16x8 *)&vs[(t + kThreads * (i0 + i)) * 8] = tmp[i];
+        }
+        if (has_next && t < kAttnChunk)
+            toks[cur ^ 1][t] = next_tok;
         __syncthreads();
+        if (has_next)
+            issue_loads(toks[cur ^ 1]);
 
         // ---- online softmax update for this wave's heads
 #pragma unroll
@@ -172,15 +239,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         }
         __syncthreads();
 
-        // ---- PV
+        // ---- PV from the LDS copy of the chunk's V rows.  Cells past the end or
+        // dropped have p = 0 and zeroed V rows, so all 64 are walked unguarded and
+        // fully unrolled (the LDS reads of many cells are in flight together).
         if (wave * HPW < G) {
-            const int nvalid = max(0, min(kAttnChunk, count - c0));
-            for (int c = 0; c < nvalid; c++) {
-                const int32_t tok = toks[c];
-                if (tok < 0)
-                    continue;
-                const vtype vv = *(const vtype *)(a.vbase + (int64_t)tok * a.v_tok + vg +
-                                                  lane * DPL);
+#pragma unroll 16
+            for (int c = 0; c < kAttnChunk; c++) {
+                const vtype vv = *(const vtype *)&vs[c * DV + lane * DPL];
 #pragma unroll
                 for (int hh = 0; hh < HPW; hh++) {
                     const int h = wave * HPW + hh;
@@ -215,6 +280,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         return;
     }
 
+    // ---- split-K: write (m, l, o) partials; the last work group of (row, g) merges
     const int S = a.splits;
 #pragma unroll
     for (int hh = 0; hh < HPW; hh++) {
@@ -238,20 +304,56 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     if (!flag)
         return;
     __threadfence();
-    for (int e = t; e < G * DV; e += kThreads) {
-        const int h = e / DV, j = e - h * DV;
+    // per-head weights exp2(m_s - M) / L, one wave per group of heads
+    for (int h = wave; h < G; h += kThreads / kWave) {
         const float *pb = a.part + (hq0 + h) * S * (DV + 2);
-        float M = -INFINITY;
-        for (int s = 0; s < S; s++)
-            M = fmaxf(M, __builtin_nontemporal_load(&pb[s * (DV + 2)]));
-        float L = 0.f, O = 0.f;
-        for (int s = 0; s < S; s++) {
-            const float ms = __builtin_nontemporal_load(&pb[s * (DV + 2)]);
-            const float w = exp2f(ms - M);
-            L += w * __builtin_nontemporal_load(&pb[s * (DV + 2) + 1]);
-            O += w * __builtin_nontemporal_load(&pb[s * (DV + 2) + 2 + j]);
+        float ms = -INFINITY, ls = 0.f;
+        if (lane < S) {
+            ms = pb[lane * (DV + 2)];
+            ls = pb[lane * (DV + 2) + 1];
         }
-        a.out[(hq0 + h) * DV + j] = overflow ? NAN : O / L;
+        const float M = group_max<kWave>(ms);
+        const float w = (lane < S) ? exp2f(ms - M) : 0.f;
+        const float L = group_sum<kWave>(w * ls);
+        if (lane < S)
+            wts[h][lane] = w / L;
+    }
+    __syncthreads();
+    // out = sum_s w_s o_s; every partial this thread needs in a batch is loaded
+    // before any is used (issued one by one, their latencies would add up)
+    constexpr int OPT = (G * DV + kThreads - 1) / kThreads;  // outputs per thread
+    constexpr int SB = 8;                                     // splits per batch
+    float O[OPT];
+#pragma unroll
+    for (int i = 0; i < OPT; i++)
+        O[i] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += SB) {
+        float pv[OPT][SB];
+#pragma unroll
+        for (int i = 0; i < OPT; i++) {
+            const int e = t + kThreads * i;
+            const int h = e / DV, j = e - h * DV;
+#pragma unroll
+            for (int u = 0; u < SB; u++)
+                pv[i][u] = (e < G * DV && s0 + u < S)
+                               ? a.part[((hq0 + h) * S + s0 + u) * (DV + 2) + 2 + j]
+                               : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < OPT; i++) {
+            const int e = t + kThreads * i;
+            const int h = e < G * DV ? e / DV : 0;
+#pragma unroll
+            for (int u = 0; u < SB; u++)
+                if (s0 + u < S)
+                    O[i] += wts[h][s0 + u] * pv[i][u];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < OPT; i++) {
+        const int e = t + kThreads * i;
+        if (e < G * DV)
+            a.out[(hq0 + e / DV) * DV + (e % DV)] = overflow ? NAN : O[i];
     }
     if (t == 0)
         a.tickets[(int64_t)row * a.hkv + g] = 0;

@@ -175,11 +175,27 @@ AttnArgs attn_base(const qsa_config *c)
     return a;
 }
 
+// Splits of a cell range for split-K attention: each work group walks
+// kAttnChunksPerSplit 64-cell chunks (the next chunk's loads overlap the current
+// chunk's math), more if that would exceed kAttnMaxSplits work groups per
+// (row, KV head).  Fewer splits keep the final merge small.
+void split_plan(int32_t cells, int32_t *splits, int32_t *chunks)
+{
+    const int32_t nch = cells > 0 ? (cells + kAttnChunk - 1) / kAttnChunk : 1;
+    int32_t c = kAttnChunksPerSplit;
+    const int32_t cmin = (nch + kAttnMaxSplits - 1) / kAttnMaxSplits;
+    if (c < cmin)
+        c = cmin;
+    if (c > nch)
+        c = nch;
+    *chunks = c;
+    *splits = (nch + c - 1) / c;
+}
+
 int attn_decode_launch(const qsa_config *c, AttnArgs a, int32_t cells, void *ws, const Layout &L,
                        hipStream_t s)
 {
-    a.splits = cells > 0 ? (cells + kAttnChunk - 1) / kAttnChunk : 1;
-    a.chunks = 1;
+    split_plan(cells, &a.splits, &a.chunks);
     a.part = at<float>(ws, L.part);
     a.tickets = at<uint32_t>(ws, L.tickets);
     HIP_CHECK(launch_attn(a, c->d, c->dv, s));
@@ -680,8 +696,7 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
     a.list_cap = list_cap;
     a.bias = H(mask);
     a.scale = scale;
-    a.splits = (list_cap + kAttnChunk - 1) / kAttnChunk;
-    a.chunks = 1;
+    split_plan(list_cap, &a.splits, &a.chunks);
     a.part = part;
     a.tickets = ticket;
     a.out = out;

@@ -62,6 +62,8 @@ hipError_t launch_gather(const int32_t *blk, int32_t n_blk, int32_t n_tokens,
 
 enum CellMode : int32_t { kCellsCompact = 0, kCellsBlocks = 1, kCellsList = 2 };
 constexpr int kAttnChunk = 64;
+constexpr int kAttnMaxSplits = 64;
+constexpr int kAttnChunksPerSplit = 4;
 
 struct AttnArgs {
     const h16 *q;           // [rows][hq][D]

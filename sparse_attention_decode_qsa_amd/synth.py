@@ -97,9 +97,8 @@ class Workload:
 
     @property
     def cap_tokens(self) -> int:
-        if self.kind == "prefill":
-            return self.n_tokens + self.n_q + 64
-        return self.n_tokens + 64
+        need = self.n_tokens + (self.n_q if self.kind == "prefill" else 0) + 64
+        return (need + 3) // 4 * 4
 
     @property
     def scale(self) -> float:

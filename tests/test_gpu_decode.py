@@ -119,7 +119,7 @@ def crafted(nb, kind, r):
 
 @pytest.mark.parametrize("kind", ["normal", "all_equal", "few_values", "zeros_signed", "nan_inf",
                                   "tie_at_cut", "narrow"])
-@pytest.mark.parametrize("nb", [513, 5000, 63795])
+@pytest.mark.parametrize("nb", [513, 5000, 20000, 40000, 63795, 65536, 70001])
 def test_topk_decode_bit_exact(gpu, kind, nb):
     r = np.random.default_rng(nb + len(kind))
     s = crafted(nb, kind, r)

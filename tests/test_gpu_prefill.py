@@ -1,0 +1,191 @@
+"""GPU parity of the prefill-chunk path (MFMA scoring, per-row top-k, per-row
+attention, the fused prefill step) against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_decode_qsa_amd import binding as qb
+from sparse_attention_decode_qsa_amd import synth
+from _helpers import (SCORE_ABS_REL, SCORE_REL, OracleLayer, assert_attn_close, cfg_of, dev, host,
+                      shape_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def score_bound(q_row, P, nb):
+    return SCORE_ABS_REL * (np.abs(P[:nb].astype(np.float64).reshape(nb, -1)) @
+                            np.abs(q_row.astype(np.float64).ravel()))
+
+
+def run_prefill_scores(H, d, n_q, pos0, seed, rows_to_check):
+    cap = pos0 + n_q + 64
+    cap -= cap % 4
+    cfg = qb.Config(h_idx=H, d_idx=d, cap_tokens=cap)
+    nb_max = (pos0 + n_q) // 4
+    P = synth.normal_f16(seed, (nb_max, H, d))
+    Q = synth.normal_f16(seed + 1, (n_q, H, d))
+    pool = torch.zeros((cap // 4, H, d), dtype=torch.float16, device="cuda")
+    pool[:nb_max] = dev(P)
+    ld = ((nb_max + 63) // 64) * 64
+    S = torch.full((n_q, ld), 777.0, device="cuda")
+    qb.qsa_index_score(cfg, dev(Q), pos0, pool, S, ld=ld)
+    got = host(S)
+    for r in rows_to_check:
+        nb = (pos0 + r + 1) // 4
+        s64, _ = O.index_score(Q[r], P, nb)
+        assert np.all(np.abs(got[r, :nb] - s64) <= score_bound(Q[r], P, nb)), r
+    assert np.all(got[:, nb_max:] == 777.0)
+
+
+@pytest.mark.parametrize("H,d,n_q,pos0", [(16, 128, 300, 1000), (16, 128, 257, 3), (4, 64, 100, 999),
+                                          (8, 128, 1, 5000), (16, 128, 1024, 7)])
+def test_index_score_prefill_mfma(gpu, H, d, n_q, pos0):
+    if n_q == 1:
+        pytest.skip("n_q == 1 is the decode kernel")
+    run_prefill_scores(H, d, n_q, pos0, 50, range(n_q))
+
+
+def test_index_score_prefill_mfma_full_size(gpu):
+    w = synth.WORKLOADS["prefill_1024_at_126253"]
+    r = np.random.default_rng(4)
+    rows = sorted({0, w.n_q - 1, *r.choice(w.n_q, 14, replace=False).tolist()})
+    run_prefill_scores(w.h_idx, w.d_idx, w.n_q, w.n_tokens, 60, rows)
+
+
+def crafted_row(nb, kind, r):
+    if kind == "normal":
+        return r.standard_normal(nb).astype(np.float32) * 45
+    if kind == "few_values":
+        return r.integers(-2, 3, nb).astype(np.float32)
+    if kind == "narrow":
+        return (1.0 + r.random(nb).astype(np.float32) * 1e-3).astype(np.float32)
+    if kind == "all_equal":
+        return np.full(nb, -2.5, np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "few_values", "narrow", "all_equal"])
+def test_topk_rows_bit_exact(gpu, kind):
+    # rows see growing causal prefixes; first rows have nb <= k
+    n_q, pos0, k = 64, 2030, 512
+    cfg = qb.Config(topk_blocks=k, cap_tokens=4096)
+    nb_max = (pos0 + n_q) // 4
+    ld = nb_max + 3
+    r = np.random.default_rng(len(kind))
+    S = np.stack([np.concatenate([crafted_row(nb_max, kind, r), np.zeros(3, np.float32)])
+                  for _ in range(n_q)])
+    blk = torch.full((n_q, k), -5, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros(n_q, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, n_q, pos0 + n_q)
+    qb.qsa_topk_blocks(cfg, dev(S), n_q, ld, pos0, blk, nsel, ws)
+    b, ns = host(blk), host(nsel)
+    for i in range(n_q):
+        nb = (pos0 + i + 1) // 4
+        assert ns[i] == min(k, nb)
+        assert np.array_equal(b[i, :ns[i]], O.topk_sort(S[i, :nb], k)), i
+
+
+@pytest.mark.parametrize("n_q,pos0", [(24, 127253), (6, 262150), (5, 300001)])
+def test_topk_rows_large_rows(gpu, n_q, pos0):
+    # rows of the 128k prefill size (~31.8k blocks each), and rows past the
+    # register-resident limit of 65,536 blocks
+    k = 512
+    cfg = qb.Config(topk_blocks=k, cap_tokens=(pos0 + n_q + 64) // 4 * 4)
+    nb_max = (pos0 + n_q) // 4
+    r = np.random.default_rng(9)
+    S = (r.standard_normal((n_q, nb_max)) * 45).astype(np.float32)
+    S[3] = np.round(S[3])           # many ties
+    S[min(5, n_q - 1)] = 7.0         # all equal
+    blk = torch.full((n_q, k), -5, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros(n_q, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, n_q, pos0 + n_q)
+    qb.qsa_topk_blocks(cfg, dev(S), n_q, nb_max, pos0, blk, nsel, ws)
+    b = host(blk)
+    for i in range(n_q):
+        nb = (pos0 + i + 1) // 4
+        assert np.array_equal(b[i], O.topk_sort(S[i, :nb], k)), i
+
+
+def prefill_case(w, layer=0):
+    I = synth.prefill_inputs(w, layer)
+    depth, n_q = I["depth"], w.n_q
+    cfg = cfg_of(w)
+    g = qb.Layer(cfg)
+    qb.qsa_pool_append(cfg, dev(I["raw"][:depth]), 0, g.k_raw, g.k_pool)
+    g.k_cache[:depth] = dev(I["k"][:depth])
+    g.v_cache[:depth] = dev(I["v"][:depth])
+    out = torch.empty((n_q, w.hq, w.dv), device="cuda")
+    nb_end = (depth + n_q) // 4
+    ld = ((nb_end + 1 + 63) // 64) * 64
+    scores = torch.empty((n_q, ld), device="cuda")
+    blk = torch.full((n_q, w.topk), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, n_q, depth + n_q)
+    qb.qsa_prefill_step(cfg, g, depth, dev(I["q_idx"]), dev(I["raw"][depth:]), dev(I["q"]),
+                        dev(I["k"][depth:]), dev(I["v"][depth:]), out, ws, scores_out=scores,
+                        ld_scores=ld, blk_out=blk)
+    return I, cfg, g, host(out), host(scores), host(blk)
+
+
+def check_prefill_rows(w, I, g, out, scores, blk, rows, oracle_pooled=None):
+    depth = I["depth"]
+    n_all = depth + w.n_q
+    pooled_gpu = host(g.k_pool[:n_all // 4])
+    for r in rows:
+        pos = depth + r
+        nb = (pos + 1) // 4
+        nsel = min(w.topk, nb)
+        s_gpu = scores[r, :nb]
+        # scores against the oracle on the GPU's pooled rows (tight)
+        s64, _ = O.index_score(I["q_idx"][r], pooled_gpu, nb)
+        assert np.all(np.abs(s_gpu - s64) <= score_bound(I["q_idx"][r], pooled_gpu, nb)), r
+        if oracle_pooled is not None:
+            s_or, _ = O.index_score(I["q_idx"][r], oracle_pooled, nb)
+            assert np.max(np.abs(s_gpu - s_or)) <= SCORE_REL * np.max(np.abs(s_or)), r
+        b = blk[r, :nsel]
+        assert np.array_equal(b, O.topk_sort(s_gpu, w.topk)), r
+        cells = O.cells(b, pos + 1)
+        ref = O.attn_cells(I["q"][r], I["k"], I["v"], cells, w.scale)
+        assert_attn_close(out[r], ref, f"row {r}")
+
+
+def test_prefill_step_small(gpu):
+    w = synth.Workload("prefill_small", 6, "prefill", 4 * 700 + 1, n_q=300)
+    I, cfg, g, out, scores, blk = prefill_case(w)
+    depth = I["depth"]
+    n_all = depth + w.n_q
+    oracle_pooled = O.pool_rebuild(I["raw"], n_all)
+    check_prefill_rows(w, I, g, out, scores, blk, range(w.n_q), oracle_pooled)
+    # the chunk's raw/K/V rows landed in the caches
+    assert np.array_equal(host(g.k_raw[depth:n_all]).view(np.uint16),
+                          I["raw"][depth:].view(np.uint16))
+    assert np.array_equal(host(g.v_cache[depth:n_all]).view(np.uint16),
+                          I["v"][depth:].view(np.uint16))
+
+
+def test_prefill_step_is_decode_per_row(gpu):
+    # a chunk row equals a decode step at that length (small chunk, every row)
+    w = synth.Workload("prefill_vs_decode", 6, "prefill", 4 * 600 + 2, n_q=9, topk=64)
+    I, cfg, g, out, scores, blk = prefill_case(w)
+    depth = I["depth"]
+    for r in range(w.n_q):
+        o = OracleLayer(w, w.cap_tokens)
+        O.pool_append(I["raw"][:depth + r], 0, o.raw, o.pooled)
+        o.k[:depth + r], o.v[:depth + r] = I["k"][:depth + r], I["v"][:depth + r]
+        ref = O.decode_step(shape_of(w), o.raw, o.pooled, o.k, o.v, depth + r, I["q_idx"][r],
+                            I["raw"][depth + r], I["q"][r], I["k"][depth + r], I["v"][depth + r])
+        nb = (depth + r + 1) // 4
+        diff = set(blk[r, :min(w.topk, nb)].tolist()) ^ set(ref["blk"].tolist())
+        kth = np.sort(ref["scores64"])[::-1][w.topk - 1]
+        for b in diff:
+            assert abs(ref["scores64"][b] - kth) <= SCORE_REL * np.max(np.abs(ref["scores64"]))
+        if not diff:
+            assert_attn_close(out[r], ref["out"], f"row {r}")
+
+
+def test_prefill_step_full_size_sampled(gpu):
+    w = synth.WORKLOADS["prefill_1024_at_126253"]
+    I, cfg, g, out, scores, blk = prefill_case(w)
+    r = np.random.default_rng(8)
+    rows = sorted({0, 1, w.n_q - 1, *r.choice(w.n_q, 9, replace=False).tolist()})
+    check_prefill_rows(w, I, g, out, scores, blk, rows)
