@@ -11,8 +11,8 @@
 //     query heads held in LDS, and reduce across the quarters;
 //   * PV: each wave owns G/4 query heads; a lane owns DV/64 value dims and walks
 //     the chunk's cells, reading each V row once per wave, coalesced.
-// With several splits, each writes (m, l, o) partials; the last work group of a
-// (row, g) to finish (an atomic ticket) merges them and resets the ticket.
+// With several splits, each writes (m, l, o) partials and attn_combine_kernel (a
+// second launch; the kernel boundary makes the partials visible) merges them.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -71,20 +71,20 @@ struct CellMap {
 template <int G, int D, int DV>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
 {
-    constexpr int HPW = G >= 4 ? G / 4 : 1;        // query heads per wave in PV
-    constexpr int DPL = DV / kWave;                // value dims per lane in PV
-    constexpr int QV = D / 32;                     // 16-byte K pieces per lane (a quarter row)
-    constexpr int VPR = DV / 8;                    // 16-byte pieces per V row
+    constexpr int HPW = G >= 4 ? G / 4 : 1;          // query heads per wave (softmax, PV)
+    constexpr int DPL = DV / kWave;                  // value dims per lane in PV
+    constexpr int QV = D / 32;                       // 16-byte K pieces per lane (a quarter row)
+    constexpr int VPR = DV / 8;                      // 16-byte pieces per V row
     constexpr int VV = kAttnChunk * VPR / kThreads;  // V pieces per thread per chunk
+    constexpr int KP = QV < 4 ? QV : 4;              // K pieces loaded a chunk ahead
+    constexpr int VP = VV < 4 ? VV : 4;              // V pieces loaded a chunk ahead
     static_assert(D % 32 == 0 && DV % kWave == 0 && VV >= 1, "shape");
     typedef typename VecH<DPL>::T vtype;
 
     __shared__ __attribute__((aligned(16))) h16 qs[G * D];
     __shared__ __attribute__((aligned(16))) h16 vs[kAttnChunk * DV];
-    __shared__ float ps[G][kAttnChunk];
+    __shared__ __attribute__((aligned(16))) float ps[G][kAttnChunk];
     __shared__ int32_t toks[2][kAttnChunk];
-    __shared__ float wts[G][kAttnMaxSplits];  // split-K merge weights, one wave per head
-    __shared__ uint32_t flag;
 
     const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
@@ -125,14 +125,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     }
     const float sl2 = a.scale * kLog2e;
     const int64_t kg = (int64_t)g * D, vg = (int64_t)g * DV;
-    const int cl = wave * 16 + (lane & 15);  // QK: this lane's cell in the chunk
-    const int pt = lane >> 4;                // QK: this lane's quarter of the head dim
+    // QK: wave w takes cells 16w .. 16w+15 of the chunk; the 4 lanes of a quad
+    // split one cell's head dim in quarters, so their partial dots meet in-quad
+    const int cl = wave * 16 + (lane >> 2);
+    const int pt = lane & 3;
     const int32_t cbase = split * a.chunks * kAttnChunk;
 
-    // The first KP pieces of this lane's K quarter row and the first VP of its V
-    // pieces are loaded one chunk ahead; the rest (large head dims) when used.
-    constexpr int KP = QV < 4 ? QV : 4;
-    constexpr int VP = VV < 4 ? VV : 4;
     h16x8 kreg[KP], vreg[VP];
     auto kaddr = [&](int32_t tok) {
         return a.kbase + (int64_t)max(tok, 0) * a.k_tok + kg + pt * (D / 4);
@@ -168,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         if (has_next && t < kAttnChunk)
             next_tok = cm(c0 + kAttnChunk + t);
 
-        // ---- QK on this lane's quarter row, reduced over the 4 quarters
+        // ---- QK
         {
             const int32_t tok = toks[cur][cl];
             float acc[G];
@@ -189,10 +187,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
             if (a.bias && tok >= 0)
                 bias = h2f(a.bias[tok]) * kLog2e;
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                acc[h] += __shfl_xor(acc[h], 16, kWave);
-                acc[h] += __shfl_xor(acc[h], 32, kWave);
-            }
+            for (int h = 0; h < G; h++)
+                acc[h] = quad_sum(acc[h]);
             if (pt == 0) {
 #pragma unroll
                 for (int h = 0; h < G; h++)
@@ -219,18 +215,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         if (has_next)
             issue_loads(toks[cur ^ 1]);
 
-        // ---- online softmax update for this wave's heads
+        // ---- online softmax update for this wave's heads (lane = cell)
 #pragma unroll
         for (int hh = 0; hh < HPW; hh++) {
             const int h = wave * HPW + hh;
             if (h < G) {
                 const float s = ps[h][lane];
-                const float cmax = group_max<kWave>(s);
-                const float mnew = fmaxf(m_run[hh], cmax);
+                const float mnew = fmaxf(m_run[hh], wave_max(s));
                 const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run[hh] - mnew);
                 const float p = (s == -INFINITY) ? 0.f : exp2f(s - mnew);
                 ps[h][lane] = p;
-                l_run[hh] = l_run[hh] * alpha + group_sum<kWave>(p);
+                l_run[hh] = l_run[hh] * alpha + wave_sum(p);
                 m_run[hh] = mnew;
 #pragma unroll
                 for (int j = 0; j < DPL; j++)
@@ -240,17 +235,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         __syncthreads();
 
         // ---- PV from the LDS copy of the chunk's V rows.  Cells past the end or
-        // dropped have p = 0 and zeroed V rows, so all 64 are walked unguarded and
-        // fully unrolled (the LDS reads of many cells are in flight together).
+        // dropped have p = 0 and zeroed V rows, so all 64 are walked unguarded.
         if (wave * HPW < G) {
-#pragma unroll 16
-            for (int c = 0; c < kAttnChunk; c++) {
-                const vtype vv = *(const vtype *)&vs[c * DV + lane * DPL];
+#pragma unroll 4
+            for (int c4 = 0; c4 < kAttnChunk; c4 += 4) {
+                f32x4 p4[HPW];
 #pragma unroll
-                for (int hh = 0; hh < HPW; hh++) {
-                    const int h = wave * HPW + hh;
-                    if (h < G) {
-                        const float p = ps[h][c];
+                for (int hh = 0; hh < HPW; hh++)
+                    p4[hh] = *(const f32x4 *)&ps[min(wave * HPW + hh, G - 1)][c4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const vtype vv = *(const vtype *)&vs[(c4 + u) * DV + lane * DPL];
+#pragma unroll
+                    for (int hh = 0; hh < HPW; hh++) {
+                        const float p = p4[hh][u];
                         if constexpr (DPL == 1) {
                             o[hh][0] += p * h2f(vv);
                         } else {
@@ -266,97 +264,63 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     }
 
     const int64_t hq0 = (int64_t)row * a.hq + (int64_t)g * G;
-    if (a.splits == 1) {
-#pragma unroll
-        for (int hh = 0; hh < HPW; hh++) {
-            const int h = wave * HPW + hh;
-            if (h < G) {
-                const float inv = 1.f / l_run[hh];
-#pragma unroll
-                for (int j = 0; j < DPL; j++)
-                    a.out[(hq0 + h) * DV + lane * DPL + j] = overflow ? NAN : o[hh][j] * inv;
-            }
-        }
-        return;
-    }
-
-    // ---- split-K: write (m, l, o) partials; the last work group of (row, g) merges
-    const int S = a.splits;
 #pragma unroll
     for (int hh = 0; hh < HPW; hh++) {
         const int h = wave * HPW + hh;
         if (h < G) {
-            float *pb = a.part + ((hq0 + h) * S + split) * (DV + 2);
-            if (lane == 0) {
-                pb[0] = m_run[hh];
-                pb[1] = l_run[hh];
+            if (a.splits == 1) {
+                const float inv = 1.f / l_run[hh];
+#pragma unroll
+                for (int j = 0; j < DPL; j++)
+                    a.out[(hq0 + h) * DV + lane * DPL + j] = overflow ? NAN : o[hh][j] * inv;
+            } else {
+                // split-K partial (m, l, o); attn_combine_kernel merges them
+                float *pb = a.part + ((hq0 + h) * a.splits + split) * (DV + 2);
+                if (lane == 0) {
+                    pb[0] = m_run[hh];
+                    pb[1] = l_run[hh];
+                }
+#pragma unroll
+                for (int j = 0; j < DPL; j++)
+                    pb[2 + lane * DPL + j] = o[hh][j];
             }
-#pragma unroll
-            for (int j = 0; j < DPL; j++)
-                pb[2 + lane * DPL + j] = o[hh][j];
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (t == 0)
-        flag = (atomicAdd(&a.tickets[(int64_t)row * a.hkv + g], 1u) == (uint32_t)(S - 1)) ? 1u : 0u;
-    __syncthreads();
-    if (!flag)
-        return;
-    __threadfence();
-    // per-head weights exp2(m_s - M) / L, one wave per group of heads
-    for (int h = wave; h < G; h += kThreads / kWave) {
-        const float *pb = a.part + (hq0 + h) * S * (DV + 2);
-        float ms = -INFINITY, ls = 0.f;
-        if (lane < S) {
-            ms = pb[lane * (DV + 2)];
-            ls = pb[lane * (DV + 2) + 1];
-        }
-        const float M = group_max<kWave>(ms);
-        const float w = (lane < S) ? exp2f(ms - M) : 0.f;
-        const float L = group_sum<kWave>(w * ls);
-        if (lane < S)
-            wts[h][lane] = w / L;
+}
+
+// Merge of split-K partials: one work group per (query head, row), one output
+// dim per thread.  Every thread loads all S (m, l, o_j) it needs in one round
+// (the (m, l) pairs are the same for all threads of the group) and forms
+// out_j = sum_s exp2(m_s - M) o_sj / sum_s exp2(m_s - M) l_s.
+template <int DV>
+__global__ __launch_bounds__(DV) void attn_combine_kernel(const float *__restrict__ part,
+                                                          int32_t hq, int32_t S,
+                                                          const int32_t *n_list, int32_t list_cap,
+                                                          float *__restrict__ out)
+{
+    const int h = blockIdx.x, row = blockIdx.y, j = threadIdx.x;
+    const float *pb = part + ((int64_t)row * hq + h) * S * (DV + 2);
+    const bool overflow = n_list && *n_list > list_cap;
+    float m[kAttnMaxSplits], l[kAttnMaxSplits], o[kAttnMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kAttnMaxSplits; s++) {
+        const bool ok = s < S;
+        m[s] = ok ? pb[s * (DV + 2)] : -INFINITY;
+        l[s] = ok ? pb[s * (DV + 2) + 1] : 0.f;
+        o[s] = ok ? pb[s * (DV + 2) + 2 + j] : 0.f;
     }
-    __syncthreads();
-    // out = sum_s w_s o_s; every partial this thread needs in a batch is loaded
-    // before any is used (issued one by one, their latencies would add up)
-    constexpr int OPT = (G * DV + kThreads - 1) / kThreads;  // outputs per thread
-    constexpr int SB = 8;                                     // splits per batch
-    float O[OPT];
+    float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < OPT; i++)
-        O[i] = 0.f;
-    for (int s0 = 0; s0 < S; s0 += SB) {
-        float pv[OPT][SB];
+    for (int s = 0; s < kAttnMaxSplits; s++)
+        M = fmaxf(M, m[s]);
+    float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int i = 0; i < OPT; i++) {
-            const int e = t + kThreads * i;
-            const int h = e / DV, j = e - h * DV;
-#pragma unroll
-            for (int u = 0; u < SB; u++)
-                pv[i][u] = (e < G * DV && s0 + u < S)
-                               ? a.part[((hq0 + h) * S + s0 + u) * (DV + 2) + 2 + j]
-                               : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < OPT; i++) {
-            const int e = t + kThreads * i;
-            const int h = e < G * DV ? e / DV : 0;
-#pragma unroll
-            for (int u = 0; u < SB; u++)
-                if (s0 + u < S)
-                    O[i] += wts[h][s0 + u] * pv[i][u];
-        }
+    for (int s = 0; s < kAttnMaxSplits; s++) {
+        const float w = (s < S) ? exp2f(m[s] - M) : 0.f;
+        L += w * l[s];
+        O += w * o[s];
     }
-#pragma unroll
-    for (int i = 0; i < OPT; i++) {
-        const int e = t + kThreads * i;
-        if (e < G * DV)
-            a.out[(hq0 + e / DV) * DV + (e % DV)] = overflow ? NAN : O[i];
-    }
-    if (t == 0)
-        a.tickets[(int64_t)row * a.hkv + g] = 0;
+    out[((int64_t)row * hq + h) * DV + j] = overflow ? NAN : O / L;
 }
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restrict__ blk,
@@ -400,6 +364,12 @@ hipError_t launch_g(const AttnArgs &a, int G, hipStream_t s)
     case 16: hipLaunchKernelGGL((attn_kernel<16, D, DV>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1)
+        return e;
+    hipLaunchKernelGGL((attn_combine_kernel<DV>), dim3((uint32_t)a.hq, (uint32_t)a.rows),
+                       dim3(DV), 0, s, a.part, a.hq, a.splits,
+                       a.mode == kCellsList ? a.n_list : nullptr, a.list_cap, a.out);
     return hipGetLastError();
 }
 
@@ -408,6 +378,8 @@ hipError_t launch_g(const AttnArgs &a, int G, hipStream_t s)
 hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s)
 {
     const int G = a.hq / a.hkv;
+    if (a.splits > kAttnMaxSplits)
+        return hipErrorInvalidValue;
     if (D == 128 && DV == 128)
         return launch_g<128, 128>(a, G, s);
     if (D == 64 && DV == 64)

@@ -30,16 +30,16 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kCandCap = 4096;
 constexpr int kMaxBlocks = 1 << 19;  // bitmap of 64 KiB in LDS
-constexpr int kDecodePerWg = 512;
 
 // control words in TopkWs::ctrl
-enum : int { kTicketA = 0, kTicketB = 1, kSureCnt = 2, kCandCnt = 3, kBin = 4, kAbove = 5 };
+enum : int { kCandCnt = 3 };
 
 template <int NT>
 struct Scratch {
     uint32_t tmp[NT];
     uint32_t res[4];
     uint32_t cnt;
+    uint32_t cnt2;
     uint32_t flag;
 };
 
@@ -281,6 +281,7 @@ __device__ void zero_words(uint32_t *p, uint32_t n)
 // read once and nothing leaves the work group.  Used for rows of up to 1024*KPT
 // blocks (65,536 at KPT = 64, i.e. contexts up to 262,147 tokens).
 constexpr int kRegThreads = 1024;
+constexpr int kListCap = 4096;  // keys in bins >= the lower bound, kept in LDS
 
 template <int KPT>
 __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__restrict__ scores,
@@ -292,6 +293,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
     constexpr int V4 = KPT / 4;
     __shared__ uint32_t hist[kHistBins];
     __shared__ uint64_t cand[kCandCap];
+    __shared__ uint32_t lst[kListCap];
     __shared__ uint32_t bitmap[NT * KPT / 32];
     __shared__ Scratch<NT> S;
 
@@ -343,35 +345,86 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
         const uint32_t k16 = (j & 1) ? (w >> 16) : (w & 0xffffu);
         return k16 >> (16 - kHistBits);
     };
-    // 1. a lower bound L on the threshold bin from every 16th key: the bin where
-    //    the sample reaches about twice its expected share of k
-    for (int i = t; i < kHistBins; i += NT)
-        hist[i] = 0;
-    if (t == 0)
-        S.cnt = 0;
-    __syncthreads();
+    // 1. A lower bound L on the threshold bin: the k-th largest of the per-thread
+    //    maximum bins.  The k threads at or above it each hold a key in a bin
+    //    >= L, so at least k keys lie in bins >= L (k <= 1024 = NT).
+    uint32_t mybin = 0;
     {
         const int tt = fresh_t();
 #pragma unroll
-        for (int j = 0; j < KPT; j += 16)
-            if ((uint32_t)(4 * ((j / 4) * NT + tt)) < nb)
-                atomicAdd(&hist[bin_of(j)], 1u);
+        for (int j = 0; j < KPT; j++)
+            if ((uint32_t)(4 * ((j / 4) * NT + tt) + j % 4) < nb)
+                mybin = max(mybin, bin_of(j));
+    }
+    for (int i = t; i < kHistBins; i += NT)
+        hist[i] = 0;
+    if (t == 0) {
+        S.cnt = 0;
+        S.cnt2 = 0;
     }
     __syncthreads();
-    find_from_top<NT>(hist, kHistBins, (uint32_t)(k / 8 + 16), S);
-    uint32_t L = S.res[0] == 0xffffffffu ? 0u : S.res[0];
+    atomicAdd(&hist[mybin], 1u);
     __syncthreads();
-    // 2. exact histogram of the keys in bins >= L; if they are fewer than k, the
-    //    bound was too high: redo it over every key
-    for (int pass = 0; pass < 2; pass++) {
-        // opaque keys: keeps the 64 bin values from being hoisted out of the
-        // loop into registers of their own
+    find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
+    const uint32_t L = S.res[0];
+    __syncthreads();
+    // 2. The keys in bins >= L (a few per cent of the row) go to a short LDS list
+    //    (16 key bits, 16 id bits).  Each thread counts its own first, so a wave
+    //    reserves its slots with one LDS atomic instead of one per key.
+    uint32_t mine = 0;
+    {
 #pragma unroll
         for (int j = 0; j < KPT / 2; j++)
             asm volatile("" : "+v"(kp[j]));
-        for (int i = t; i < kHistBins; i += NT)
-            hist[i] = 0;
-        __syncthreads();
+        const int tt = fresh_t();
+#pragma unroll
+        for (int j = 0; j < KPT; j++)
+            mine += ((uint32_t)(4 * ((j / 4) * NT + tt) + j % 4) < nb && bin_of(j) >= L) ? 1u : 0u;
+    }
+    {
+        uint32_t incl = mine;  // inclusive scan over the wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t u = __shfl_up(incl, o, kWave);
+            if ((t & (kWave - 1)) >= o)
+                incl += u;
+        }
+        uint32_t base = 0;
+        if ((t & (kWave - 1)) == kWave - 1 && incl)
+            base = atomicAdd(&S.cnt, incl);
+        base = __shfl(base, kWave - 1, kWave) + incl - mine;
+        if (mine) {
+#pragma unroll
+            for (int j = 0; j < KPT / 2; j++)
+                asm volatile("" : "+v"(kp[j]));
+            const int tt = fresh_t();
+#pragma unroll
+            for (int j = 0; j < KPT; j++) {
+                const uint32_t id = (uint32_t)(4 * ((j / 4) * NT + tt) + j % 4);
+                if (id < nb && bin_of(j) >= L) {
+                    if (base < (uint32_t)kListCap) {
+                        const uint32_t w = kp[j >> 1];
+                        const uint32_t k16 = (j & 1) ? (w >> 16) : (w & 0xffffu);
+                        lst[base] = (k16 << 16) | id;
+                    }
+                    base++;
+                }
+            }
+        }
+    }
+    for (int i = t; i < kHistBins; i += NT)
+        hist[i] = 0;
+    __syncthreads();
+    const uint32_t n_list = S.cnt;
+    const bool short_list = n_list <= (uint32_t)kListCap;
+    if (short_list) {
+        for (uint32_t i = t; i < n_list; i += NT)
+            atomicAdd(&hist[lst[i] >> (32 - kHistBits)], 1u);
+    } else {
+        // long list (flat score distributions): histogram of every key >= L
+#pragma unroll
+        for (int j = 0; j < KPT / 2; j++)
+            asm volatile("" : "+v"(kp[j]));
         const int tt = fresh_t();
 #pragma unroll
         for (int j = 0; j < KPT; j++) {
@@ -379,21 +432,67 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
             if ((uint32_t)(4 * ((j / 4) * NT + tt) + j % 4) < nb && bin >= L)
                 atomicAdd(&hist[bin], 1u);
         }
-        __syncthreads();
-        find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
-        if (S.res[0] != 0xffffffffu || L == 0)
-            break;
-        L = 0;
-        __syncthreads();
     }
+    __syncthreads();
+    find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
     const uint32_t B = S.res[0];
-    const uint32_t need = (uint32_t)k - S.res[1];
+    uint32_t need = (uint32_t)k - S.res[1];
     const uint32_t W = (nb + 31) / 32;
     for (uint32_t i = t; i < W; i += NT)
         bitmap[i] = 0;
+    for (int i = t; i < 16; i += NT)  // hist[0..15] becomes a digit histogram
+        hist[i] = 0;
+    if (t == 0)
+        S.cnt2 = 0;
     __syncthreads();
-    // 3. bins above B are in; ids of bin B become candidates
-    {
+    if (short_list) {
+        // 3. Bins above B are in.  Bin B's entries are split once more by the next
+        //    4 key bits, which the list already holds.
+        for (uint32_t i = t; i < n_list; i += NT) {
+            const uint32_t e = lst[i];
+            const uint32_t bin = e >> (32 - kHistBits);
+            if (bin > B) {
+                set_bit(bitmap, e & 0xffffu);
+            } else if (bin == B) {
+                atomicAdd(&hist[(e >> 16) & 15u], 1u);
+            }
+        }
+        __syncthreads();
+        // digit d where the count from the top reaches need (16 bins: one lane scan)
+        if (t == 0) {
+            uint32_t acc = 0, d = 0;
+            for (int b = 15; b >= 0; b--) {
+                if (acc + hist[b] >= need) {
+                    d = (uint32_t)b;
+                    break;
+                }
+                acc += hist[b];
+            }
+            S.res[0] = d;
+            S.res[1] = acc;
+            S.cnt = 0;
+        }
+        __syncthreads();
+        const uint32_t d = S.res[0];
+        need -= S.res[1];
+        for (uint32_t i = t; i < n_list; i += NT) {
+            const uint32_t e = lst[i];
+            if ((e >> (32 - kHistBits)) != B)
+                continue;
+            const uint32_t dig = (e >> 16) & 15u;
+            if (dig > d) {
+                set_bit(bitmap, e & 0xffffu);
+            } else if (dig == d) {
+                const uint32_t slot = atomicAdd(&S.cnt, 1u);
+                if (slot < kCandCap)
+                    cand[slot] = e & 0xffffu;
+            }
+        }
+    } else {
+        // long list: walk every register-held key
+        if (t == 0)
+            S.cnt = 0;
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < KPT / 2; j++)
             asm volatile("" : "+v"(kp[j]));
@@ -424,10 +523,9 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
     if (c <= (uint32_t)NT) {
         // 4a. rank by counting: order (key desc, id asc) is strict, so candidate i
         //     is chosen iff fewer than `need` candidates rank before it
-        // pad to a multiple of 16 with entries that never rank before anyone
         const uint32_t c16 = (c + 15) & ~15u;
         if ((uint32_t)t >= c && (uint32_t)t < c16)
-            cand[t] = 0x00000000ffffffffull;
+            cand[t] = 0x00000000ffffffffull;  // never ranks before anyone
         __syncthreads();
         if ((uint32_t)t < c) {
             const uint64_t me = cand[t];
@@ -475,7 +573,62 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
 }
 
 // ---------------------------------------------------------------- rows form
-// Dynamic LDS: hist[4096] | cand[kCandCap] (u64) | bitmap[ceil(nb_max/32)]
+// Generic exact selection of one row straight from global memory (any nb up to
+// kMaxBlocks): histogram pass, candidates of the threshold bin to LDS (or
+// re-read from L2 when there are too many), digit passes, bitmap compaction.
+template <int NT>
+__device__ void select_row_global(const float *row, uint32_t nb, int32_t k, int32_t *outr,
+                                  uint32_t *hist, uint64_t *cand, uint32_t *bitmap,
+                                  Scratch<NT> &S)
+{
+    zero_words<NT>(hist, kHistBins);
+    if (threadIdx.x == 0)
+        S.cnt = 0;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < nb; i += NT)
+        atomicAdd(&hist[score_key(row[i]) >> (32 - kHistBits)], 1u);
+    __syncthreads();
+    find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
+    const uint32_t B = S.res[0];
+    const uint32_t need = (uint32_t)k - S.res[1];
+    zero_words<NT>(bitmap, (nb + 31) / 32);
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < nb; i += NT) {
+        const uint32_t key = score_key(row[i]);
+        const uint32_t bin = key >> (32 - kHistBits);
+        if (bin > B) {
+            set_bit(bitmap, i);
+        } else if (bin == B) {
+            const uint32_t slot = atomicAdd(&S.cnt, 1u);
+            if (slot < kCandCap)
+                cand[slot] = ((uint64_t)key << 32) | i;
+        }
+    }
+    __syncthreads();
+    const uint32_t c = S.cnt;
+    uint32_t *h256 = hist;  // the 12-bit histogram is no longer needed
+    if (c <= (uint32_t)kCandCap) {
+        LdsCands<NT> src{cand, c};
+        resolve<NT>(src, B, need, nb, h256, S);
+        const uint32_t T = S.res[0], I = S.res[1];
+        src.each([&](uint32_t key, uint32_t id) {
+            if (key > T || (key == T && id <= I))
+                set_bit(bitmap, id);
+        });
+    } else {
+        RowCands<NT> src{row, nb, B};
+        resolve<NT>(src, B, need, nb, h256, S);
+        const uint32_t T = S.res[0], I = S.res[1];
+        src.each([&](uint32_t key, uint32_t id) {
+            if (key > T || (key == T && id <= I))
+                set_bit(bitmap, id);
+        });
+    }
+    __syncthreads();
+    compact_bitmap<NT>(bitmap, nb, outr, (uint32_t)k, S);
+}
+
+// Dynamic LDS: cand[kCandCap] (u64) | hist[4096] | bitmap[ceil(nb_max/32)]
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__restrict__ scores,
                                                              int32_t ld, int32_t pos0, int32_t k,
                                                              int32_t *__restrict__ blk,
@@ -498,173 +651,180 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
             n_sel[r] = (int32_t)nb;
         return;
     }
-    zero_words<kThreads>(hist, kHistBins);
-    if (threadIdx.x == 0)
-        S.cnt = 0;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nb; i += kThreads)
-        atomicAdd(&hist[score_key(row[i]) >> (32 - kHistBits)], 1u);
-    __syncthreads();
-    find_from_top<kThreads>(hist, kHistBins, (uint32_t)k, S);
-    const uint32_t B = S.res[0];
-    const uint32_t need = (uint32_t)k - S.res[1];
-    zero_words<kThreads>(bitmap, (nb + 31) / 32);
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nb; i += kThreads) {
-        const uint32_t key = score_key(row[i]);
-        const uint32_t bin = key >> (32 - kHistBits);
-        if (bin > B) {
-            set_bit(bitmap, i);
-        } else if (bin == B) {
-            const uint32_t slot = atomicAdd(&S.cnt, 1u);
-            if (slot < kCandCap)
-                cand[slot] = ((uint64_t)key << 32) | i;
-        }
-    }
-    __syncthreads();
-    const uint32_t c = S.cnt;
-    uint32_t *h256 = hist;  // the 12-bit histogram is no longer needed
-    if (c <= (uint32_t)kCandCap) {
-        LdsCands<kThreads> src{cand, c};
-        resolve<kThreads>(src, B, need, nb, h256, S);
-        const uint32_t T = S.res[0], I = S.res[1];
-        src.each([&](uint32_t key, uint32_t id) {
-            if (key > T || (key == T && id <= I))
-                set_bit(bitmap, id);
-        });
-    } else {
-        RowCands<kThreads> src{row, nb, B};
-        resolve<kThreads>(src, B, need, nb, h256, S);
-        const uint32_t T = S.res[0], I = S.res[1];
-        src.each([&](uint32_t key, uint32_t id) {
-            if (key > T || (key == T && id <= I))
-                set_bit(bitmap, id);
-        });
-    }
-    __syncthreads();
-    compact_bitmap<kThreads>(bitmap, nb, outr, (uint32_t)k, S);
+    select_row_global<kThreads>(row, nb, k, outr, hist, cand, bitmap, S);
     if (threadIdx.x == 0)
         n_sel[r] = k;
 }
 
 // ---------------------------------------------------------------- decode form
-__global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float *__restrict__ scores,
-                                                             int32_t nb, int32_t k, TopkWs ws)
+// One long row spread over many CUs, two launches that meet only at the kernel
+// boundary (no fences; the only global atomics reserve list slots, one per wave
+// that has something to append):
+//   filter  every work group takes the same deterministic sample of the row
+//           (every stride-th score), finds the bin holding the r-th largest
+//           sampled key (r about 3x the sample's expected share of k), and
+//           appends each of its own keys in that bin or above to ws.cand;
+//   final   one work group selects exactly from that list: 12-bit histogram,
+//           threshold bin, one more 8-bit digit, rank counting of the last few.
+//           If the list holds fewer than k keys (the sample misled the bound) or
+//           more than fit in LDS (flat scores), it selects from the whole row.
+// The final step clears the control words it used.
+constexpr int kFilterPerWg = 1024;  // scores per filter work group (4 per thread)
+constexpr int kSample = 1024;       // sampled scores (4 per thread)
+constexpr int kFinalThreads = 1024;
+constexpr int kListMax = 4096;      // list entries the final step keeps in LDS
+
+__global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float *__restrict__ scores,
+                                                               int32_t nb, int32_t k, TopkWs ws)
 {
     __shared__ uint32_t hist[kHistBins];
     __shared__ Scratch<kThreads> S;
+    const int t = threadIdx.x;
+    const uint32_t stride = max(64u, ((uint32_t)nb + kSample - 1) / kSample);
+    const uint32_t ns = ((uint32_t)nb + stride - 1) / stride;
+    // this work group's own 4 scores per thread and 4 sampled scores per thread
+    const int32_t i0 = blockIdx.x * kFilterPerWg + 4 * t;
+    float own[4], smp[4];
+    if (i0 + 3 < nb && ((((uintptr_t)scores) & 15) == 0)) {
+        const f32x4 v = *(const f32x4 *)(scores + i0);
+        own[0] = v[0], own[1] = v[1], own[2] = v[2], own[3] = v[3];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            own[e] = (i0 + e < nb) ? scores[i0 + e] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const uint32_t j = (uint32_t)(t + kThreads * e);
+        smp[e] = (j < ns) ? scores[(size_t)j * stride] : 0.f;
+    }
     zero_words<kThreads>(hist, kHistBins);
     __syncthreads();
-    const int32_t lo = blockIdx.x * kDecodePerWg;
-    const int32_t hi = min(nb, lo + kDecodePerWg);
-    for (int32_t i = lo + threadIdx.x; i < hi; i += kThreads)
-        atomicAdd(&hist[score_key(scores[i]) >> (32 - kHistBits)], 1u);
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        if ((uint32_t)(t + kThreads * e) < ns)
+            atomicAdd(&hist[score_key(smp[e]) >> (32 - kHistBits)], 1u);
     __syncthreads();
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads)
-        if (hist[i])
-            atomicAdd(&ws.hist[i], hist[i]);
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0)
-        S.flag = (atomicAdd(&ws.ctrl[kTicketA], 1u) == gridDim.x - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!S.flag)
-        return;
-    __threadfence();
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) {
-        hist[i] = __hip_atomic_load(&ws.hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ws.hist[i] = 0;
+    // r-th largest sampled key: about 3x the sample's expected count of top-k
+    // keys, so the bound keeps ~3k keys of the row; exactness is checked later
+    const uint32_t want = (uint32_t)(((uint64_t)3 * k * ns + nb - 1) / nb) + 8;
+    find_from_top<kThreads>(hist, kHistBins, min(want, ns), S);
+    const uint32_t Lb = (S.res[0] == 0xffffffffu) ? 0u : S.res[0];
+    // slots: per-thread count, work-group scan, one global atomic per work group
+    uint32_t key[4], mine = 0;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        key[e] = score_key(own[e]);
+        mine += (i0 + e < nb && (key[e] >> (32 - kHistBits)) >= Lb) ? 1u : 0u;
+    }
+    uint32_t off = wg_exclusive_scan<kThreads>(mine, S);
+    if (t == kThreads - 1) {
+        const uint32_t total = off + mine;
+        S.res[3] = total ? atomicAdd(&ws.ctrl[kCandCnt], total) : 0u;
     }
     __syncthreads();
-    find_from_top<kThreads>(hist, kHistBins, (uint32_t)k, S);
-    if (threadIdx.x == 0) {
-        ws.ctrl[kBin] = S.res[0];
-        ws.ctrl[kAbove] = S.res[1];
-        ws.ctrl[kTicketA] = 0;
-    }
+    off += S.res[3];
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        if (i0 + e < nb && (key[e] >> (32 - kHistBits)) >= Lb)
+            ws.cand[off++] = ((uint64_t)key[e] << 32) | (uint32_t)(i0 + e);
 }
 
-// Dynamic LDS: cand[kCandCap] (u64) | h256[256] | bitmap[ceil(nb/32)]
-__global__ __launch_bounds__(kThreads) void topk_select_kernel(const float *__restrict__ scores,
-                                                               int32_t nb, int32_t k,
-                                                               int32_t *__restrict__ blk,
-                                                               int32_t *__restrict__ n_sel,
-                                                               TopkWs ws)
+__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float *__restrict__ scores,
+                                                                   int32_t nb, int32_t k,
+                                                                   int32_t *__restrict__ blk,
+                                                                   int32_t *__restrict__ n_sel,
+                                                                   TopkWs ws)
 {
-    extern __shared__ uint64_t lds64[];
-    uint64_t *cand = lds64;
-    uint32_t *h256 = (uint32_t *)(cand + kCandCap);
-    uint32_t *bitmap = h256 + kThreads;
-    __shared__ Scratch<kThreads> S;
-
-    const uint32_t B = ws.ctrl[kBin];
-    const int32_t lo = blockIdx.x * kDecodePerWg;
-    const int32_t hi = min(nb, lo + kDecodePerWg);
-    for (int32_t i0 = lo; i0 < hi; i0 += kThreads) {
-        const int32_t i = i0 + threadIdx.x;
-        uint32_t key = 0, bin = 0;
-        if (i < hi) {
-            key = score_key(scores[i]);
-            bin = key >> (32 - kHistBits);
-        }
-        const bool sure = i < hi && bin > B;
-        const bool maybe = i < hi && bin == B;
-        const uint32_t s1 = wave_append_slot(sure, &ws.ctrl[kSureCnt]);
-        if (sure)
-            ws.sure[s1] = i;
-        const uint32_t s2 = wave_append_slot(maybe, &ws.ctrl[kCandCnt]);
-        if (maybe)
-            ws.cand[s2] = ((uint64_t)key << 32) | (uint32_t)i;
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0)
-        S.flag = (atomicAdd(&ws.ctrl[kTicketB], 1u) == gridDim.x - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!S.flag)
-        return;
-    __threadfence();
-
-    const uint32_t above = __hip_atomic_load(&ws.ctrl[kAbove], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t n_sure = __hip_atomic_load(&ws.ctrl[kSureCnt], __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t c = __hip_atomic_load(&ws.ctrl[kCandCnt], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t need = (uint32_t)k - above;
-    zero_words<kThreads>(bitmap, ((uint32_t)nb + 31) / 32);
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < min(n_sure, (uint32_t)k); i += kThreads)
-        set_bit(bitmap, min((uint32_t)ws.sure[i], (uint32_t)nb - 1u));
-    if (c <= (uint32_t)kCandCap) {
-        for (uint32_t i = threadIdx.x; i < c; i += kThreads)
-            cand[i] = ws.cand[i];
-        __syncthreads();
-        LdsCands<kThreads> src{cand, c};
-        resolve<kThreads>(src, B, need, (uint32_t)nb, h256, S);
-        const uint32_t T = S.res[0], I = S.res[1];
-        src.each([&](uint32_t key, uint32_t id) {
-            if (key > T || (key == T && id <= I))
-                set_bit(bitmap, id);
-        });
+    constexpr int NT = kFinalThreads;
+    __shared__ uint64_t cand[kListMax];
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t bitmap[kMaxBlocks / 32];
+    __shared__ Scratch<NT> S;
+    const int t = threadIdx.x;
+    const uint32_t c = ws.ctrl[kCandCnt];
+    if (c < (uint32_t)k || c > (uint32_t)kListMax) {
+        // the list cannot be used: select from the whole row
+        select_row_global<NT>(scores, (uint32_t)nb, k, blk, hist, cand, bitmap, S);
     } else {
-        GlobalCands<kThreads> src{ws.cand, c};
-        resolve<kThreads>(src, B, need, (uint32_t)nb, h256, S);
-        const uint32_t T = S.res[0], I = S.res[1];
-        src.each([&](uint32_t key, uint32_t id) {
-            if (key > T || (key == T && id <= I))
-                set_bit(bitmap, id);
-        });
+        for (uint32_t i = t; i < c; i += NT)
+            cand[i] = ws.cand[i];
+        zero_words<NT>(hist, kHistBins);
+        zero_words<NT>(bitmap, ((uint32_t)nb + 31) / 32);
+        __syncthreads();
+        for (uint32_t i = t; i < c; i += NT)
+            atomicAdd(&hist[(uint32_t)(cand[i] >> (64 - kHistBits))], 1u);
+        __syncthreads();
+        find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
+        const uint32_t B = S.res[0];
+        const uint32_t need0 = (uint32_t)k - S.res[1];
+        __syncthreads();
+        // bins above B are in; bin B is split by key bits 19..12
+        uint32_t *h256 = hist;
+        if (t < 256)
+            h256[t] = 0;
+        __syncthreads();
+        for (uint32_t i = t; i < c; i += NT) {
+            const uint64_t e = cand[i];
+            const uint32_t bin = (uint32_t)(e >> (64 - kHistBits));
+            if (bin > B)
+                set_bit(bitmap, (uint32_t)e);
+            else if (bin == B)
+                atomicAdd(&h256[(uint32_t)(e >> 44) & 255u], 1u);
+        }
+        __syncthreads();
+        find_from_top<NT>(h256, 256, need0, S);
+        const uint32_t d = S.res[0];
+        const uint32_t need = need0 - S.res[1];
+        const uint32_t cd = h256[d];
+        if (t == 0)
+            S.cnt = 0;
+        __syncthreads();
+        uint32_t *dl = hist + 256;  // ids (list indices) of the threshold digit
+        for (uint32_t i = t; i < c; i += NT) {
+            const uint64_t e = cand[i];
+            if ((uint32_t)(e >> (64 - kHistBits)) != B)
+                continue;
+            const uint32_t dig = (uint32_t)(e >> 44) & 255u;
+            if (dig > d) {
+                set_bit(bitmap, (uint32_t)e);
+            } else if (dig == d && cd <= 64u) {
+                const uint32_t slot = atomicAdd(&S.cnt, 1u);
+                dl[slot] = i;
+            }
+        }
+        __syncthreads();
+        if (cd <= 64u) {
+            // rank by counting: (key desc, id asc) is strict
+            if ((uint32_t)t < cd) {
+                const uint64_t me = cand[dl[t]];
+                const uint32_t mk = (uint32_t)(me >> 32), mid = (uint32_t)me;
+                uint32_t before = 0;
+                for (uint32_t j = 0; j < cd; j++) {
+                    const uint64_t o = cand[dl[j]];
+                    const uint32_t ok = (uint32_t)(o >> 32), oid = (uint32_t)o;
+                    before += (ok > mk || (ok == mk && oid < mid)) ? 1u : 0u;
+                }
+                if (before < need)
+                    set_bit(bitmap, mid);
+            }
+        } else {
+            // many equal keys: digit passes over the whole threshold bin
+            LdsCands<NT> all{cand, c};
+            // resolve() only counts entries whose top 12 bits equal B
+            resolve<NT>(all, B, need0, (uint32_t)nb, hist + 512, S);
+            const uint32_t T = S.res[0], I = S.res[1];
+            all.each([&](uint32_t kk, uint32_t id) {
+                if (kk > T || (kk == T && id <= I))
+                    set_bit(bitmap, id);
+            });
+        }
+        __syncthreads();
+        compact_bitmap<NT>(bitmap, (uint32_t)nb, blk, (uint32_t)k, S);
     }
-    __syncthreads();
-    compact_bitmap<kThreads>(bitmap, (uint32_t)nb, blk, (uint32_t)k, S);
-    if (threadIdx.x == 0) {
+    if (t == 0) {
         n_sel[0] = k;
-        ws.ctrl[kSureCnt] = 0;
         ws.ctrl[kCandCnt] = 0;
-        ws.ctrl[kBin] = 0;
-        ws.ctrl[kAbove] = 0;
-        ws.ctrl[kTicketB] = 0;
     }
 }
 
@@ -713,21 +873,12 @@ hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_
         hipLaunchKernelGGL(iota_kernel, dim3(grid), dim3(kThreads), 0, s, blk, nb, n_sel);
         return hipGetLastError();
     }
-    if (nb <= kRegThreads * 64)
-        return launch_reg(scores, 1, nb, 0, k, blk, n_sel, s, true);
-    const int32_t G = (nb + kDecodePerWg - 1) / kDecodePerWg;
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(G), dim3(kThreads), 0, s, scores, nb, k, ws);
+    const int32_t G = (nb + kFilterPerWg - 1) / kFilterPerWg;
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(G), dim3(kThreads), 0, s, scores, nb, k, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const size_t lds = sizeof(uint64_t) * kCandCap + sizeof(uint32_t) * kThreads +
-                       sizeof(uint32_t) * (size_t)((nb + 31) / 32);
-    static std::once_flag once;
-    std::call_once(once, [] {
-        (void)hipFuncSetAttribute((const void *)topk_select_kernel,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 112 * 1024);
-    });
-    hipLaunchKernelGGL(topk_select_kernel, dim3(G), dim3(kThreads), lds, s, scores, nb, k, blk,
+    hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kFinalThreads), 0, s, scores, nb, k, blk,
                        n_sel, ws);
     return hipGetLastError();
 }

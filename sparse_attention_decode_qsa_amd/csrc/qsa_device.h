@@ -59,6 +59,52 @@ __device__ __forceinline__ float group_max(float v)
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
+// ---- cross-lane moves without LDS round trips (DPP within 16-lane rows, then
+// v_readlane across the 4 rows of the wave)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xb1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4e;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// sum over each aligned group of 4 lanes, result in all 4
+__device__ __forceinline__ float quad_sum(float x)
+{
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = fmaxf(x, dpp<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp<kDppRowMirror>(x));  // every lane of a row holds the row's max
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    x += dpp<kDppRowHalfMirror>(x);
+    x += dpp<kDppRowMirror>(x);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (a + b) + (c + d);
+}
+
 // Rank of this lane among the set lanes of a 64-bit ballot mask.
 __device__ __forceinline__ uint32_t rank_in_mask(uint64_t mask)
 {

@@ -17,6 +17,9 @@ struct CopySeg {
     int64_t n16;
 };
 
+constexpr int kHistBits = 12;  // top-k: bins of the top 12 bits of a score key
+constexpr int kHistBins = 1 << kHistBits;
+
 // ---- append (k_pool.hip) ----------------------------------------------------
 struct AppendArgs {
     CopySeg seg[3];      // raw rows, K rows, V rows (unused entries have n16 == 0)
@@ -39,8 +42,6 @@ hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h
                                 int32_t row_elems, float *scores, int32_t ld, hipStream_t s);
 
 // ---- top-k (k_topk.hip) -----------------------------------------------------
-constexpr int kHistBits = 12;
-constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCtrlWords = 64;
 
 struct TopkWs {
@@ -49,6 +50,7 @@ struct TopkWs {
     int32_t *sure;   // up to k entries
     uint64_t *cand;  // up to nb entries (key << 32 | id)
 };
+// Leaves ws.ctrl cleared.
 hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_t *blk,
                               int32_t *n_sel, TopkWs ws, hipStream_t s);
 hipError_t launch_topk_rows(const float *scores, int32_t n_q, int32_t ld, int32_t pos0,
@@ -63,7 +65,7 @@ hipError_t launch_gather(const int32_t *blk, int32_t n_blk, int32_t n_tokens,
 enum CellMode : int32_t { kCellsCompact = 0, kCellsBlocks = 1, kCellsList = 2 };
 constexpr int kAttnChunk = 64;
 constexpr int kAttnMaxSplits = 64;
-constexpr int kAttnChunksPerSplit = 4;
+constexpr int kAttnChunksPerSplit = 1;
 
 struct AttnArgs {
     const h16 *q;           // [rows][hq][D]
