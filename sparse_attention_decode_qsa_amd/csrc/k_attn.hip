@@ -288,39 +288,90 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     }
 }
 
-// Merge of split-K partials: one work group per (query head, row), one output
-// dim per thread.  Every thread loads all S (m, l, o_j) it needs in one round
-// (the (m, l) pairs are the same for all threads of the group) and forms
-// out_j = sum_s exp2(m_s - M) o_sj / sum_s exp2(m_s - M) l_s.
+// Merge of split-K partials: one work group per (query head, row).  Wave 0
+// turns the S (m, l) pairs into weights w_s = exp2(m_s - M) and
+// L = sum_s w_s l_s (one split per lane) while every thread already loads its
+// share of the o_s rows: output dim j, splits s = grp, grp + G, ... (G groups of
+// DV threads when DV < 256).  out_j = sum_s w_s o_sj / L, the group sums added
+// in group order.
+constexpr int kCombThreads = 256;
+static_assert(kAttnMaxSplits <= kWave, "one split per lane of wave 0");
+
 template <int DV>
-__global__ __launch_bounds__(DV) void attn_combine_kernel(const float *__restrict__ part,
-                                                          int32_t hq, int32_t S,
-                                                          const int32_t *n_list, int32_t list_cap,
-                                                          float *__restrict__ out)
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const float *__restrict__ part,
+                                                                   int32_t hq, int32_t S,
+                                                                   const int32_t *n_list,
+                                                                   int32_t list_cap,
+                                                                   float *__restrict__ out)
 {
-    const int h = blockIdx.x, row = blockIdx.y, j = threadIdx.x;
-    const float *pb = part + ((int64_t)row * hq + h) * S * (DV + 2);
+    constexpr int DPT = DV > kCombThreads ? DV / kCombThreads : 1;  // dims per thread
+    constexpr int G = DV < kCombThreads ? kCombThreads / DV : 1;    // split groups
+    constexpr int CH = 32 / DPT;                                     // splits per thread per round
+    __shared__ float w_sh[kAttnMaxSplits];
+    __shared__ float l_sh;
+    __shared__ float red[G][DV];
+
+    const int h = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
+    const int grp = t / (DV / DPT), jt = t % (DV / DPT);
+    const int64_t stride = DV + 2;
+    const float *pb = part + ((int64_t)row * hq + h) * S * stride;
+
+    float m = -INFINITY, l = 0.f;
+    if (t < kWave && t < S) {
+        m = pb[t * stride];
+        l = pb[t * stride + 1];
+    }
+    float acc[DPT];
+#pragma unroll
+    for (int p = 0; p < DPT; p++)
+        acc[p] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += G * CH) {
+        float o[CH][DPT];
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            const int sl = s0 + grp + G * i;
+            const int sc = sl < S ? sl : S - 1;
+#pragma unroll
+            for (int p = 0; p < DPT; p++)
+                o[i][p] = pb[sc * stride + 2 + jt + p * (DV / DPT)];
+        }
+        if (s0 == 0) {
+            if (t < kWave) {
+                const float M = wave_max(m);
+                const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+                const float L = wave_sum(w * l);
+                w_sh[t] = w;
+                if (t == 0)
+                    l_sh = L;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            const int sl = s0 + grp + G * i;
+            const float w = sl < S ? w_sh[sl < kAttnMaxSplits ? sl : 0] : 0.f;
+#pragma unroll
+            for (int p = 0; p < DPT; p++)
+                acc[p] = sl < S ? fmaf(w, o[i][p], acc[p]) : acc[p];
+        }
+    }
     const bool overflow = n_list && *n_list > list_cap;
-    float m[kAttnMaxSplits], l[kAttnMaxSplits], o[kAttnMaxSplits];
+    if (G > 1) {
+        red[grp][jt] = acc[0];
+        __syncthreads();
+        if (grp == 0) {
+            float O = red[0][jt];
 #pragma unroll
-    for (int s = 0; s < kAttnMaxSplits; s++) {
-        const bool ok = s < S;
-        m[s] = ok ? pb[s * (DV + 2)] : -INFINITY;
-        l[s] = ok ? pb[s * (DV + 2) + 1] : 0.f;
-        o[s] = ok ? pb[s * (DV + 2) + 2 + j] : 0.f;
+            for (int g = 1; g < G; g++)
+                O += red[g][jt];
+            out[((int64_t)row * hq + h) * DV + jt] = overflow ? NAN : O / l_sh;
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < DPT; p++)
+            out[((int64_t)row * hq + h) * DV + jt + p * (DV / DPT)] =
+                overflow ? NAN : acc[p] / l_sh;
     }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kAttnMaxSplits; s++)
-        M = fmaxf(M, m[s]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int s = 0; s < kAttnMaxSplits; s++) {
-        const float w = (s < S) ? exp2f(m[s] - M) : 0.f;
-        L += w * l[s];
-        O += w * o[s];
-    }
-    out[((int64_t)row * hq + h) * DV + j] = overflow ? NAN : O / L;
 }
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restrict__ blk,
@@ -368,7 +419,7 @@ hipError_t launch_g(const AttnArgs &a, int G, hipStream_t s)
     if (e != hipSuccess || a.splits == 1)
         return e;
     hipLaunchKernelGGL((attn_combine_kernel<DV>), dim3((uint32_t)a.hq, (uint32_t)a.rows),
-                       dim3(DV), 0, s, a.part, a.hq, a.splits,
+                       dim3(kCombThreads), 0, s, a.part, a.hq, a.splits,
                        a.mode == kCellsList ? a.n_list : nullptr, a.list_cap, a.out);
     return hipGetLastError();
 }

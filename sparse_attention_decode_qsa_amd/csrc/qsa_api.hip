@@ -328,7 +328,7 @@ int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, i
     const int32_t row = cfg->h_idx * cfg->d_idx;
     if (n_q == 1) {
         HIP_CHECK(launch_score_decode(H(q_idx), H(k_pool), (pos0 + 1) / kBlockTokens, row, scores,
-                                      (hipStream_t)stream));
+                                      nullptr, (hipStream_t)stream));
         return QSA_OK;
     }
     if (ld % 4)
@@ -515,11 +515,11 @@ int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_b
     ap.n_blocks = nb - ap.b_lo;
     ap.eps = cfg->rms_eps;
     ap.base = cfg->rope_base;
-    HIP_CHECK(launch_append(ap, s));
 
-    // 2. scores over the nb complete blocks
+    // 2. scores over the nb complete blocks; the append runs in the same launch
+    // and scores the block it completes
     float *scores = scores_out ? scores_out : at<float>(ws, L.scores);
-    HIP_CHECK(launch_score_decode(H(q_idx), H(Lb->k_pool), nb, (int32_t)row, scores, s));
+    HIP_CHECK(launch_score_decode(H(q_idx), H(Lb->k_pool), ap.b_lo, (int32_t)row, scores, &ap, s));
 
     // 3. top-k blocks (ascending ids)
     int32_t *blk = blk_out ? blk_out : at<int32_t>(ws, L.blk);

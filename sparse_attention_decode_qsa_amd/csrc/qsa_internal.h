@@ -36,8 +36,10 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 
 // ---- scores (k_score.hip) ---------------------------------------------------
+// ap (may be NULL): append work run in the same launch (at most one completed
+// block, block nb; scores[nb] is then written too).
 hipError_t launch_score_decode(const h16 *q, const h16 *pool, int32_t nb, int32_t row_elems,
-                               float *scores, hipStream_t s);
+                               float *scores, const AppendArgs *ap, hipStream_t s);
 hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h16 *pool,
                                 int32_t row_elems, float *scores, int32_t ld, hipStream_t s);
 
