@@ -16,6 +16,10 @@ Reported:
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Other workloads (one JSON line each, same keys): prefill_1024_at_126253 (prefill
+chunk tokens/s; roofline = MFMA scoring against the f16 dense peak, plus the
+attention's K/V GB/s) and mla_list_262144 (list-attention calls/s, latency-bound).
 """
 from __future__ import annotations
 
@@ -253,25 +257,225 @@ def bench_decode(args):
     return res
 
 
+def _timed(stream, fn, reps):
+    """Average µs of fn() over reps launches on stream (HIP events on that stream)."""
+    import torch
+    with torch.cuda.stream(stream):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def _contract(metric, value, unit, steps, warmup, ms, dtype, config, roofline, hib=True):
+    return {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": hib, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic", "config": config, "roofline": roofline}
+
+
+def bench_prefill(args):
+    """One prefill chunk: 1024 query rows at depth 126,253, each row with its own
+    causal prefix (append, MFMA scores, per-row top-k, per-row sparse attention)."""
+    import torch
+    from sparse_attention_decode_qsa_amd import binding as qb
+    from sparse_attention_decode_qsa_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    qb.load()
+    cfg = qb.Config(h_idx=w.h_idx, d_idx=w.d_idx, topk_blocks=w.topk, hq=w.hq, hkv=w.hkv, d=w.d,
+                    dv=w.dv, cap_tokens=w.cap_tokens)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    t0 = time.time()
+    I = synth.prefill_inputs(w, 0)
+    depth, n_q = I["depth"], w.n_q
+    g = qb.Layer(cfg, dev)
+    qb.qsa_pool_append(cfg, t(I["raw"][:depth]), 0, g.k_raw, g.k_pool)
+    g.k_cache[:depth] = t(I["k"][:depth])
+    g.v_cache[:depth] = t(I["v"][:depth])
+    q_idx, q = t(I["q_idx"]), t(I["q"])
+    raw_new, k_new, v_new = t(I["raw"][depth:]), t(I["k"][depth:]), t(I["v"][depth:])
+    torch.cuda.synchronize()
+    log(f"[setup] prefill caches ready ({time.time() - t0:.1f}s)")
+    nb_end = (depth + n_q) // 4
+    ld = (nb_end + 1 + 63) // 64 * 64
+    out = torch.empty((n_q, w.hq, w.dv), dtype=torch.float32, device=dev)
+    scores = torch.empty((n_q, ld), dtype=torch.float32, device=dev)
+    blk = torch.empty((n_q, w.topk), dtype=torch.int32, device=dev)
+    nsel = torch.empty(n_q, dtype=torch.int32, device=dev)
+    ws = qb.workspace(cfg, n_q, depth + n_q, dev)
+    stream = torch.cuda.Stream()
+
+    def step():
+        qb.qsa_prefill_step(cfg, g, depth, q_idx, raw_new, q, k_new, v_new, out, ws,
+                            scores_out=scores, ld_scores=ld, blk_out=blk)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    stream.synchronize()
+    step_us = _timed(stream, step, args.steps)
+    # the stages alone, on the caches the step leaves behind
+    score_us = _timed(stream, lambda: qb.qsa_index_score(cfg, q_idx, depth, g.k_pool, scores,
+                                                         ld=ld), args.steps)
+    topk_us = _timed(stream, lambda: qb.qsa_topk_blocks(cfg, scores, n_q, ld, depth, blk, nsel,
+                                                        ws), args.steps)
+    attn_us = _timed(stream, lambda: qb.qsa_prefill_attn(cfg, q, depth, blk, w.topk, g.k_cache,
+                                                         g.v_cache, out, ws), args.steps)
+    nbs = [(depth + r + 1) // 4 for r in range(n_q)]
+    flop = 2.0 * w.h_idx * w.d_idx * float(sum(nbs))
+    cells = [4 * min(w.topk, nb) + (depth + r + 1) % 4 for r, nb in enumerate(nbs)]
+    kv_bytes = float(sum(cells)) * w.hkv * (w.d + w.dv) * 2
+    tflops = flop / (score_us * 1e-6) / 1e12
+    res = _contract(
+        "QSA prefill chunk tokens/s (1024 queries at depth 126,253)", n_q / (step_us * 1e-6),
+        "tokens/s", args.steps, args.warmup, step_us / 1e3, "f16",
+        {"workload": w.name, "depth": depth, "n_q": n_q, "indexer": f"{w.h_idx}x{w.d_idx}",
+         "topk_blocks": w.topk, "attention": f"{w.hq}/{w.hkv}x{w.d}", "launch": "eager"},
+        {"bound": "mfma", "kernel": "score_prefill_kernel", "achieved": round(tflops, 2),
+         "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+         "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+         "algorithmic_flop_per_launch": flop, "avg_launch_us": round(score_us, 2)})
+    res["stages_us"] = {"step": round(step_us, 2), "score": round(score_us, 2),
+                        "topk": round(topk_us, 2), "attn": round(attn_us, 2)}
+    res["attention_hbm"] = {"bound": "hbm", "algorithmic_bytes": kv_bytes,
+                            "achieved": round(kv_bytes / (attn_us * 1e-6) / 1e9, 1),
+                            "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+                            "frac": round(kv_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(w, I, args.cpu_budget)
+    return res
+
+
+def cpu_baseline_prefill(w, I, budget_s):
+    """Oracle prefill rows (each a decode-equivalent row), single thread."""
+    import oracle as O
+    depth = I["depth"]
+    n_all = depth + w.n_q
+    t0 = time.time()
+    pooled = O.pool_rebuild(I["raw"], n_all)
+    log(f"[cpu] oracle pooled rebuild {time.time() - t0:.1f}s")
+    sh = O.Shape(w.h_idx, w.d_idx, w.topk, w.hq, w.hkv, w.d, w.dv)
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        r = (rows * 97) % w.n_q
+        O.prefill_row(sh, pooled, I["k"], I["v"], depth + r, I["q_idx"][r], I["q"][r])
+        rows += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or rows >= 64:
+            break
+    return dict(value=rows / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{rows} oracle prefill rows of the chunk (positions depth+r), single "
+                       f"thread, {el:.1f} s")
+
+
+def bench_mla(args):
+    """MLA-style list attention at N = 262,144 with 2,048 visible positions."""
+    import torch
+    from sparse_attention_decode_qsa_amd import binding as qb
+    from sparse_attention_decode_qsa_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    qb.load()
+    I = synth.mla_inputs(w)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, kv, mask = t(I["q"]), t(I["kv"]), t(I["mask"])
+    ws = torch.zeros(qb.qsa_mla_workspace_size(w.hq, w.dv, w.list_len), dtype=torch.uint8,
+                     device=dev)
+    qb.qsa_workspace_init(ws)
+    out = torch.empty((w.hq, w.dv), dtype=torch.float32, device=dev)
+    n_list = torch.zeros(1, dtype=torch.int32, device=dev)
+    scale = 1.0 / float(np.sqrt(w.d))
+    stream = torch.cuda.Stream()
+
+    def call():
+        qb.qsa_mla_sparse_attn(q, kv, None, mask, w.list_len, scale, n_list, out, ws)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            call()
+    stream.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=stream):
+        call()
+    stream.synchronize()
+    eager_us = _timed(stream, call, args.steps)
+    graph_us = _timed(stream, gr.replay, args.steps)
+    nbytes = w.n_tokens * 2 + w.list_len * w.d * 2 + w.hq * w.d * 2 + w.hq * w.dv * 4
+    res = _contract(
+        "QSA MLA list attention calls/s (N = 262,144, 2,048 visible)", 1e6 / graph_us, "calls/s",
+        args.steps, args.warmup, graph_us / 1e3, "f16",
+        {"workload": w.name, "n": w.n_tokens, "list": w.list_len, "hq": w.hq,
+         "dkq": w.d, "dv": w.dv, "launch": "hip graph"},
+        {"bound": "latency", "kernel": "mla path (mask list + attention + combine)",
+         "achieved": round(nbytes / (graph_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+         "unit": "GB/s", "frac": round(nbytes / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+         "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+         "avg_launch_us": round(graph_us, 2)})
+    res["eager_us"] = round(eager_us, 2)
+    if not args.no_cpu_baseline:
+        import oracle as O
+        lst = O.mask_list(I["mask"])
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            O.mla_attn(I["q"], I["kv"], None, I["mask"], lst, w.dv, scale)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_budget or calls >= 64:
+                break
+        res["cpu_baseline"] = dict(value=calls / el, unit="calls/s", cores=1, kind="oracle",
+                                   sample=f"{calls} oracle list-attention calls on the same "
+                                          f"inputs, single thread, {el:.1f} s")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_255181",
-                    choices=["decode_255181", "decode_61789", "tiny_decode_4k"])
+                    choices=["decode_255181", "decode_61789", "tiny_decode_4k",
+                             "prefill_1024_at_126253", "mla_list_262144"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
     ap.add_argument("--eager", action="store_true", help="launch per call instead of graphs")
     ap.add_argument("--compact-gather", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=240)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (a counter "
+                         "calibration kernel of known size for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("this build runs on one GPU only: the QSA layer step has no multi-GPU path here "
               "(see the sharding notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    res = bench_decode(args)
+    if args.calib_copy_mib:
+        import torch
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.workload.startswith("prefill"):
+        res = bench_prefill(args)
+    elif args.workload.startswith("mla"):
+        res = bench_mla(args)
+    else:
+        res = bench_decode(args)
     print(json.dumps(res), flush=True)
 
 

@@ -1,0 +1,84 @@
+"""Summarises rocprofv3 counter CSVs into HBM bytes per kernel launch.
+
+    python -m sparse_attention_decode_qsa_amd.counters \
+        --fetch K_FETCH.csv --write K_WRITE.csv \
+        --calib-fetch C_FETCH.csv --calib-write C_WRITE.csv --calib-mib 256 \
+        --kernel <substring of the mangled name> --key score_decode_kernel \
+        [--json profiles/traffic.json]
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch; each counter in a run of its own)
+are averaged over the dispatches whose kernel name contains --kernel.  The
+calibration runs (bench.py --calib-copy-mib N: a device-to-device copy of N MiB,
+nothing else) give the scale factor per counter: the bytes the copy must read
+(or write) / what the counter reports for the copy dispatches.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def per_dispatch(path: str, counter: str) -> dict:
+    """{(dispatch id, kernel name): value} for one counter."""
+    vals = defaultdict(float)
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            vals[(row["Dispatch_Id"], row["Kernel_Name"])] += float(row["Counter_Value"])
+    return vals
+
+
+def mean_kib(path: str, counter: str, sub: str):
+    v = [x for (_, name), x in per_dispatch(path, counter).items() if sub in name]
+    if not v:
+        raise SystemExit(f"no dispatch matching {sub!r} in {path}")
+    return sum(v) / len(v), len(v)
+
+
+def src_hash(name: str) -> str:
+    with open(os.path.join(HERE, "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--calib-fetch", required=True)
+    ap.add_argument("--calib-write", required=True)
+    ap.add_argument("--calib-mib", type=int, default=256)
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--key", required=True)
+    ap.add_argument("--source", default="k_score.hip")
+    ap.add_argument("--json", default=None)
+    a = ap.parse_args()
+    cb = float(a.calib_mib << 20)
+    out = {"source_hash": src_hash(a.source), "kernel_match": a.kernel}
+    total = 0.0
+    for name, kpath, cpath, counter in (("fetch", a.fetch, a.calib_fetch, "FETCH_SIZE"),
+                                        ("write", a.write, a.calib_write, "WRITE_SIZE")):
+        kib, n = mean_kib(kpath, counter, a.kernel)
+        ckib, cn = mean_kib(cpath, counter, "copyBuffer")
+        factor = cb / (ckib * 1024.0)
+        out[name] = dict(counter=counter, kib_per_dispatch=round(kib, 1), dispatches=n,
+                         calib_kib_per_copy=round(ckib, 1), calib_copies=cn,
+                         factor=round(factor, 4), bytes_per_dispatch=round(kib * 1024 * factor))
+        total += kib * 1024 * factor
+    out["bytes_per_launch"] = round(total)
+    print(json.dumps(out, indent=1))
+    if a.json:
+        d = json.load(open(a.json)) if os.path.exists(a.json) else {}
+        d[a.key] = out
+        with open(a.json, "w") as f:
+            json.dump(d, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()
