@@ -31,8 +31,6 @@ constexpr int kThreads = 256;
 constexpr int kCandCap = 4096;
 constexpr int kMaxBlocks = 1 << 19;  // bitmap of 64 KiB in LDS
 
-// control words in TopkWs::ctrl
-enum : int { kCandCnt = 3 };
 
 template <int NT>
 struct Scratch {
@@ -43,64 +41,58 @@ struct Scratch {
     uint32_t flag;
 };
 
-// Over nbins (4096 or 256) LDS bins, finds the bin where the count taken from
-// the top reaches need.  res[0] = bin (0xffffffff if the total is below need),
-// res[1] = count in the bins above it, res[2] = total.  All NT threads call it.
-template <int NT>
-__device__ void find_from_top(const uint32_t *hist, int nbins, uint32_t need, Scratch<NT> &S)
+// Over NBINS (4096 or 256) LDS bins, finds the bin where the count taken from
+// the top reaches need (need >= 1).  res[0] = bin (0xffffffff if the total is
+// below need), res[1] = count in the bins above it, res[2] = total.  All NT
+// threads call it; wave 0 does the work: lane l sums bins [l*per, (l+1)*per), a
+// wave scan finds the lane where the count from the top crosses need, and a
+// second wave scan over that lane's bins finds the bin.  hist is 16-byte aligned;
+// NBINS is 256 or 4096.
+template <int NT, int NBINS>
+__device__ void find_from_top(const uint32_t *hist, uint32_t need, Scratch<NT> &S)
 {
-    // Per-thread bin sums, a suffix scan within each wave, then across the wave
-    // totals; every step is a parallel shuffle scan (no single-lane LDS walks).
-    constexpr int NW = NT / kWave;
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const int per = nbins >= NT ? nbins / NT : 1;
-    const int nthr = nbins >= NT ? NT : nbins;
-    uint32_t c = 0;
-    if (t < nthr)
-        for (int i = 0; i < per; i++)
-            c += hist[t * per + i];
-    // inclusive suffix sum over the lanes of this wave (bins of higher threads)
-    uint32_t sfx = c;
+    static_assert(NBINS == 256 || NBINS == 4096, "bins");
+    if (threadIdx.x < kWave) {
+        const uint32_t lane = threadIdx.x;
+        constexpr int per = NBINS / kWave;  // 4 or 64
+        uint32_t c = 0;
+        if (per == 4) {
+            const uint4 v = *(const uint4 *)(hist + lane * 4);
+            c = v.x + v.y + v.z + v.w;
+        } else {
+            // rotated order: at step i the 64 lanes read 64 different banks; all
+            // loads are issued before the sum
+            uint32_t h[per];
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t v = __shfl_down(sfx, o, kWave);
-        if (lane + o < kWave)
-            sfx += v;
-    }
-    if (lane == 0)
-        S.tmp[w] = sfx;  // wave total
-    __syncthreads();
-    // count in the waves above this one
-    uint32_t wt = lane < NW ? S.tmp[lane] : 0u;
-    uint32_t wsfx = wt;
+            for (int i = 0; i < per; i++)
+                h[i] = hist[lane * per + ((i + (int)lane) & (per - 1))];
 #pragma unroll
-    for (int o = 1; o < NW; o <<= 1) {
-        const uint32_t v = __shfl_down(wsfx, o, kWave);
-        if (lane + o < NW)
-            wsfx += v;
-    }
-    const uint32_t above_wave = __shfl(wsfx - wt, w, kWave) ;
-    const uint32_t total = __shfl(wsfx, 0, kWave);
-    const uint32_t above = above_wave + sfx - c;  // count in all higher threads
-    __syncthreads();
-    if (t == 0) {
-        S.res[2] = total;
-        if (need > total)
-            S.res[0] = 0xffffffffu;  // not reached
-    }
-    if (above < need && need <= above + c) {
-        uint32_t acc = above;
-        int sel = t * per;
-        for (int i = per - 1; i >= 0; i--) {
-            const uint32_t h = hist[t * per + i];
-            if (acc + h >= need) {
-                sel = t * per + i;
-                break;
-            }
-            acc += h;
+            for (int i = 0; i < per; i++)
+                c += h[i];
         }
-        S.res[0] = (uint32_t)sel;
-        S.res[1] = acc;
+        const uint32_t incl = wave_incl_scan(c);
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+        const uint32_t above = total - incl;  // in the bins of the lanes above
+        if (need > total) {
+            if (lane == 0) {
+                S.res[0] = 0xffffffffu;
+                S.res[2] = total;
+            }
+        } else {
+            const uint64_t m = __ballot(above < need && need <= above + c);
+            const int L = __ffsll((unsigned long long)m) - 1;
+            const uint32_t aboveL = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+            const uint32_t h = ((int)lane < per) ? hist[L * per + (int)lane] : 0u;
+            const uint32_t incl2 = wave_incl_scan(h);
+            const uint32_t tot2 = (uint32_t)__builtin_amdgcn_readlane((int)incl2, kWave - 1);
+            const uint32_t above2 = aboveL + (tot2 - incl2);
+            if ((int)lane < per && above2 < need && need <= above2 + h) {
+                S.res[0] = (uint32_t)(L * per + (int)lane);
+                S.res[1] = above2;
+            }
+            if (lane == 0)
+                S.res[2] = total;
+        }
     }
     __syncthreads();
 }
@@ -170,7 +162,7 @@ __device__ void resolve(const Src &src, uint32_t bin, uint32_t need, uint32_t nb
                 atomicAdd(&h256[(key >> sh) & mask], 1u);
         });
         __syncthreads();
-        find_from_top<NT>(h256, 256, need, S);
+        find_from_top<NT, 256>(h256, need, S);
         const uint32_t d = S.res[0];
         need -= S.res[1];
         last_count = h256[d];
@@ -194,7 +186,7 @@ __device__ void resolve(const Src &src, uint32_t bin, uint32_t need, uint32_t nb
                     atomicAdd(&h256[255u - ((id >> s2) & 255u)], 1u);
             });
             __syncthreads();
-            find_from_top<NT>(h256, 256, need, S);
+            find_from_top<NT, 256>(h256, need, S);
             const uint32_t d = 255u - S.res[0];
             need -= S.res[1];
             ip = (ip << 8) | d;
@@ -216,26 +208,14 @@ __device__ uint32_t wg_exclusive_scan(uint32_t v, Scratch<NT> &S)
 {
     constexpr int NW = NT / kWave;
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    uint32_t s = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t u = __shfl_up(s, o, kWave);
-        if (lane >= o)
-            s += u;
-    }
+    const uint32_t s = wave_incl_scan(v);
     __syncthreads();
     if (lane == kWave - 1)
         S.tmp[w] = s;
     __syncthreads();
-    uint32_t wt = lane < NW ? S.tmp[lane] : 0u;
-    uint32_t ws = wt;
-#pragma unroll
-    for (int o = 1; o < NW; o <<= 1) {
-        const uint32_t u = __shfl_up(ws, o, kWave);
-        if (lane >= o)
-            ws += u;
-    }
-    const uint32_t base = __shfl(ws - wt, w, kWave);  // sum of the waves below
+    const uint32_t wt = lane < NW ? S.tmp[lane] : 0u;
+    const uint32_t ws = wave_incl_scan(wt);
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(ws - wt), w);  // waves below
     __syncthreads();
     return base + s - v;
 }
@@ -291,7 +271,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
 {
     constexpr int NT = kRegThreads;
     constexpr int V4 = KPT / 4;
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
     __shared__ uint64_t cand[kCandCap];
     __shared__ uint32_t lst[kListCap];
     __shared__ uint32_t bitmap[NT * KPT / 32];
@@ -365,7 +345,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
     __syncthreads();
     atomicAdd(&hist[mybin], 1u);
     __syncthreads();
-    find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
+    find_from_top<NT, kHistBins>(hist, (uint32_t)k, S);
     const uint32_t L = S.res[0];
     __syncthreads();
     // 2. The keys in bins >= L (a few per cent of the row) go to a short LDS list
@@ -434,7 +414,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
         }
     }
     __syncthreads();
-    find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
+    find_from_top<NT, kHistBins>(hist, (uint32_t)k, S);
     const uint32_t B = S.res[0];
     uint32_t need = (uint32_t)k - S.res[1];
     const uint32_t W = (nb + 31) / 32;
@@ -588,7 +568,7 @@ __device__ void select_row_global(const float *row, uint32_t nb, int32_t k, int3
     for (uint32_t i = threadIdx.x; i < nb; i += NT)
         atomicAdd(&hist[score_key(row[i]) >> (32 - kHistBits)], 1u);
     __syncthreads();
-    find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
+    find_from_top<NT, kHistBins>(hist, (uint32_t)k, S);
     const uint32_t B = S.res[0];
     const uint32_t need = (uint32_t)k - S.res[1];
     zero_words<NT>(bitmap, (nb + 31) / 32);
@@ -658,26 +638,35 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
 
 // ---------------------------------------------------------------- decode form
 // One long row spread over many CUs, two launches that meet only at the kernel
-// boundary (no fences; the only global atomics reserve list slots, one per wave
-// that has something to append):
-//   filter  every work group takes the same deterministic sample of the row
-//           (every stride-th score), finds the bin holding the r-th largest
-//           sampled key (r about 3x the sample's expected share of k), and
-//           appends each of its own keys in that bin or above to ws.cand;
-//   final   one work group selects exactly from that list: 12-bit histogram,
-//           threshold bin, one more 8-bit digit, rank counting of the last few.
+// boundary.  Neither uses a fence or a global atomic: on this part a device-scope
+// fence or a contended atomic costs more than the kernel boundary itself.
+//   filter  work group g takes scores [1024 g, 1024 g + 1024) and the same
+//           deterministic sample of the row (every stride-th score), finds the
+//           bin of the r-th largest sampled key (r about 3x the sample's expected
+//           share of k) and writes its own keys in that bin or above, in id
+//           order, to region g of ws.cand, and their count to ws.rcnt[g];
+//   final   one work group reads all region counts and the first `head` entries
+//           of every region in one round (regions longer than that in a second
+//           round), so it holds the list in ascending id order.  It selects
+//           exactly: a 12-bit histogram gives the threshold bin, an 8-bit digit
+//           histogram splits it, rank counting settles the threshold digit (or
+//           further digit passes, when it is crowded), and a prefix sum over the
+//           list writes the chosen ids in ascending order.
 //           If the list holds fewer than k keys (the sample misled the bound) or
 //           more than fit in LDS (flat scores), it selects from the whole row.
-// The final step clears the control words it used.
 constexpr int kFilterPerWg = 1024;  // scores per filter work group (4 per thread)
 constexpr int kSample = 1024;       // sampled scores (4 per thread)
 constexpr int kFinalThreads = 1024;
 constexpr int kListMax = 4096;      // list entries the final step keeps in LDS
+constexpr int kMaxRegions = kMaxBlocks / kFilterPerWg;
+static_assert(kMaxRegions % kWave == 0, "whole regions per lane of wave 0");
+static_assert(kListMax == 4 * kFinalThreads, "four list entries per final thread");
 
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float *__restrict__ scores,
-                                                               int32_t nb, int32_t k, TopkWs ws)
+                                                               int32_t nb, int32_t k, TopkWs ws,
+                                                               uint32_t head)
 {
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
     __shared__ Scratch<kThreads> S;
     const int t = threadIdx.x;
     const uint32_t stride = max(64u, ((uint32_t)nb + kSample - 1) / kSample);
@@ -708,124 +697,194 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float *__re
     // r-th largest sampled key: about 3x the sample's expected count of top-k
     // keys, so the bound keeps ~3k keys of the row; exactness is checked later
     const uint32_t want = (uint32_t)(((uint64_t)3 * k * ns + nb - 1) / nb) + 8;
-    find_from_top<kThreads>(hist, kHistBins, min(want, ns), S);
+    find_from_top<kThreads, kHistBins>(hist, min(want, ns), S);
     const uint32_t Lb = (S.res[0] == 0xffffffffu) ? 0u : S.res[0];
-    // slots: per-thread count, work-group scan, one global atomic per work group
     uint32_t key[4], mine = 0;
+    bool keep[4];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
         key[e] = score_key(own[e]);
-        mine += (i0 + e < nb && (key[e] >> (32 - kHistBits)) >= Lb) ? 1u : 0u;
+        keep[e] = i0 + e < nb && (key[e] >> (32 - kHistBits)) >= Lb;
+        mine += keep[e] ? 1u : 0u;
     }
     uint32_t off = wg_exclusive_scan<kThreads>(mine, S);
-    if (t == kThreads - 1) {
-        const uint32_t total = off + mine;
-        S.res[3] = total ? atomicAdd(&ws.ctrl[kCandCnt], total) : 0u;
-    }
-    __syncthreads();
-    off += S.res[3];
+    uint64_t *region = ws.cand + (size_t)blockIdx.x * kFilterPerWg;
 #pragma unroll
     for (int e = 0; e < 4; e++)
-        if (i0 + e < nb && (key[e] >> (32 - kHistBits)) >= Lb)
-            ws.cand[off++] = ((uint64_t)key[e] << 32) | (uint32_t)(i0 + e);
+        if (keep[e])
+            region[off++] = ((uint64_t)key[e] << 32) | (uint32_t)(i0 + e);
+    if (t == kThreads - 1) {
+        ws.rcnt[blockIdx.x] = off;  // exclusive offset + own count = region total
+        S.res[3] = off;
+    }
+    __syncthreads();
+    // pad the region up to the head the final step reads in its first round, so
+    // that read only touches lines written by this launch
+    for (uint32_t i = S.res[3] + t; i < head; i += kThreads)
+        region[i] = 0ull;
 }
 
+// head: entries read from every region in the first round (a power of two,
+// head * regions <= kListMax, head <= kFilterPerWg).
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float *__restrict__ scores,
                                                                    int32_t nb, int32_t k,
                                                                    int32_t *__restrict__ blk,
                                                                    int32_t *__restrict__ n_sel,
-                                                                   TopkWs ws)
+                                                                   TopkWs ws, int32_t head_log2)
 {
     constexpr int NT = kFinalThreads;
     __shared__ uint64_t cand[kListMax];
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
     __shared__ uint32_t bitmap[kMaxBlocks / 32];
+    __shared__ uint32_t rbase[kMaxRegions], rlen[kMaxRegions];
+    __shared__ __attribute__((aligned(16))) uint8_t sel[kListMax];
+    __shared__ __attribute__((aligned(16))) uint32_t h256[256];
     __shared__ Scratch<NT> S;
     const int t = threadIdx.x;
-    const uint32_t c = ws.ctrl[kCandCnt];
+    const int32_t G = (nb + kFilterPerWg - 1) / kFilterPerWg;
+    const uint32_t head = 1u << head_log2;
+
+    // one round of loads: every region count and the head of every region
+    uint64_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint32_t sl = (uint32_t)(t + NT * j);
+        const uint32_t g = sl >> head_log2, i = sl & (head - 1u);
+        e[j] = (g < (uint32_t)G) ? ws.cand[(size_t)g * kFilterPerWg + i] : 0ull;
+    }
+    // wave 0: the region counts (8 consecutive regions per lane) and their
+    // exclusive prefix, i.e. where each region starts in the list
+    constexpr int RPL = kMaxRegions / kWave;
+    if (t < kWave) {
+        uint32_t rc[RPL], tot = 0;
+#pragma unroll
+        for (int q = 0; q < RPL; q++) {
+            const int32_t g = RPL * t + q;
+            rc[q] = (g < G) ? ws.rcnt[g] : 0u;
+            tot += rc[q];
+        }
+        const uint32_t incl = wave_incl_scan(tot);
+        uint32_t b = incl - tot;
+        bool over = false;
+#pragma unroll
+        for (int q = 0; q < RPL; q++) {
+            const int32_t g = RPL * t + q;
+            if (g < G) {
+                rbase[g] = b;
+                rlen[g] = rc[q];
+                over |= rc[q] > head;  // longer than its head: a second round
+            }
+            b += rc[q];
+        }
+        const uint64_t anyover = __ballot(over);
+        if (t == 0) {
+            S.cnt = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+            S.flag = anyover ? 1u : 0u;
+        }
+    }
+    ((uint32_t *)sel)[t] = 0u;
+    __syncthreads();
+    const uint32_t c = S.cnt;
     if (c < (uint32_t)k || c > (uint32_t)kListMax) {
         // the list cannot be used: select from the whole row
         select_row_global<NT>(scores, (uint32_t)nb, k, blk, hist, cand, bitmap, S);
     } else {
-        for (uint32_t i = t; i < c; i += NT)
-            cand[i] = ws.cand[i];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t sl = (uint32_t)(t + NT * j);
+            const uint32_t g = sl >> head_log2, i = sl & (head - 1u);
+            if (g < (uint32_t)G && i < rlen[g])
+                cand[rbase[g] + i] = e[j];
+        }
+        if (S.flag) {
+            // rare: the tails of long regions, one region at a time
+            for (int32_t g = 0; g < G; g++) {
+                const uint32_t n = rlen[g];
+                for (uint32_t i = head + t; i < n; i += NT)
+                    cand[rbase[g] + i] = ws.cand[(size_t)g * kFilterPerWg + i];
+            }
+        }
         zero_words<NT>(hist, kHistBins);
-        zero_words<NT>(bitmap, ((uint32_t)nb + 31) / 32);
+        if (t < 256)
+            h256[t] = 0;
+        if (t == 0)
+            S.cnt2 = 0;
         __syncthreads();
         for (uint32_t i = t; i < c; i += NT)
             atomicAdd(&hist[(uint32_t)(cand[i] >> (64 - kHistBits))], 1u);
         __syncthreads();
-        find_from_top<NT>(hist, kHistBins, (uint32_t)k, S);
+        find_from_top<NT, kHistBins>(hist, (uint32_t)k, S);
         const uint32_t B = S.res[0];
-        const uint32_t need0 = (uint32_t)k - S.res[1];
-        __syncthreads();
-        // bins above B are in; bin B is split by key bits 19..12
-        uint32_t *h256 = hist;
-        if (t < 256)
-            h256[t] = 0;
-        __syncthreads();
+        const uint32_t need = (uint32_t)k - S.res[1];
         for (uint32_t i = t; i < c; i += NT) {
-            const uint64_t e = cand[i];
-            const uint32_t bin = (uint32_t)(e >> (64 - kHistBits));
+            const uint64_t v = cand[i];
+            const uint32_t bin = (uint32_t)(v >> (64 - kHistBits));
             if (bin > B)
-                set_bit(bitmap, (uint32_t)e);
+                sel[i] = 1;
             else if (bin == B)
-                atomicAdd(&h256[(uint32_t)(e >> 44) & 255u], 1u);
+                atomicAdd(&h256[(uint32_t)(v >> 44) & 255u], 1u);
         }
         __syncthreads();
-        find_from_top<NT>(h256, 256, need0, S);
+        find_from_top<NT, 256>(h256, need, S);
         const uint32_t d = S.res[0];
-        const uint32_t need = need0 - S.res[1];
+        const uint32_t need2 = need - S.res[1];
         const uint32_t cd = h256[d];
-        if (t == 0)
-            S.cnt = 0;
-        __syncthreads();
-        uint32_t *dl = hist + 256;  // ids (list indices) of the threshold digit
+        uint32_t *dl = hist;  // list indices of digit d
         for (uint32_t i = t; i < c; i += NT) {
-            const uint64_t e = cand[i];
-            if ((uint32_t)(e >> (64 - kHistBits)) != B)
+            const uint64_t v = cand[i];
+            if ((uint32_t)(v >> (64 - kHistBits)) != B)
                 continue;
-            const uint32_t dig = (uint32_t)(e >> 44) & 255u;
-            if (dig > d) {
-                set_bit(bitmap, (uint32_t)e);
-            } else if (dig == d && cd <= 64u) {
-                const uint32_t slot = atomicAdd(&S.cnt, 1u);
-                dl[slot] = i;
-            }
+            const uint32_t dig = (uint32_t)(v >> 44) & 255u;
+            if (dig > d)
+                sel[i] = 1;
+            else if (dig == d && cd <= (uint32_t)kWave)
+                dl[atomicAdd(&S.cnt2, 1u)] = i;
         }
         __syncthreads();
-        if (cd <= 64u) {
-            // rank by counting: (key desc, id asc) is strict
+        if (cd <= (uint32_t)kWave) {
             if ((uint32_t)t < cd) {
-                const uint64_t me = cand[dl[t]];
-                const uint32_t mk = (uint32_t)(me >> 32), mid = (uint32_t)me;
+                const uint32_t me = dl[t];
+                const uint64_t v = cand[me];
+                const uint32_t mk = (uint32_t)(v >> 32), mid = (uint32_t)v;
                 uint32_t before = 0;
                 for (uint32_t j = 0; j < cd; j++) {
                     const uint64_t o = cand[dl[j]];
                     const uint32_t ok = (uint32_t)(o >> 32), oid = (uint32_t)o;
                     before += (ok > mk || (ok == mk && oid < mid)) ? 1u : 0u;
                 }
-                if (before < need)
-                    set_bit(bitmap, mid);
+                if (before < need2)
+                    sel[me] = 1;
             }
         } else {
-            // many equal keys: digit passes over the whole threshold bin
             LdsCands<NT> all{cand, c};
-            // resolve() only counts entries whose top 12 bits equal B
-            resolve<NT>(all, B, need0, (uint32_t)nb, hist + 512, S);
+            resolve<NT>(all, B, need, (uint32_t)nb, h256, S);
             const uint32_t T = S.res[0], I = S.res[1];
-            all.each([&](uint32_t kk, uint32_t id) {
-                if (kk > T || (kk == T && id <= I))
-                    set_bit(bitmap, id);
-            });
+            for (uint32_t i = t; i < c; i += NT) {
+                const uint64_t v = cand[i];
+                const uint32_t kk = (uint32_t)(v >> 32), id = (uint32_t)v;
+                if ((kk >> (32 - kHistBits)) == B && (kk > T || (kk == T && id <= I)))
+                    sel[i] = 1;
+            }
         }
         __syncthreads();
-        compact_bitmap<NT>(bitmap, (uint32_t)nb, blk, (uint32_t)k, S);
+        // chosen ids in list order = ascending ids; thread t owns entries 4t..4t+3
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            cnt += (4u * t + j < c) ? sel[4 * t + j] : 0u;
+        uint32_t pos = wg_exclusive_scan<NT>(cnt, S);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t i = 4u * t + j;
+            if (i < c && sel[i]) {
+                if (pos < (uint32_t)k)
+                    blk[pos] = (int32_t)(uint32_t)cand[i];
+                pos++;
+            }
+        }
     }
-    if (t == 0) {
+    if (t == 0)
         n_sel[0] = k;
-        ws.ctrl[kCandCnt] = 0;
-    }
 }
 
 __global__ void iota_kernel(int32_t *blk, int32_t n, int32_t *n_sel)
@@ -874,12 +933,16 @@ hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_
         return hipGetLastError();
     }
     const int32_t G = (nb + kFilterPerWg - 1) / kFilterPerWg;
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(G), dim3(kThreads), 0, s, scores, nb, k, ws);
+    int32_t head_log2 = 0;  // largest power of two with head * G <= kListMax
+    while (head_log2 < 10 && ((int64_t)2 << head_log2) * G <= kListMax)
+        head_log2++;
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(G), dim3(kThreads), 0, s, scores, nb, k, ws,
+                       1u << head_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kFinalThreads), 0, s, scores, nb, k, blk,
-                       n_sel, ws);
+                       n_sel, ws, head_log2);
     return hipGetLastError();
 }
 

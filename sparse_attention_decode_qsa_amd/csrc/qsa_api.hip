@@ -95,7 +95,7 @@ int check_cfg(const qsa_config *c)
 // different sizes may share one workspace.
 struct Layout {
     size_t ctrl, hist, tickets, zero_end;
-    size_t sure, cand, scores, blk, nsel, part, ksel, vsel, total;
+    size_t sure, cand, rcnt, scores, blk, nsel, part, ksel, vsel, total;
     int64_t ld;  // score row stride
 };
 
@@ -118,7 +118,8 @@ Layout layout(const qsa_config *c, int32_t n_q, int32_t n_ctx)
     const int64_t nb = (int64_t)n_ctx / kBlockTokens + 1;
     L.ld = (int64_t)round_up((size_t)nb, 64);
     L.sure = take(sizeof(int32_t) * (size_t)c->topk_blocks);
-    L.cand = take(sizeof(uint64_t) * (size_t)nb);
+    L.cand = take(sizeof(uint64_t) * round_up((size_t)nb, 1024));
+    L.rcnt = take(sizeof(uint32_t) * (round_up((size_t)nb, 1024) / 1024));
     L.scores = take(sizeof(float) * (size_t)n_q * (size_t)L.ld);
     L.blk = take(sizeof(int32_t) * (size_t)n_q * (size_t)c->topk_blocks);
     L.nsel = take(sizeof(int32_t) * (size_t)n_q);
@@ -142,6 +143,7 @@ TopkWs topk_ws(void *ws, const Layout &L)
     t.hist = at<uint32_t>(ws, L.hist);
     t.sure = at<int32_t>(ws, L.sure);
     t.cand = at<uint64_t>(ws, L.cand);
+    t.rcnt = at<uint32_t>(ws, L.rcnt);
     return t;
 }
 

@@ -105,6 +105,49 @@ __device__ __forceinline__ float wave_sum(float x)
     return (a + b) + (c + d);
 }
 
+// Minimum / maximum of a uint32 over the 64 lanes (every lane gets it).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x)
+{
+    x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor1, 0xf, 0xf, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor2, 0xf, 0xf, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowHalfMirror, 0xf, 0xf, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowMirror, 0xf, 0xf, false));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return min(min(a, b), min(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
+{
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor1, 0xf, 0xf, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor2, 0xf, 0xf, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowHalfMirror, 0xf, 0xf, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowMirror, 0xf, 0xf, false));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 inside each row of
+// 16 lanes (lanes shifted in from outside the row read 0), then the totals of
+// the rows below are added from lanes 15, 31 and 47.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const uint32_t row = lane_id() >> 4;
+    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Rank of this lane among the set lanes of a 64-bit ballot mask.
 __device__ __forceinline__ uint32_t rank_in_mask(uint64_t mask)
 {

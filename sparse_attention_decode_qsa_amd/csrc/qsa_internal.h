@@ -50,9 +50,10 @@ struct TopkWs {
     uint32_t *ctrl;  // kCtrlWords control words (tickets, counters, threshold)
     uint32_t *hist;  // kHistBins
     int32_t *sure;   // up to k entries
-    uint64_t *cand;  // up to nb entries (key << 32 | id)
+    uint64_t *cand;  // nb rounded up to 1024 entries (key << 32 | id), by regions of 1024
+    uint32_t *rcnt;  // entries per region
 };
-// Leaves ws.ctrl cleared.
+// Uses ws.cand and ws.rcnt only; keeps no state between calls.
 hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_t *blk,
                               int32_t *n_sel, TopkWs ws, hipStream_t s);
 hipError_t launch_topk_rows(const float *scores, int32_t n_q, int32_t ld, int32_t pos0,

@@ -114,11 +114,24 @@ def crafted(nb, kind, r):
         return s
     if kind == "narrow":   # everything in one 12-bit bin: candidate path overflows LDS
         return (1.0 + r.random(nb).astype(np.float32) * 1e-3).astype(np.float32)
+    if kind == "ascending":  # every candidate in the last regions of the row
+        return np.sort(r.standard_normal(nb).astype(np.float32) * 45)
+    if kind == "sample_misleads":  # the sampled scores alone sit far above the rest
+        s = r.standard_normal(nb).astype(np.float32)
+        stride = max(64, -(-nb // 1024))
+        s[:40 * stride:stride] = 1000.0
+        return s
+    if kind == "crowded_bin":  # the threshold bin holds more than 1024 keys
+        s = r.standard_normal(nb).astype(np.float32) * 45
+        idx = r.choice(nb, min(1500, nb // 2), replace=False)
+        s[idx] = (1000.0 + r.random(idx.size) * 0.1).astype(np.float32)
+        return s
     raise ValueError(kind)
 
 
 @pytest.mark.parametrize("kind", ["normal", "all_equal", "few_values", "zeros_signed", "nan_inf",
-                                  "tie_at_cut", "narrow"])
+                                  "tie_at_cut", "narrow", "ascending", "sample_misleads",
+                                  "crowded_bin"])
 @pytest.mark.parametrize("nb", [513, 5000, 20000, 40000, 63795, 65536, 70001])
 def test_topk_decode_bit_exact(gpu, kind, nb):
     r = np.random.default_rng(nb + len(kind))
