@@ -43,7 +43,8 @@ struct Scratch {
 
 // Over NBINS (4096 or 256) LDS bins, finds the bin where the count taken from
 // the top reaches need (need >= 1).  res[0] = bin (0xffffffff if the total is
-// below need), res[1] = count in the bins above it, res[2] = total.  All NT
+// below need), res[1] = count in the bins above it, res[2] = total, res[3] =
+// count in the bin.  All NT
 // threads call it; wave 0 does the work: lane l sums bins [l*per, (l+1)*per), a
 // wave scan finds the lane where the count from the top crosses need, and a
 // second wave scan over that lane's bins finds the bin.  hist is 16-byte aligned;
@@ -53,7 +54,10 @@ __device__ void find_from_top(const uint32_t *hist, uint32_t need, Scratch<NT> &
 {
     static_assert(NBINS == 256 || NBINS == 4096, "bins");
     if (threadIdx.x < kWave) {
-        const uint32_t lane = threadIdx.x;
+        // opaque copy of the lane: keeps the compiler from hoisting the 64 bin
+        // addresses out of a caller's loop (they would stay live and spill)
+        uint32_t lane = threadIdx.x;
+        asm volatile("" : "+v"(lane));
         constexpr int per = NBINS / kWave;  // 4 or 64
         uint32_t c = 0;
         if (per == 4) {
@@ -89,10 +93,57 @@ __device__ void find_from_top(const uint32_t *hist, uint32_t need, Scratch<NT> &
             if ((int)lane < per && above2 < need && need <= above2 + h) {
                 S.res[0] = (uint32_t)(L * per + (int)lane);
                 S.res[1] = above2;
+                S.res[3] = h;
             }
             if (lane == 0)
                 S.res[2] = total;
         }
+    }
+    __syncthreads();
+}
+
+// As find_from_top for NBINS = 4 * NT, with every thread taking part: thread t
+// owns bins 4t..4t+3, a work-group prefix sum (wave scans, then the NT/64 wave
+// totals through wtot) gives the count in the bins of higher threads, and the
+// one thread whose bins reach `need` finds the bin.  Sets res[0..3] as
+// find_from_top does.
+template <int NT>
+__device__ void find_from_top_wg(const uint32_t *hist, uint32_t need, Scratch<NT> &S,
+                                 uint32_t *wtot)
+{
+    constexpr int NW = NT / kWave;
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const uint4 v = ((const uint4 *)hist)[t];
+    const uint32_t c = v.x + v.y + v.z + v.w;
+    const uint32_t incl = wave_incl_scan(c);
+    if (lane == kWave - 1)
+        wtot[w] = incl;
+    __syncthreads();
+    uint32_t total = 0, above = 0;
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+        const uint32_t x = wtot[i];
+        total += x;
+        above += i > w ? x : 0u;
+    }
+    above += wtot[w] - incl;  // higher lanes of this wave
+    if (need > total) {
+        if (t == 0) {
+            S.res[0] = 0xffffffffu;
+            S.res[2] = total;
+        }
+    } else if (above < need && need <= above + c) {
+        const uint32_t h[4] = {v.w, v.z, v.y, v.x};  // bins 4t+3 .. 4t
+        uint32_t a = above;
+        int i = 0;
+        while (a + h[i] < need) {
+            a += h[i];
+            i++;
+        }
+        S.res[0] = (uint32_t)(4 * t + 3 - i);
+        S.res[1] = a;
+        S.res[2] = total;
+        S.res[3] = h[i];
     }
     __syncthreads();
 }
@@ -887,6 +938,219 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float *
         n_sel[0] = k;
 }
 
+// ---------------------------------------------------------------- list form
+// The decode step's scan leaves, per work group w, its kListLen best rank keys
+// (in any order, 0 for an empty slot) and its row count.  One 1024-thread work group, thread w holding
+// list w in registers:
+//   1. selection of R*, the k-th largest rank key of the lists: 4096-bucket
+//      histograms over the range of the live score keys (the whole range of the
+//      lists' keys first, then the chosen bucket; equal-width buckets over the
+//      actual range keep the LDS atomics spread out, where fixed float-bit
+//      digits would pile the candidates into a few bins), then digits of the
+//      block id when one key is shared by many entries, until at most 64
+//      entries are live; those are ranked by counting.  Rank keys are distinct
+//      (ids are), so R* is exact and the chosen set is {R >= R*};
+//   2. if a list is full (its work group scored more than kListLen rows) and
+//      its smallest key is >= R* (checked on the per-wave maxima of those
+//      smallest keys, by the wave that finds R*), rows of that work group missing from the list
+//      could outrank R*: the whole score row is selected from instead
+//      (select_row_global).  Otherwise every row outside the lists ranks below
+//      the smallest key of its own list, hence below R*, and the lists hold the
+//      top-k exactly;
+//   3. chosen ids go into an LDS bitmap, compacted in ascending id order.
+constexpr int kSmallRank = 64;  // keys ranked by counting (one per lane of wave 0)
+
+__global__ __launch_bounds__(kFinalThreads) void topk_lists_kernel(const float *__restrict__ scores,
+                                                                   int32_t nb, int32_t k,
+                                                                   CandLists cl, int32_t W,
+                                                                   int32_t *__restrict__ blk,
+                                                                   int32_t *__restrict__ n_sel)
+{
+    constexpr int NT = kFinalThreads;
+    static_assert(kListWgs <= NT, "one list per thread");
+    __shared__ uint32_t bitmap[kMaxBlocks / 32];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2][kHistBins];
+    __shared__ uint64_t cand[kCandCap];
+    __shared__ Scratch<NT> S;
+    __shared__ uint32_t wtot[NT / kWave];
+    __shared__ uint64_t wlast[NT / kWave];
+    __shared__ uint32_t wkey[2][NT / kWave];
+    __shared__ uint64_t rstar;
+    __shared__ uint32_t hidden;
+    const int t = threadIdx.x;
+
+    // one round of loads: this thread's list and row count
+    uint64_t R[kListLen];
+    uint32_t nrows = 0;
+    if (t < W) {
+        const uint4 *src = (const uint4 *)(cl.list + (int64_t)t * kListLen);
+#pragma unroll
+        for (int j = 0; j < kListLen / 2; j++) {
+            const uint4 v = src[j];
+            R[2 * j] = ((uint64_t)v.y << 32) | v.x;
+            R[2 * j + 1] = ((uint64_t)v.w << 32) | v.z;
+        }
+        nrows = cl.rows[t];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kListLen; j++)
+            R[j] = 0ull;
+    }
+    // while they are in flight: clear both histograms and the bitmap
+    ((uint4 *)hist[0])[t] = uint4{0, 0, 0, 0};
+    ((uint4 *)hist[1])[t] = uint4{0, 0, 0, 0};
+    zero_words<NT>(bitmap, ((uint32_t)nb + 31) / 32);
+    if (t == 0)
+        S.cnt = 0;
+    // per wave: the smallest and largest score key of the nonempty entries, and
+    // the largest smallest entry of a full list (for step 2)
+    {
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+        uint64_t last = ~0ull;
+#pragma unroll
+        for (int j = 0; j < kListLen; j++) {
+            const uint32_t key = (uint32_t)(R[j] >> 32);
+            if (R[j] != 0ull) {
+                kmin = min(kmin, key);
+                kmax = max(kmax, key);
+            }
+            last = R[j] < last ? R[j] : last;
+        }
+        if (!(t < W && nrows > (uint32_t)kListLen))
+            last = 0ull;
+        last = wave_max_u64(last);
+        kmin = wave_min_u32(kmin);
+        kmax = wave_max_u32(kmax);
+        if ((t & (kWave - 1)) == 0) {
+            wlast[t / kWave] = last;
+            wkey[0][t / kWave] = kmin;
+            wkey[1][t / kWave] = kmax;
+        }
+    }
+    __syncthreads();
+
+    // 1. select R*.  Key passes: the live keys [lo, lo + span] go into 4096
+    // equal buckets ((key - lo) >> s); the bucket holding the need-th key from
+    // the top becomes the new range, until one key is left or few entries.  If
+    // that key is shared by many entries, id passes follow: the id bits 18..0
+    // (bits 31..19 of ~id are 1 for every id below kMaxBlocks = 2^19) in 8, 8
+    // and 3 bits, with (imask, ival) the low-word bits fixed so far.
+    static_assert(kMaxBlocks == 1 << 19, "id digits cover 19 bits");
+    uint32_t lo = 0xffffffffu, hi_key = 0u;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; i++) {
+        lo = min(lo, wkey[0][i]);
+        hi_key = max(hi_key, wkey[1][i]);
+    }
+    uint32_t span = hi_key - lo;
+    uint32_t imask = 0u, ival = 0u;
+    auto live = [&](uint64_t r) {
+        const uint32_t key = (uint32_t)(r >> 32);
+        return r != 0ull && key >= lo && key - lo <= span && ((uint32_t)r & imask) == ival;
+    };
+    uint32_t need = (uint32_t)k, cnt = 0;
+    bool ok = hi_key >= lo;  // some entry at all
+    int p = 0;
+    while (ok) {
+        const int s = span >= (uint32_t)kHistBins ? 32 - __clz((int)span) - kHistBits : 0;
+        uint32_t *h = hist[p & 1];
+#pragma unroll
+        for (int j = 0; j < kListLen; j++)
+            if (live(R[j]))
+                atomicAdd(&h[((uint32_t)(R[j] >> 32) - lo) >> s], 1u);
+        __syncthreads();
+        find_from_top_wg<NT>(h, need, S, wtot);
+        const uint32_t d = S.res[0];
+        if (d == 0xffffffffu) {  // fewer than k keys in the lists
+            ok = false;
+            break;
+        }
+        need -= S.res[1];
+        cnt = S.res[3];
+        // nobody reads h again in this pass; the next pass uses the other one
+        ((uint4 *)h)[t] = uint4{0, 0, 0, 0};
+        p++;
+        lo += d << s;
+        span = s == 0 ? 0u : min(span - (d << s), (1u << s) - 1u);
+        if (span == 0 || cnt <= (uint32_t)kSmallRank)
+            break;
+    }
+    if (ok && cnt > (uint32_t)kSmallRank) {
+        // one key, many entries: id digits
+        imask = 0xfff80000u;
+        ival = 0xfff80000u;
+        const int shifts[3] = {11, 3, 0};
+        const int widths[3] = {8, 8, 3};
+        for (int q = 0; q < 3; q++) {
+            const int w = widths[q], sh = shifts[q];
+            uint32_t *h = hist[p & 1];
+#pragma unroll
+            for (int j = 0; j < kListLen; j++)
+                if (live(R[j]))
+                    atomicAdd(&h[((uint32_t)R[j] >> sh) & ((1u << w) - 1u)], 1u);
+            __syncthreads();
+            find_from_top<NT, 256>(h, need, S);
+            const uint32_t d = S.res[0];
+            need -= S.res[1];
+            cnt = S.res[3];
+            if (t < 64)
+                ((uint4 *)h)[t] = uint4{0, 0, 0, 0};
+            p++;
+            imask |= ((1u << w) - 1u) << sh;
+            ival |= d << sh;
+            if (cnt <= (uint32_t)kSmallRank)
+                break;
+        }
+    }
+    if (ok) {
+        // the <= 64 live entries; R* is the one with `need - 1` of them above it
+#pragma unroll
+        for (int j = 0; j < kListLen; j++) {
+            if (live(R[j])) {
+                const uint32_t slot = atomicAdd(&S.cnt, 1u);
+                if (slot < (uint32_t)kSmallRank)
+                    cand[slot] = R[j];
+            }
+        }
+        __syncthreads();
+        if (t < kWave) {
+            const uint64_t me = (uint32_t)t < cnt ? cand[t] : 0ull;
+            uint32_t above = 0;
+            for (uint32_t j = 0; j < cnt; j++)
+                above += cand[j] > me ? 1u : 0u;
+            const bool is_rs = (uint32_t)t < cnt && above == need - 1u;
+            if (is_rs)
+                rstar = me;
+            // 2. a full list whose last key is chosen may hide chosen rows
+            const uint64_t last = t < NT / kWave ? wlast[t] : 0ull;
+            const uint64_t rs = __shfl(me, __ffsll((unsigned long long)__ballot(is_rs)) - 1, kWave);
+            const bool hid = __ballot(last >= rs) != 0ull;
+            if (t == 0)
+                hidden = hid ? 1u : 0u;
+        }
+        __syncthreads();
+        const uint64_t rs = rstar;
+        ok = hidden == 0u;
+        if (ok) {
+#pragma unroll
+            for (int j = 0; j < kListLen; j++)
+                if (R[j] >= rs) {
+                    const uint32_t id = rank_id(R[j]);
+                    if (id < (uint32_t)nb)
+                        set_bit(bitmap, id);
+                }
+            __syncthreads();
+            compact_bitmap<NT>(bitmap, (uint32_t)nb, blk, (uint32_t)k, S);
+        }
+    }
+    if (!ok) {
+        __syncthreads();
+        select_row_global<NT>(scores, (uint32_t)nb, k, blk, hist[0], cand, bitmap, S);
+    }
+    if (t == 0)
+        n_sel[0] = k;
+}
+
 __global__ void iota_kernel(int32_t *blk, int32_t n, int32_t *n_sel)
 {
     for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
@@ -943,6 +1207,21 @@ hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_
         return e;
     hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kFinalThreads), 0, s, scores, nb, k, blk,
                        n_sel, ws, head_log2);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,
+                             int32_t n_lists, int32_t *blk, int32_t *n_sel, hipStream_t s)
+{
+    if (nb > kMaxBlocks || n_lists < 1 || n_lists > kListWgs)
+        return hipErrorInvalidValue;
+    if (nb <= k) {
+        const int32_t grid = nb > 0 ? (nb + kThreads - 1) / kThreads : 1;
+        hipLaunchKernelGGL(iota_kernel, dim3(grid), dim3(kThreads), 0, s, blk, nb, n_sel);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(topk_lists_kernel, dim3(1), dim3(kFinalThreads), 0, s, scores, nb, k, cl,
+                       n_lists, blk, n_sel);
     return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ int check_cfg(const qsa_config *c)
 // different sizes may share one workspace.
 struct Layout {
     size_t ctrl, hist, tickets, zero_end;
-    size_t sure, cand, rcnt, scores, blk, nsel, part, ksel, vsel, total;
+    size_t sure, cand, rcnt, lists, lrows, scores, blk, nsel, part, ksel, vsel, total;
     int64_t ld;  // score row stride
 };
 
@@ -120,6 +120,8 @@ Layout layout(const qsa_config *c, int32_t n_q, int32_t n_ctx)
     L.sure = take(sizeof(int32_t) * (size_t)c->topk_blocks);
     L.cand = take(sizeof(uint64_t) * round_up((size_t)nb, 1024));
     L.rcnt = take(sizeof(uint32_t) * (round_up((size_t)nb, 1024) / 1024));
+    L.lists = take(sizeof(uint64_t) * (size_t)kListWgs * kListLen);
+    L.lrows = take(sizeof(uint32_t) * (size_t)kListWgs);
     L.scores = take(sizeof(float) * (size_t)n_q * (size_t)L.ld);
     L.blk = take(sizeof(int32_t) * (size_t)n_q * (size_t)c->topk_blocks);
     L.nsel = take(sizeof(int32_t) * (size_t)n_q);
@@ -330,7 +332,7 @@ int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, i
     const int32_t row = cfg->h_idx * cfg->d_idx;
     if (n_q == 1) {
         HIP_CHECK(launch_score_decode(H(q_idx), H(k_pool), (pos0 + 1) / kBlockTokens, row, scores,
-                                      nullptr, (hipStream_t)stream));
+                                      nullptr, nullptr, nullptr, (hipStream_t)stream));
         return QSA_OK;
     }
     if (ld % 4)
@@ -519,13 +521,17 @@ int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_b
     ap.base = cfg->rope_base;
 
     // 2. scores over the nb complete blocks; the append runs in the same launch
-    // and scores the block it completes
+    // and scores the block it completes; every scan work group leaves its
+    // best kListLen candidates
     float *scores = scores_out ? scores_out : at<float>(ws, L.scores);
-    HIP_CHECK(launch_score_decode(H(q_idx), H(Lb->k_pool), ap.b_lo, (int32_t)row, scores, &ap, s));
+    const CandLists cl{at<uint64_t>(ws, L.lists), at<uint32_t>(ws, L.lrows)};
+    int32_t n_lists = 0;
+    HIP_CHECK(launch_score_decode(H(q_idx), H(Lb->k_pool), ap.b_lo, (int32_t)row, scores, &ap, &cl,
+                                  &n_lists, s));
 
-    // 3. top-k blocks (ascending ids)
+    // 3. top-k blocks (ascending ids) from the candidate lists
     int32_t *blk = blk_out ? blk_out : at<int32_t>(ws, L.blk);
-    HIP_CHECK(launch_topk_decode(scores, nb, k, blk, at<int32_t>(ws, L.nsel), topk_ws(ws, L), s));
+    HIP_CHECK(launch_topk_lists(scores, nb, k, cl, n_lists, blk, at<int32_t>(ws, L.nsel), s));
 
     // 4-5. attention over the chosen cells plus the tail
     AttnArgs a = attn_base(cfg);

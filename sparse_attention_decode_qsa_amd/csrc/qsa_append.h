@@ -9,29 +9,32 @@ namespace qsa {
 
 constexpr int kAppendThreads = 256;
 
-// Copies of AppendArgs::seg by work group wg of nwg (16-byte units, coalesced).
+// Copies of AppendArgs::seg by work group wg of nwg, NT threads each (16-byte
+// units, coalesced).
+template <int NT = kAppendThreads>
 __device__ __forceinline__ void append_copy(const AppendArgs &a, int wg, int nwg)
 {
-    const int64_t stride = (int64_t)nwg * kAppendThreads;
+    const int64_t stride = (int64_t)nwg * NT;
 #pragma unroll
     for (int s = 0; s < 3; s++) {
         const uint4 *src = (const uint4 *)a.seg[s].src;
         uint4 *dst = (uint4 *)a.seg[s].dst;
-        for (int64_t i = (int64_t)wg * kAppendThreads + threadIdx.x; i < a.seg[s].n16; i += stride)
+        for (int64_t i = (int64_t)wg * NT + threadIdx.x; i < a.seg[s].n16; i += stride)
             dst[i] = src[i];
     }
 }
 
-// Pooled rows of blocks [b0, b0 + nbk) by one work group of kAppendThreads.
+// Pooled rows of blocks [b0, b0 + nbk) by one work group of NT threads.
 // cs: LDS for nbk * d/2 (cos, sin) pairs.  row_lds (may be NULL, nbk == 1): the
 // pooled row is also left there in binary16.  A block's tokens below n_before
 // come from k_raw, the others from k_new.
+template <int NT = kAppendThreads>
 __device__ void append_pool(const AppendArgs &a, int32_t b0, int32_t nbk, f32x2 *cs, h16 *row_lds)
 {
     const int32_t d = a.d, H = a.H, half = d / 2;
     const int64_t row = (int64_t)H * d;
     // RoPE angles of pair i at block position 4b: 4b * base^(-2i/d), in fp64.
-    for (int e = threadIdx.x; e < nbk * half; e += kAppendThreads) {
+    for (int e = threadIdx.x; e < nbk * half; e += NT) {
         const int bl = e / half, i = e - bl * half;
         const double pos = (double)kBlockTokens * (double)(b0 + bl);
         const double inv = pow((double)a.base, -2.0 * (double)i / (double)d);
@@ -44,7 +47,7 @@ __device__ void append_pool(const AppendArgs &a, int32_t b0, int32_t nbk, f32x2 
     // The d/8 units of one head sit in consecutive lanes of one wave.
     const int32_t qph = d / 8;
     const int32_t units = nbk * H * qph;
-    for (int32_t ub = 0; ub < units; ub += kAppendThreads) {
+    for (int32_t ub = 0; ub < units; ub += NT) {
         const int32_t u = ub + threadIdx.x;
         const bool active = u < units;
         const int32_t uu = active ? u : 0;

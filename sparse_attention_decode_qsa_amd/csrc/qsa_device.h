@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace qsa {
 
 typedef _Float16 h16;
@@ -28,6 +30,16 @@ __device__ __forceinline__ uint32_t score_key(float s)
         u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// Total order of (score, block id) pairs as one 64-bit word: the score key in
+// the high half, the complemented id in the low half, so a larger word ranks
+// higher and equal scores rank the lower id first.  0 ranks below every pair
+// and marks an empty slot.
+__device__ __forceinline__ uint64_t rank_key(float s, uint32_t id)
+{
+    return ((uint64_t)score_key(s) << 32) | (uint32_t)~id;
+}
+__device__ __forceinline__ uint32_t rank_id(uint64_t r) { return ~(uint32_t)r; }
 
 __device__ __forceinline__ float dot8(h16x8 a, h16x8 b, float acc)
 {
@@ -130,6 +142,27 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
     const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
     const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
     return max(max(a, b), max(c, d));
+}
+
+// Maximum of a uint64 over the 64 lanes (every lane gets it).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x)
+{
+    auto step = [](uint64_t v, uint64_t o) { return o > v ? o : v; };
+    auto dpp64 = [](uint64_t v, auto ctrl) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, decltype(ctrl)::value, 0xf, 0xf, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), decltype(ctrl)::value, 0xf, 0xf, false);
+        return ((uint64_t)hi << 32) | lo;
+    };
+    x = step(x, dpp64(x, std::integral_constant<int, kDppQuadXor1>{}));
+    x = step(x, dpp64(x, std::integral_constant<int, kDppQuadXor2>{}));
+    x = step(x, dpp64(x, std::integral_constant<int, kDppRowHalfMirror>{}));
+    x = step(x, dpp64(x, std::integral_constant<int, kDppRowMirror>{}));
+    auto rl = [](uint64_t v, int l) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+        return ((uint64_t)hi << 32) | lo;
+    };
+    return step(step(rl(x, 0), rl(x, 16)), step(rl(x, 32), rl(x, 48)));
 }
 
 // Inclusive prefix sum over the 64 lanes: shifts of 1, 2, 4, 8 inside each row of

@@ -35,11 +35,27 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 
+// ---- decode top-k candidate lists (written by the scan, read by the top-k) ----
+// Each work group of the decode-step scan keeps the kListLen highest rank keys
+// (rank_key) of the rows it scored, in any order (0 = empty slot), and the
+// number of rows it scored.  The global top-k is contained in the union of the
+// lists unless some work group scored more than kListLen rows and the smallest
+// entry of its list is itself chosen; the top-k kernel checks exactly that.
+constexpr int kListLen = 8;
+constexpr int kListWgs = 1024;  // lists at most (one per thread of the top-k kernel)
+struct CandLists {
+    uint64_t *list;  // [kListWgs][kListLen]
+    uint32_t *rows;  // [kListWgs]
+};
+
 // ---- scores (k_score.hip) ---------------------------------------------------
-// ap (may be NULL): append work run in the same launch (at most one completed
-// block, block nb; scores[nb] is then written too).
+// Stand-alone scan (qsa_index_score, n_q = 1): scores[0, nb).
+// Decode-step scan (ap and cl non-NULL): the append work runs in the same launch
+// (at most one completed block, block nb; scores[nb] is then written too) and
+// every work group writes its candidate list; *n_lists gets the list count.
 hipError_t launch_score_decode(const h16 *q, const h16 *pool, int32_t nb, int32_t row_elems,
-                               float *scores, const AppendArgs *ap, hipStream_t s);
+                               float *scores, const AppendArgs *ap, const CandLists *cl,
+                               int32_t *n_lists, hipStream_t s);
 hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h16 *pool,
                                 int32_t row_elems, float *scores, int32_t ld, hipStream_t s);
 
@@ -56,6 +72,10 @@ struct TopkWs {
 // Uses ws.cand and ws.rcnt only; keeps no state between calls.
 hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_t *blk,
                               int32_t *n_sel, TopkWs ws, hipStream_t s);
+// Top-k of one row from the scan's candidate lists (n_lists of them); selects
+// from the whole score row when the lists cannot be shown to hold the top-k.
+hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,
+                             int32_t n_lists, int32_t *blk, int32_t *n_sel, hipStream_t s);
 hipError_t launch_topk_rows(const float *scores, int32_t n_q, int32_t ld, int32_t pos0,
                             int32_t k, int32_t *blk, int32_t *n_sel, hipStream_t s);
 int32_t topk_max_blocks();

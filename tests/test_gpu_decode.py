@@ -289,3 +289,71 @@ def test_decode_step_255181_planted(gpu):
     assert_pool_close(host(g.k_pool[torch.from_numpy(rows).cuda()]), o.pooled[rows])
     b = check_step(w, L, cfg, g, o, n0, 0, qb.QSA_STEP_FUSED_GATHER)
     assert set(L["planted"].tolist()) <= set(b.tolist())
+
+
+# ------------------------------------------------------------------ decode top-k on clustered scores
+def clustered_values(pattern, nb, r):
+    """Per-block values v_b; a pooled row of all v_b against an all-ones query scores
+    exactly 2048 * v_b, on the GPU and in the oracle."""
+    v = (np.round(r.standard_normal(nb) * 6.4) / 64).astype(np.float16)  # no subnormals
+    if pattern == "one_scan_group":
+        # the blocks b with b mod 4092 in [20, 24) on top: the decode scan's 1023 work
+        # groups read runs of 4 neighbouring rows, so these all belong to one work
+        # group, whose 8-entry candidate list cannot hold them (full-row fallback)
+        sel = (np.arange(nb) % 4092 >= 20) & (np.arange(nb) % 4092 < 24)
+        v[sel] = (4.0 + np.arange(sel.sum()) / 64).astype(np.float16)
+    elif pattern == "recent_window":
+        v[-700:] = np.linspace(1.0, 2.0, 700).astype(np.float16)
+    elif pattern == "ascending":
+        v = np.sort(v)
+    elif pattern == "all_equal":
+        v[:] = 1.0
+    elif pattern == "few_values":
+        v = r.integers(-2, 3, nb).astype(np.float16)
+    return v
+
+
+@pytest.mark.parametrize("pattern", ["one_scan_group", "recent_window", "ascending", "all_equal",
+                                     "few_values"])
+def test_decode_step_clustered_scores(gpu, pattern):
+    nb0, H, d = 20000, 16, 128
+    n_before = 4 * nb0 + 3        # the step completes block nb0 (scored by the append)
+    w = small(n_before + 1)
+    cfg = cfg_of(w)
+    r = np.random.default_rng(len(pattern))
+    v = clustered_values(pattern, nb0, r)
+    pooled = np.zeros((w.cap_tokens // 4, H, d), np.float16)
+    pooled[:nb0] = v[:, None, None]
+    raw = np.zeros((w.cap_tokens, H, d), np.float16)
+    raw[4 * nb0:n_before] = synth.normal_f16(60, (3, H, d))
+    K = synth.normal_f16(61, (w.cap_tokens, 4, 128))
+    V = synth.normal_f16(62, (w.cap_tokens, 4, 128))
+    K[n_before:] = 0
+    V[n_before:] = 0
+    q_idx = np.ones((H, d), np.float16)
+    q = synth.normal_f16(63, (32, 128))
+    k_idx_new = synth.normal_f16(64, (H, d))
+    k_new, v_new = synth.normal_f16(65, (4, 128)), synth.normal_f16(66, (4, 128))
+
+    g = qb.Layer(cfg)
+    g.k_pool.copy_(dev(pooled))
+    g.k_raw.copy_(dev(raw))
+    g.k_cache.copy_(dev(K))
+    g.v_cache.copy_(dev(V))
+    out = torch.empty((32, 128), device="cuda")
+    scores = torch.empty(nb0 + 1, device="cuda")
+    blk = torch.full((512,), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, 1, w.cap_tokens)
+    qb.qsa_decode_step(cfg, g, n_before, dev(q_idx), dev(k_idx_new), dev(q), dev(k_new),
+                       dev(v_new), out, ws, scores_out=scores, blk_out=blk)
+    ref = O.decode_step(shape_of(w), raw, pooled, K, V, n_before, q_idx, k_idx_new, q, k_new,
+                        v_new)
+    s_gpu = host(scores)
+    # complete blocks score exactly; the appended one within the score bound
+    assert np.array_equal(s_gpu[:nb0], 2048.0 * v.astype(np.float32))
+    assert abs(s_gpu[nb0] - ref["scores64"][nb0]) <= SCORE_REL * np.max(np.abs(ref["scores64"]))
+    b_gpu = host(blk)
+    assert np.array_equal(b_gpu, O.topk_sort(s_gpu, 512))
+    assert np.array_equal(b_gpu, ref["blk"])
+    ref_out = O.attn_cells(q, K, V, O.cells(b_gpu, n_before + 1), w.scale)
+    assert_attn_close(host(out), ref_out)
