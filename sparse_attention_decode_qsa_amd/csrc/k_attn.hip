@@ -440,6 +440,26 @@ hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_combine(const float *part, int32_t hq, int32_t splits, int32_t dv, float *out,
+                          hipStream_t s)
+{
+    if (splits < 1 || splits > kAttnMaxSplits)
+        return hipErrorInvalidValue;
+    const dim3 grid((uint32_t)hq, 1);
+    switch (dv) {
+    case 64:
+        hipLaunchKernelGGL((attn_combine_kernel<64>), grid, dim3(kCombThreads), 0, s, part, hq,
+                           splits, nullptr, 0, out);
+        break;
+    case 128:
+        hipLaunchKernelGGL((attn_combine_kernel<128>), grid, dim3(kCombThreads), 0, s, part, hq,
+                           splits, nullptr, 0, out);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gather(const int32_t *blk, int32_t n_blk, int32_t n_tokens, const h16 *k_cache,
                          const h16 *v_cache, int32_t k_row16, int32_t v_row16, h16 *k_sel,
                          h16 *v_sel, hipStream_t s)

@@ -1,0 +1,306 @@
+// Decode-step tail in one launch: block-domain top-k, then attention over the
+// chosen cells only (Qiita part 10, "QSAとQSA indexerについて": keep the
+// highest-scoring blocks plus the incomplete tail block; "selected QSA K/V
+// gather（COMMON-005）": attention over those cells; the COMMON-006 section:
+// selection in the block domain).
+//
+// Grid: (split, KV head), 1024 threads.  Every work group first selects the
+// same top-k blocks from the decode scan's candidate lists (lists_select; the
+// whole score row if the lists are not enough), in the deterministic order of
+// the selection (attention does not depend on the order of its cells); the
+// threads holding the chosen blocks of this work group's split write its 64
+// cell tokens to LDS.  Then all 16 waves attend those 64 cells for one KV head:
+// thread (cell, 16-byte piece) loads one piece of the cell's K row and one of
+// its V row, dots the K piece with the G query heads and the partial dots of a
+// cell meet by DPP across its lanes; wave h runs the softmax of head h (log2
+// domain); thread (head, dim) sums P x V from LDS; each head leaves an (m, l, o)
+// partial for attn_combine_kernel.  Selecting in every work group costs a few
+// microseconds of LDS work but saves a kernel boundary and a round trip through
+// global memory for the chosen ids.
+//
+// Work group (0, 0) also writes blk_out (ascending ids, through an LDS bitmap)
+// and n_sel when asked for.
+#include "qsa_select.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kNT = kSelThreads;  // 16 waves
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct TailArgs {
+    CandLists cl;
+    int32_t n_lists;
+    const float *scores;  // the score row (fallback selection)
+    int32_t n_tokens;     // N: the context after the step's append
+    int32_t k;
+    const h16 *q;         // [hq][D]
+    const h16 *kc;        // [N][hkv][D]
+    const h16 *vc;        // [N][hkv][DV]
+    int32_t hq, hkv;
+    float scale;
+    int32_t splits;       // ceil(cells / 64)
+    float *part;          // [hq][splits][DV + 2]
+    int32_t *blk_out;     // optional
+    int32_t *n_sel;       // optional
+};
+
+template <int G, int D, int DV>
+struct alignas(16) TailLds {
+    union alignas(16) {
+        struct {
+            uint32_t bitmap[kMaxBlocks / 32];
+            uint64_t cand[kCandCap];
+        } sel;  // the fallback selection and the blk_out sort
+        struct {
+            alignas(16) h16 vs[kAttnChunk * DV];
+            alignas(16) float ps[G][kAttnChunk];
+            float ml[G][2];
+        } att;
+    } u;
+    ListSelLds L;
+    alignas(16) h16 qs[G * D];
+    alignas(16) int32_t ids[kMaxTopk];
+    alignas(16) int32_t toks[kAttnChunk];
+    uint32_t wsum[kNT / kWave];
+};
+
+// Sum over aligned groups of W lanes (W = 8 or 16) by DPP within 16-lane rows.
+template <int W>
+__device__ __forceinline__ float row_group_sum(float x)
+{
+    static_assert(W == 8 || W == 16, "group");
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    x += dpp<kDppRowHalfMirror>(x);
+    if (W == 16)
+        x += dpp<kDppRowMirror>(x);
+    return x;
+}
+
+template <int G, int D, int DV>
+__global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
+{
+    constexpr int PK = D / 8;                  // 16-byte pieces per K row
+    constexpr int PV = DV / 8;                 // 16-byte pieces per V row
+    static_assert(PK == 8 || PK == 16, "K row pieces");
+    static_assert(kAttnChunk * PK <= kNT && kAttnChunk * PV <= kNT, "one piece per thread");
+    static_assert(G <= kNT / kWave, "one wave per head in the softmax");
+
+    __shared__ TailLds<G, D, DV> sm;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    const int split = blockIdx.x, g = blockIdx.y;
+    const int32_t N = a.n_tokens, nb = N / kBlockTokens;
+    const int32_t nsel = nb < a.k ? nb : a.k;
+    const int32_t cells = kBlockTokens * nsel + (N - kBlockTokens * nb);
+    const int32_t c_lo = split * kAttnChunk;       // this split's cells
+    const int32_t b_lo = c_lo / kBlockTokens;      // its chosen-block positions
+    const int32_t b_hi = b_lo + kAttnChunk / kBlockTokens;
+
+    // the query rows of this KV head (independent of the selection)
+    const h16 *qrow = a.q + (int64_t)g * G * D;
+    for (int i = t; i < G * D / 8; i += kNT)
+        ((h16x8 *)sm.qs)[i] = ((const h16x8 *)qrow)[i];
+    // the split's tail cells (the incomplete block, after the chosen ones)
+    if (t < kAttnChunk) {
+        const int32_t c = c_lo + t;
+        sm.toks[t] = (c >= kBlockTokens * nsel && c < cells)
+                         ? kBlockTokens * nb + (c - kBlockTokens * nsel)
+                         : -1;
+    }
+    __syncthreads();
+    // the chosen blocks; position i goes to cells 4i .. 4i + 3
+    auto place = [&](int32_t pos, int32_t id) {
+        if (pos >= b_lo && pos < b_hi) {
+#pragma unroll
+            for (int e = 0; e < kBlockTokens; e++)
+                sm.toks[(pos - b_lo) * kBlockTokens + e] = kBlockTokens * id + e;
+        }
+    };
+
+    // ---- 1. selection
+    const bool want_blk = a.blk_out && blockIdx.x == 0 && blockIdx.y == 0;
+    if (nb <= a.k) {
+        for (int32_t i = t; i < nb; i += kNT) {
+            place(i, i);
+            if (want_blk)
+                sm.ids[i] = i;
+        }
+    } else {
+        uint64_t R[kListLen];
+        uint32_t nrows;
+        load_list(a.cl, a.n_lists, R, &nrows);
+        uint64_t rs = 0;
+        if (lists_select(R, nrows, t < a.n_lists, (uint32_t)a.k, sm.L, &rs)) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int j = 0; j < kListLen; j++)
+                c += R[j] >= rs ? 1u : 0u;
+            // exclusive prefix over the work group: wave scans, one barrier, then
+            // the totals of the waves below (sm.wsum is written only here)
+            const uint32_t incl = wave_incl_scan(c);
+            if (lane == kWave - 1)
+                sm.wsum[wave] = incl;
+            __syncthreads();
+            uint32_t pos = incl - c;
+            for (int i = 0; i < wave; i++)
+                pos += sm.wsum[i];
+#pragma unroll
+            for (int j = 0; j < kListLen; j++)
+                if (R[j] >= rs) {
+                    uint32_t id = rank_id(R[j]);
+                    id = id < (uint32_t)nb ? id : 0u;
+                    if (pos < (uint32_t)a.k) {
+                        place((int32_t)pos, (int32_t)id);
+                        if (want_blk)
+                            sm.ids[pos] = (int32_t)id;
+                    }
+                    pos++;
+                }
+        } else {
+            __syncthreads();
+            select_row_global<kNT>(a.scores, (uint32_t)nb, a.k, sm.ids, sm.L.hist[0],
+                                   sm.u.sel.cand, sm.u.sel.bitmap, sm.L.S);
+            __syncthreads();
+            for (int32_t i = t; i < nsel; i += kNT)
+                place(i, sm.ids[i]);
+        }
+    }
+    __syncthreads();
+
+    if (want_blk) {
+        if (a.n_sel && t == 0)
+            a.n_sel[0] = nsel;
+        zero_words<kNT>(sm.u.sel.bitmap, ((uint32_t)nb + 31) / 32);
+        __syncthreads();
+        for (int32_t i = t; i < nsel; i += kNT)
+            set_bit(sm.u.sel.bitmap, (uint32_t)sm.ids[i]);
+        __syncthreads();
+        compact_bitmap<kNT>(sm.u.sel.bitmap, (uint32_t)nb, a.blk_out, (uint32_t)a.k, sm.L.S);
+        __syncthreads();  // the bitmap shares LDS with the attention arrays
+    }
+
+    // ---- 2. attention over the split's 64 cells for KV head g
+    const int64_t k_tok = (int64_t)a.hkv * D, v_tok = (int64_t)a.hkv * DV;
+    // K: thread (cell, piece); V: thread (cell, piece); both loads in flight
+    const int kc = t / PK, kp = t % PK;
+    const int vc = t / PV, vp = t % PV;
+    const bool k_on = kc < kAttnChunk, v_on = vc < kAttnChunk;
+    const int32_t ktok = k_on ? sm.toks[kc] : -1;
+    const int32_t vtok = v_on ? sm.toks[vc] : -1;
+    h16x8 kv = h16x8{0, 0, 0, 0, 0, 0, 0, 0}, vv = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (ktok >= 0)
+        kv = *(const h16x8 *)(a.kc + (int64_t)ktok * k_tok + (int64_t)g * D + kp * 8);
+    if (vtok >= 0)
+        vv = *(const h16x8 *)(a.vc + (int64_t)vtok * v_tok + (int64_t)g * DV + vp * 8);
+    const float sl2 = a.scale * kLog2e;
+    {
+        float acc[G];
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            acc[h] = dot8(*(const h16x8 *)&sm.qs[h * D + kp * 8], kv, 0.f);
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            acc[h] = row_group_sum<PK>(acc[h]);
+        if (k_on && kp == 0) {
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                sm.u.att.ps[h][kc] = ktok >= 0 ? acc[h] * sl2 : -INFINITY;
+        }
+    }
+    if (v_on)
+        *(h16x8 *)&sm.u.att.vs[vc * DV + vp * 8] = vv;
+    __syncthreads();
+
+    // softmax of head `wave` over the 64 cells (lane = cell); every split has
+    // at least one cell, so the maximum is finite
+    if (wave < G) {
+        const float s = sm.u.att.ps[wave][lane];
+        const float m = wave_max(s);
+        const float p = (s == -INFINITY) ? 0.f : exp2f(s - m);
+        sm.u.att.ps[wave][lane] = p;
+        const float l = wave_sum(p);
+        if (lane == 0) {
+            sm.u.att.ml[wave][0] = m;
+            sm.u.att.ml[wave][1] = l;
+        }
+    }
+    __syncthreads();
+
+    // thread (head, dim): o = sum over cells of p x v; cells past the end have
+    // p = 0 and zeroed V rows
+    for (int o = t; o < G * DV; o += kNT) {
+        const int h = o / DV, d = o % DV;
+        float acc = 0.f;
+#pragma unroll 4
+        for (int c4 = 0; c4 < kAttnChunk; c4 += 4) {
+            const f32x4 p4 = *(const f32x4 *)&sm.u.att.ps[h][c4];
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                acc += p4[u] * (float)sm.u.att.vs[(c4 + u) * DV + d];
+        }
+        float *pb = a.part + (((int64_t)g * G + h) * a.splits + split) * (DV + 2);
+        if (d == 0) {
+            pb[0] = sm.u.att.ml[h][0];
+            pb[1] = sm.u.att.ml[h][1];
+        }
+        pb[2 + d] = acc;
+    }
+}
+
+template <int D, int DV>
+hipError_t launch_d(const TailArgs &a, int G, hipStream_t s)
+{
+    const dim3 grid((uint32_t)a.splits, (uint32_t)a.hkv);
+    switch (G) {
+    case 1: hipLaunchKernelGGL((step_tail_kernel<1, D, DV>), grid, dim3(kNT), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((step_tail_kernel<2, D, DV>), grid, dim3(kNT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((step_tail_kernel<4, D, DV>), grid, dim3(kNT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((step_tail_kernel<8, D, DV>), grid, dim3(kNT), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((step_tail_kernel<16, D, DV>), grid, dim3(kNT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_step_tail(const StepTail &st, hipStream_t s)
+{
+    if (st.n_tokens < 1 || st.k < 1 || st.k > kMaxTopk || st.n_tokens / kBlockTokens > kMaxBlocks ||
+        st.n_lists < 1 || st.n_lists > kListWgs || st.hq % st.hkv)
+        return hipErrorInvalidValue;
+    TailArgs a;
+    a.cl = st.cl;
+    a.n_lists = st.n_lists;
+    a.scores = st.scores;
+    a.n_tokens = st.n_tokens;
+    a.k = st.k;
+    a.q = st.q;
+    a.kc = st.k_cache;
+    a.vc = st.v_cache;
+    a.hq = st.hq;
+    a.hkv = st.hkv;
+    a.scale = st.scale;
+    const int32_t nb = st.n_tokens / kBlockTokens;
+    const int32_t cells = kBlockTokens * (nb < st.k ? nb : st.k) + st.n_tokens % kBlockTokens;
+    a.splits = (cells + kAttnChunk - 1) / kAttnChunk;
+    if (a.splits > kAttnMaxSplits)
+        return hipErrorInvalidValue;
+    a.part = st.part;
+    a.blk_out = st.blk_out;
+    a.n_sel = st.n_sel;
+    const int G = st.hq / st.hkv;
+    hipError_t e;
+    if (st.d == 128 && st.dv == 128)
+        e = launch_d<128, 128>(a, G, s);
+    else if (st.d == 64 && st.dv == 64)
+        e = launch_d<64, 64>(a, G, s);
+    else
+        return hipErrorInvalidValue;
+    if (e != hipSuccess)
+        return e;
+    return launch_combine(st.part, st.hq, a.splits, st.dv, st.out, s);
+}
+
+}  // namespace qsa

@@ -2,309 +2,24 @@
 // "QSAとQSA indexerについて": keep the highest-scoring blocks; "block-domain
 // top-k（COMMON-006）実装は見送り": select pools, then expand only the chosen ones).
 //
-// Selection is a radix select on the order-preserving 32-bit key of each fp32
-// score (score_key), made exact and deterministic:
-//   1. a 4096-bin histogram of the top 12 key bits finds the bin B that holds
-//      the k-th largest key; every block in a higher bin is chosen;
-//   2. the blocks of bin B are candidates; 8/8/4-bit digit passes over them find
-//      the exact k-th key T, then passes over block ids find the largest id I
-//      still chosen among keys equal to T (equal scores go to lower ids);
-//   3. chosen = key > T, or key == T and id <= I.  The chosen ids are set in an
-//      LDS bitmap and compacted in id order, so the output is ascending.
-// Atomics only count (histograms, list slots); the result never depends on
-// their order.
-//
-// Two forms:
-//   * rows: one work group per score row (prefill chunks);
-//   * decode: one long row spread over G work groups in two launches
-//     (histogram, then candidate extraction); the last work group to finish each
-//     launch (an atomic ticket) does the serial part, and restores the
-//     workspace words it used to zero.
+// Forms:
+//   * register form (prefill rows up to 65,536 blocks): one work group per row,
+//     the row's keys held in registers;
+//   * rows form (longer prefill rows): one work group per row, straight from
+//     global memory (select_row_global);
+//   * list form (one decode row): the row's candidate lists (written by the
+//     decode scan, or built from a score array by score_lists_kernel) and one
+//     1024-thread work group running lists_select, with select_row_global as
+//     the exact fallback.
+// Ids come out in ascending order; equal scores go to the lower id.
 #include <mutex>
 
-#include "qsa_internal.h"
+#include "qsa_select.h"
 
 namespace qsa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCandCap = 4096;
-constexpr int kMaxBlocks = 1 << 19;  // bitmap of 64 KiB in LDS
-
-
-template <int NT>
-struct Scratch {
-    uint32_t tmp[NT];
-    uint32_t res[4];
-    uint32_t cnt;
-    uint32_t cnt2;
-    uint32_t flag;
-};
-
-// Over NBINS (4096 or 256) LDS bins, finds the bin where the count taken from
-// the top reaches need (need >= 1).  res[0] = bin (0xffffffff if the total is
-// below need), res[1] = count in the bins above it, res[2] = total, res[3] =
-// count in the bin.  All NT
-// threads call it; wave 0 does the work: lane l sums bins [l*per, (l+1)*per), a
-// wave scan finds the lane where the count from the top crosses need, and a
-// second wave scan over that lane's bins finds the bin.  hist is 16-byte aligned;
-// NBINS is 256 or 4096.
-template <int NT, int NBINS>
-__device__ void find_from_top(const uint32_t *hist, uint32_t need, Scratch<NT> &S)
-{
-    static_assert(NBINS == 256 || NBINS == 4096, "bins");
-    if (threadIdx.x < kWave) {
-        // opaque copy of the lane: keeps the compiler from hoisting the 64 bin
-        // addresses out of a caller's loop (they would stay live and spill)
-        uint32_t lane = threadIdx.x;
-        asm volatile("" : "+v"(lane));
-        constexpr int per = NBINS / kWave;  // 4 or 64
-        uint32_t c = 0;
-        if (per == 4) {
-            const uint4 v = *(const uint4 *)(hist + lane * 4);
-            c = v.x + v.y + v.z + v.w;
-        } else {
-            // rotated order: at step i the 64 lanes read 64 different banks; all
-            // loads are issued before the sum
-            uint32_t h[per];
-#pragma unroll
-            for (int i = 0; i < per; i++)
-                h[i] = hist[lane * per + ((i + (int)lane) & (per - 1))];
-#pragma unroll
-            for (int i = 0; i < per; i++)
-                c += h[i];
-        }
-        const uint32_t incl = wave_incl_scan(c);
-        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-        const uint32_t above = total - incl;  // in the bins of the lanes above
-        if (need > total) {
-            if (lane == 0) {
-                S.res[0] = 0xffffffffu;
-                S.res[2] = total;
-            }
-        } else {
-            const uint64_t m = __ballot(above < need && need <= above + c);
-            const int L = __ffsll((unsigned long long)m) - 1;
-            const uint32_t aboveL = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
-            const uint32_t h = ((int)lane < per) ? hist[L * per + (int)lane] : 0u;
-            const uint32_t incl2 = wave_incl_scan(h);
-            const uint32_t tot2 = (uint32_t)__builtin_amdgcn_readlane((int)incl2, kWave - 1);
-            const uint32_t above2 = aboveL + (tot2 - incl2);
-            if ((int)lane < per && above2 < need && need <= above2 + h) {
-                S.res[0] = (uint32_t)(L * per + (int)lane);
-                S.res[1] = above2;
-                S.res[3] = h;
-            }
-            if (lane == 0)
-                S.res[2] = total;
-        }
-    }
-    __syncthreads();
-}
-
-// As find_from_top for NBINS = 4 * NT, with every thread taking part: thread t
-// owns bins 4t..4t+3, a work-group prefix sum (wave scans, then the NT/64 wave
-// totals through wtot) gives the count in the bins of higher threads, and the
-// one thread whose bins reach `need` finds the bin.  Sets res[0..3] as
-// find_from_top does.
-template <int NT>
-__device__ void find_from_top_wg(const uint32_t *hist, uint32_t need, Scratch<NT> &S,
-                                 uint32_t *wtot)
-{
-    constexpr int NW = NT / kWave;
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const uint4 v = ((const uint4 *)hist)[t];
-    const uint32_t c = v.x + v.y + v.z + v.w;
-    const uint32_t incl = wave_incl_scan(c);
-    if (lane == kWave - 1)
-        wtot[w] = incl;
-    __syncthreads();
-    uint32_t total = 0, above = 0;
-#pragma unroll
-    for (int i = 0; i < NW; i++) {
-        const uint32_t x = wtot[i];
-        total += x;
-        above += i > w ? x : 0u;
-    }
-    above += wtot[w] - incl;  // higher lanes of this wave
-    if (need > total) {
-        if (t == 0) {
-            S.res[0] = 0xffffffffu;
-            S.res[2] = total;
-        }
-    } else if (above < need && need <= above + c) {
-        const uint32_t h[4] = {v.w, v.z, v.y, v.x};  // bins 4t+3 .. 4t
-        uint32_t a = above;
-        int i = 0;
-        while (a + h[i] < need) {
-            a += h[i];
-            i++;
-        }
-        S.res[0] = (uint32_t)(4 * t + 3 - i);
-        S.res[1] = a;
-        S.res[2] = total;
-        S.res[3] = h[i];
-    }
-    __syncthreads();
-}
-
-// Candidate sources: each calls f(key, id) for every block of bin B.
-template <int NT>
-struct LdsCands {
-    const uint64_t *c;
-    uint32_t n;
-    template <class F>
-    __device__ void each(F f) const
-    {
-        for (uint32_t i = threadIdx.x; i < n; i += NT)
-            f((uint32_t)(c[i] >> 32), (uint32_t)c[i]);
-    }
-};
-
-template <int NT>
-struct GlobalCands {
-    const uint64_t *c;
-    uint32_t n;
-    template <class F>
-    __device__ void each(F f) const
-    {
-        for (uint32_t i = threadIdx.x; i < n; i += NT) {
-            const uint64_t v = c[i];
-            f((uint32_t)(v >> 32), (uint32_t)v);
-        }
-    }
-};
-
-template <int NT>
-struct RowCands {
-    const float *row;
-    uint32_t nb;
-    uint32_t bin;
-    template <class F>
-    __device__ void each(F f) const
-    {
-        for (uint32_t i = threadIdx.x; i < nb; i += NT) {
-            const uint32_t key = score_key(row[i]);
-            if ((key >> (32 - kHistBits)) == bin)
-                f(key, i);
-        }
-    }
-};
-
-// Exact threshold among the candidates: on return S.res[0] = T (key), S.res[1]
-// = I (largest chosen id among keys equal to T).
-template <int NT, class Src>
-__device__ void resolve(const Src &src, uint32_t bin, uint32_t need, uint32_t nb, uint32_t *h256,
-                        Scratch<NT> &S)
-{
-    uint32_t prefix = bin;
-    int shift = 32 - kHistBits;
-    const int widths[3] = {8, 8, 4};
-    uint32_t last_count = 0;
-    for (int p = 0; p < 3; p++) {
-        const int w = widths[p];
-        shift -= w;
-        if (threadIdx.x < 256)
-            h256[threadIdx.x] = 0;
-        __syncthreads();
-        const uint32_t pf = prefix, sh = (uint32_t)shift, mask = (1u << w) - 1u;
-        src.each([&](uint32_t key, uint32_t) {
-            if ((key >> (sh + w)) == pf)
-                atomicAdd(&h256[(key >> sh) & mask], 1u);
-        });
-        __syncthreads();
-        find_from_top<NT, 256>(h256, need, S);
-        const uint32_t d = S.res[0];
-        need -= S.res[1];
-        last_count = h256[d];
-        prefix = (prefix << w) | d;
-        __syncthreads();
-    }
-    const uint32_t T = prefix;
-    uint32_t I = 0xffffffffu;
-    if (need < last_count) {
-        // the `need` lowest ids among keys equal to T
-        const int nbits = 32 - __clz((int)(nb - 1));
-        const int top = ((nbits + 7) / 8) * 8;
-        uint32_t ip = 0;
-        for (int sh = top - 8; sh >= 0; sh -= 8) {
-            if (threadIdx.x < 256)
-                h256[threadIdx.x] = 0;
-            __syncthreads();
-            const uint32_t ipf = ip, s2 = (uint32_t)sh;
-            src.each([&](uint32_t key, uint32_t id) {
-                if (key == T && (s2 + 8 >= 32 || (id >> (s2 + 8)) == ipf))
-                    atomicAdd(&h256[255u - ((id >> s2) & 255u)], 1u);
-            });
-            __syncthreads();
-            find_from_top<NT, 256>(h256, need, S);
-            const uint32_t d = 255u - S.res[0];
-            need -= S.res[1];
-            ip = (ip << 8) | d;
-            __syncthreads();
-        }
-        I = ip;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        S.res[0] = T;
-        S.res[1] = I;
-    }
-    __syncthreads();
-}
-
-// Exclusive prefix sum over the work group; returns this thread's offset.
-template <int NT>
-__device__ uint32_t wg_exclusive_scan(uint32_t v, Scratch<NT> &S)
-{
-    constexpr int NW = NT / kWave;
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const uint32_t s = wave_incl_scan(v);
-    __syncthreads();
-    if (lane == kWave - 1)
-        S.tmp[w] = s;
-    __syncthreads();
-    const uint32_t wt = lane < NW ? S.tmp[lane] : 0u;
-    const uint32_t ws = wave_incl_scan(wt);
-    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(ws - wt), w);  // waves below
-    __syncthreads();
-    return base + s - v;
-}
-
-// Writes the ids of the set bits of bitmap[0 .. ceil(nb/32)) in ascending order;
-// never more than cap of them.
-template <int NT>
-__device__ void compact_bitmap(const uint32_t *bitmap, uint32_t nb, int32_t *out, uint32_t cap,
-                               Scratch<NT> &S)
-{
-    const uint32_t W = (nb + 31) / 32;
-    const uint32_t per = (W + NT - 1) / NT;
-    const uint32_t w0 = threadIdx.x * per;
-    const uint32_t w1 = min(W, w0 + per);
-    uint32_t c = 0;
-    for (uint32_t w = w0; w < w1; w++)
-        c += __popc(bitmap[w]);
-    uint32_t pos = wg_exclusive_scan<NT>(c, S);
-    for (uint32_t w = w0; w < w1; w++) {
-        uint32_t m = bitmap[w];
-        while (m) {
-            const uint32_t b = (uint32_t)__ffs((int)m) - 1u;
-            if (pos < cap)
-                out[pos] = (int32_t)(w * 32 + b);
-            pos++;
-            m &= m - 1u;
-        }
-    }
-}
-
-__device__ void set_bit(uint32_t *bitmap, uint32_t id) { atomicOr(&bitmap[id >> 5], 1u << (id & 31)); }
-
-template <int NT>
-__device__ void zero_words(uint32_t *p, uint32_t n)
-{
-    for (uint32_t i = threadIdx.x; i < n; i += NT)
-        p[i] = 0;
-}
 
 // ---------------------------------------------------------------- register form
 // One 1024-thread work group per row; the row's keys stay in registers (KPT per
@@ -604,61 +319,6 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
 }
 
 // ---------------------------------------------------------------- rows form
-// Generic exact selection of one row straight from global memory (any nb up to
-// kMaxBlocks): histogram pass, candidates of the threshold bin to LDS (or
-// re-read from L2 when there are too many), digit passes, bitmap compaction.
-template <int NT>
-__device__ void select_row_global(const float *row, uint32_t nb, int32_t k, int32_t *outr,
-                                  uint32_t *hist, uint64_t *cand, uint32_t *bitmap,
-                                  Scratch<NT> &S)
-{
-    zero_words<NT>(hist, kHistBins);
-    if (threadIdx.x == 0)
-        S.cnt = 0;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nb; i += NT)
-        atomicAdd(&hist[score_key(row[i]) >> (32 - kHistBits)], 1u);
-    __syncthreads();
-    find_from_top<NT, kHistBins>(hist, (uint32_t)k, S);
-    const uint32_t B = S.res[0];
-    const uint32_t need = (uint32_t)k - S.res[1];
-    zero_words<NT>(bitmap, (nb + 31) / 32);
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nb; i += NT) {
-        const uint32_t key = score_key(row[i]);
-        const uint32_t bin = key >> (32 - kHistBits);
-        if (bin > B) {
-            set_bit(bitmap, i);
-        } else if (bin == B) {
-            const uint32_t slot = atomicAdd(&S.cnt, 1u);
-            if (slot < kCandCap)
-                cand[slot] = ((uint64_t)key << 32) | i;
-        }
-    }
-    __syncthreads();
-    const uint32_t c = S.cnt;
-    uint32_t *h256 = hist;  // the 12-bit histogram is no longer needed
-    if (c <= (uint32_t)kCandCap) {
-        LdsCands<NT> src{cand, c};
-        resolve<NT>(src, B, need, nb, h256, S);
-        const uint32_t T = S.res[0], I = S.res[1];
-        src.each([&](uint32_t key, uint32_t id) {
-            if (key > T || (key == T && id <= I))
-                set_bit(bitmap, id);
-        });
-    } else {
-        RowCands<NT> src{row, nb, B};
-        resolve<NT>(src, B, need, nb, h256, S);
-        const uint32_t T = S.res[0], I = S.res[1];
-        src.each([&](uint32_t key, uint32_t id) {
-            if (key > T || (key == T && id <= I))
-                set_bit(bitmap, id);
-        });
-    }
-    __syncthreads();
-    compact_bitmap<NT>(bitmap, nb, outr, (uint32_t)k, S);
-}
-
 // Dynamic LDS: cand[kCandCap] (u64) | hist[4096] | bitmap[ceil(nb_max/32)]
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__restrict__ scores,
                                                              int32_t ld, int32_t pos0, int32_t k,
@@ -686,469 +346,87 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
     if (threadIdx.x == 0)
         n_sel[r] = k;
 }
-
-// ---------------------------------------------------------------- decode form
-// One long row spread over many CUs, two launches that meet only at the kernel
-// boundary.  Neither uses a fence or a global atomic: on this part a device-scope
-// fence or a contended atomic costs more than the kernel boundary itself.
-//   filter  work group g takes scores [1024 g, 1024 g + 1024) and the same
-//           deterministic sample of the row (every stride-th score), finds the
-//           bin of the r-th largest sampled key (r about 3x the sample's expected
-//           share of k) and writes its own keys in that bin or above, in id
-//           order, to region g of ws.cand, and their count to ws.rcnt[g];
-//   final   one work group reads all region counts and the first `head` entries
-//           of every region in one round (regions longer than that in a second
-//           round), so it holds the list in ascending id order.  It selects
-//           exactly: a 12-bit histogram gives the threshold bin, an 8-bit digit
-//           histogram splits it, rank counting settles the threshold digit (or
-//           further digit passes, when it is crowded), and a prefix sum over the
-//           list writes the chosen ids in ascending order.
-//           If the list holds fewer than k keys (the sample misled the bound) or
-//           more than fit in LDS (flat scores), it selects from the whole row.
-constexpr int kFilterPerWg = 1024;  // scores per filter work group (4 per thread)
-constexpr int kSample = 1024;       // sampled scores (4 per thread)
-constexpr int kFinalThreads = 1024;
-constexpr int kListMax = 4096;      // list entries the final step keeps in LDS
-constexpr int kMaxRegions = kMaxBlocks / kFilterPerWg;
-static_assert(kMaxRegions % kWave == 0, "whole regions per lane of wave 0");
-static_assert(kListMax == 4 * kFinalThreads, "four list entries per final thread");
-
-__global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float *__restrict__ scores,
-                                                               int32_t nb, int32_t k, TopkWs ws,
-                                                               uint32_t head)
-{
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
-    __shared__ Scratch<kThreads> S;
-    const int t = threadIdx.x;
-    const uint32_t stride = max(64u, ((uint32_t)nb + kSample - 1) / kSample);
-    const uint32_t ns = ((uint32_t)nb + stride - 1) / stride;
-    // this work group's own 4 scores per thread and 4 sampled scores per thread
-    const int32_t i0 = blockIdx.x * kFilterPerWg + 4 * t;
-    float own[4], smp[4];
-    if (i0 + 3 < nb && ((((uintptr_t)scores) & 15) == 0)) {
-        const f32x4 v = *(const f32x4 *)(scores + i0);
-        own[0] = v[0], own[1] = v[1], own[2] = v[2], own[3] = v[3];
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; e++)
-            own[e] = (i0 + e < nb) ? scores[i0 + e] : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const uint32_t j = (uint32_t)(t + kThreads * e);
-        smp[e] = (j < ns) ? scores[(size_t)j * stride] : 0.f;
-    }
-    zero_words<kThreads>(hist, kHistBins);
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 4; e++)
-        if ((uint32_t)(t + kThreads * e) < ns)
-            atomicAdd(&hist[score_key(smp[e]) >> (32 - kHistBits)], 1u);
-    __syncthreads();
-    // r-th largest sampled key: about 3x the sample's expected count of top-k
-    // keys, so the bound keeps ~3k keys of the row; exactness is checked later
-    const uint32_t want = (uint32_t)(((uint64_t)3 * k * ns + nb - 1) / nb) + 8;
-    find_from_top<kThreads, kHistBins>(hist, min(want, ns), S);
-    const uint32_t Lb = (S.res[0] == 0xffffffffu) ? 0u : S.res[0];
-    uint32_t key[4], mine = 0;
-    bool keep[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        key[e] = score_key(own[e]);
-        keep[e] = i0 + e < nb && (key[e] >> (32 - kHistBits)) >= Lb;
-        mine += keep[e] ? 1u : 0u;
-    }
-    uint32_t off = wg_exclusive_scan<kThreads>(mine, S);
-    uint64_t *region = ws.cand + (size_t)blockIdx.x * kFilterPerWg;
-#pragma unroll
-    for (int e = 0; e < 4; e++)
-        if (keep[e])
-            region[off++] = ((uint64_t)key[e] << 32) | (uint32_t)(i0 + e);
-    if (t == kThreads - 1) {
-        ws.rcnt[blockIdx.x] = off;  // exclusive offset + own count = region total
-        S.res[3] = off;
-    }
-    __syncthreads();
-    // pad the region up to the head the final step reads in its first round, so
-    // that read only touches lines written by this launch
-    for (uint32_t i = S.res[3] + t; i < head; i += kThreads)
-        region[i] = 0ull;
-}
-
-// head: entries read from every region in the first round (a power of two,
-// head * regions <= kListMax, head <= kFilterPerWg).
-__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float *__restrict__ scores,
-                                                                   int32_t nb, int32_t k,
-                                                                   int32_t *__restrict__ blk,
-                                                                   int32_t *__restrict__ n_sel,
-                                                                   TopkWs ws, int32_t head_log2)
-{
-    constexpr int NT = kFinalThreads;
-    __shared__ uint64_t cand[kListMax];
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
-    __shared__ uint32_t bitmap[kMaxBlocks / 32];
-    __shared__ uint32_t rbase[kMaxRegions], rlen[kMaxRegions];
-    __shared__ __attribute__((aligned(16))) uint8_t sel[kListMax];
-    __shared__ __attribute__((aligned(16))) uint32_t h256[256];
-    __shared__ Scratch<NT> S;
-    const int t = threadIdx.x;
-    const int32_t G = (nb + kFilterPerWg - 1) / kFilterPerWg;
-    const uint32_t head = 1u << head_log2;
-
-    // one round of loads: every region count and the head of every region
-    uint64_t e[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const uint32_t sl = (uint32_t)(t + NT * j);
-        const uint32_t g = sl >> head_log2, i = sl & (head - 1u);
-        e[j] = (g < (uint32_t)G) ? ws.cand[(size_t)g * kFilterPerWg + i] : 0ull;
-    }
-    // wave 0: the region counts (8 consecutive regions per lane) and their
-    // exclusive prefix, i.e. where each region starts in the list
-    constexpr int RPL = kMaxRegions / kWave;
-    if (t < kWave) {
-        uint32_t rc[RPL], tot = 0;
-#pragma unroll
-        for (int q = 0; q < RPL; q++) {
-            const int32_t g = RPL * t + q;
-            rc[q] = (g < G) ? ws.rcnt[g] : 0u;
-            tot += rc[q];
-        }
-        const uint32_t incl = wave_incl_scan(tot);
-        uint32_t b = incl - tot;
-        bool over = false;
-#pragma unroll
-        for (int q = 0; q < RPL; q++) {
-            const int32_t g = RPL * t + q;
-            if (g < G) {
-                rbase[g] = b;
-                rlen[g] = rc[q];
-                over |= rc[q] > head;  // longer than its head: a second round
-            }
-            b += rc[q];
-        }
-        const uint64_t anyover = __ballot(over);
-        if (t == 0) {
-            S.cnt = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-            S.flag = anyover ? 1u : 0u;
-        }
-    }
-    ((uint32_t *)sel)[t] = 0u;
-    __syncthreads();
-    const uint32_t c = S.cnt;
-    if (c < (uint32_t)k || c > (uint32_t)kListMax) {
-        // the list cannot be used: select from the whole row
-        select_row_global<NT>(scores, (uint32_t)nb, k, blk, hist, cand, bitmap, S);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t sl = (uint32_t)(t + NT * j);
-            const uint32_t g = sl >> head_log2, i = sl & (head - 1u);
-            if (g < (uint32_t)G && i < rlen[g])
-                cand[rbase[g] + i] = e[j];
-        }
-        if (S.flag) {
-            // rare: the tails of long regions, one region at a time
-            for (int32_t g = 0; g < G; g++) {
-                const uint32_t n = rlen[g];
-                for (uint32_t i = head + t; i < n; i += NT)
-                    cand[rbase[g] + i] = ws.cand[(size_t)g * kFilterPerWg + i];
-            }
-        }
-        zero_words<NT>(hist, kHistBins);
-        if (t < 256)
-            h256[t] = 0;
-        if (t == 0)
-            S.cnt2 = 0;
-        __syncthreads();
-        for (uint32_t i = t; i < c; i += NT)
-            atomicAdd(&hist[(uint32_t)(cand[i] >> (64 - kHistBits))], 1u);
-        __syncthreads();
-        find_from_top<NT, kHistBins>(hist, (uint32_t)k, S);
-        const uint32_t B = S.res[0];
-        const uint32_t need = (uint32_t)k - S.res[1];
-        for (uint32_t i = t; i < c; i += NT) {
-            const uint64_t v = cand[i];
-            const uint32_t bin = (uint32_t)(v >> (64 - kHistBits));
-            if (bin > B)
-                sel[i] = 1;
-            else if (bin == B)
-                atomicAdd(&h256[(uint32_t)(v >> 44) & 255u], 1u);
-        }
-        __syncthreads();
-        find_from_top<NT, 256>(h256, need, S);
-        const uint32_t d = S.res[0];
-        const uint32_t need2 = need - S.res[1];
-        const uint32_t cd = h256[d];
-        uint32_t *dl = hist;  // list indices of digit d
-        for (uint32_t i = t; i < c; i += NT) {
-            const uint64_t v = cand[i];
-            if ((uint32_t)(v >> (64 - kHistBits)) != B)
-                continue;
-            const uint32_t dig = (uint32_t)(v >> 44) & 255u;
-            if (dig > d)
-                sel[i] = 1;
-            else if (dig == d && cd <= (uint32_t)kWave)
-                dl[atomicAdd(&S.cnt2, 1u)] = i;
-        }
-        __syncthreads();
-        if (cd <= (uint32_t)kWave) {
-            if ((uint32_t)t < cd) {
-                const uint32_t me = dl[t];
-                const uint64_t v = cand[me];
-                const uint32_t mk = (uint32_t)(v >> 32), mid = (uint32_t)v;
-                uint32_t before = 0;
-                for (uint32_t j = 0; j < cd; j++) {
-                    const uint64_t o = cand[dl[j]];
-                    const uint32_t ok = (uint32_t)(o >> 32), oid = (uint32_t)o;
-                    before += (ok > mk || (ok == mk && oid < mid)) ? 1u : 0u;
-                }
-                if (before < need2)
-                    sel[me] = 1;
-            }
-        } else {
-            LdsCands<NT> all{cand, c};
-            resolve<NT>(all, B, need, (uint32_t)nb, h256, S);
-            const uint32_t T = S.res[0], I = S.res[1];
-            for (uint32_t i = t; i < c; i += NT) {
-                const uint64_t v = cand[i];
-                const uint32_t kk = (uint32_t)(v >> 32), id = (uint32_t)v;
-                if ((kk >> (32 - kHistBits)) == B && (kk > T || (kk == T && id <= I)))
-                    sel[i] = 1;
-            }
-        }
-        __syncthreads();
-        // chosen ids in list order = ascending ids; thread t owns entries 4t..4t+3
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            cnt += (4u * t + j < c) ? sel[4 * t + j] : 0u;
-        uint32_t pos = wg_exclusive_scan<NT>(cnt, S);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t i = 4u * t + j;
-            if (i < c && sel[i]) {
-                if (pos < (uint32_t)k)
-                    blk[pos] = (int32_t)(uint32_t)cand[i];
-                pos++;
-            }
-        }
-    }
-    if (t == 0)
-        n_sel[0] = k;
-}
-
 // ---------------------------------------------------------------- list form
-// The decode step's scan leaves, per work group w, its kListLen best rank keys
-// (in any order, 0 for an empty slot) and its row count.  One 1024-thread work group, thread w holding
-// list w in registers:
-//   1. selection of R*, the k-th largest rank key of the lists: 4096-bucket
-//      histograms over the range of the live score keys (the whole range of the
-//      lists' keys first, then the chosen bucket; equal-width buckets over the
-//      actual range keep the LDS atomics spread out, where fixed float-bit
-//      digits would pile the candidates into a few bins), then digits of the
-//      block id when one key is shared by many entries, until at most 64
-//      entries are live; those are ranked by counting.  Rank keys are distinct
-//      (ids are), so R* is exact and the chosen set is {R >= R*};
-//   2. if a list is full (its work group scored more than kListLen rows) and
-//      its smallest key is >= R* (checked on the per-wave maxima of those
-//      smallest keys, by the wave that finds R*), rows of that work group missing from the list
-//      could outrank R*: the whole score row is selected from instead
-//      (select_row_global).  Otherwise every row outside the lists ranks below
-//      the smallest key of its own list, hence below R*, and the lists hold the
-//      top-k exactly;
-//   3. chosen ids go into an LDS bitmap, compacted in ascending id order.
-constexpr int kSmallRank = 64;  // keys ranked by counting (one per lane of wave 0)
-
-__global__ __launch_bounds__(kFinalThreads) void topk_lists_kernel(const float *__restrict__ scores,
-                                                                   int32_t nb, int32_t k,
-                                                                   CandLists cl, int32_t W,
-                                                                   int32_t *__restrict__ blk,
-                                                                   int32_t *__restrict__ n_sel)
+// One 1024-thread work group: thread w holds list w, lists_select finds R*, the
+// chosen ids go into an LDS bitmap, compacted in ascending id order.
+__global__ __launch_bounds__(kSelThreads) void topk_lists_kernel(const float *__restrict__ scores,
+                                                                 int32_t nb, int32_t k,
+                                                                 CandLists cl, int32_t W,
+                                                                 int32_t *__restrict__ blk,
+                                                                 int32_t *__restrict__ n_sel)
 {
-    constexpr int NT = kFinalThreads;
-    static_assert(kListWgs <= NT, "one list per thread");
+    constexpr int NT = kSelThreads;
     __shared__ uint32_t bitmap[kMaxBlocks / 32];
-    __shared__ __attribute__((aligned(16))) uint32_t hist[2][kHistBins];
     __shared__ uint64_t cand[kCandCap];
-    __shared__ Scratch<NT> S;
-    __shared__ uint32_t wtot[NT / kWave];
-    __shared__ uint64_t wlast[NT / kWave];
-    __shared__ uint32_t wkey[2][NT / kWave];
-    __shared__ uint64_t rstar;
-    __shared__ uint32_t hidden;
+    __shared__ ListSelLds L;
     const int t = threadIdx.x;
 
-    // one round of loads: this thread's list and row count
     uint64_t R[kListLen];
-    uint32_t nrows = 0;
-    if (t < W) {
-        const uint4 *src = (const uint4 *)(cl.list + (int64_t)t * kListLen);
-#pragma unroll
-        for (int j = 0; j < kListLen / 2; j++) {
-            const uint4 v = src[j];
-            R[2 * j] = ((uint64_t)v.y << 32) | v.x;
-            R[2 * j + 1] = ((uint64_t)v.w << 32) | v.z;
-        }
-        nrows = cl.rows[t];
-    } else {
-#pragma unroll
-        for (int j = 0; j < kListLen; j++)
-            R[j] = 0ull;
-    }
-    // while they are in flight: clear both histograms and the bitmap
-    ((uint4 *)hist[0])[t] = uint4{0, 0, 0, 0};
-    ((uint4 *)hist[1])[t] = uint4{0, 0, 0, 0};
+    uint32_t nrows;
+    load_list(cl, W, R, &nrows);
     zero_words<NT>(bitmap, ((uint32_t)nb + 31) / 32);
-    if (t == 0)
-        S.cnt = 0;
-    // per wave: the smallest and largest score key of the nonempty entries, and
-    // the largest smallest entry of a full list (for step 2)
-    {
-        uint32_t kmin = 0xffffffffu, kmax = 0u;
-        uint64_t last = ~0ull;
-#pragma unroll
-        for (int j = 0; j < kListLen; j++) {
-            const uint32_t key = (uint32_t)(R[j] >> 32);
-            if (R[j] != 0ull) {
-                kmin = min(kmin, key);
-                kmax = max(kmax, key);
-            }
-            last = R[j] < last ? R[j] : last;
-        }
-        if (!(t < W && nrows > (uint32_t)kListLen))
-            last = 0ull;
-        last = wave_max_u64(last);
-        kmin = wave_min_u32(kmin);
-        kmax = wave_max_u32(kmax);
-        if ((t & (kWave - 1)) == 0) {
-            wlast[t / kWave] = last;
-            wkey[0][t / kWave] = kmin;
-            wkey[1][t / kWave] = kmax;
-        }
-    }
-    __syncthreads();
-
-    // 1. select R*.  Key passes: the live keys [lo, lo + span] go into 4096
-    // equal buckets ((key - lo) >> s); the bucket holding the need-th key from
-    // the top becomes the new range, until one key is left or few entries.  If
-    // that key is shared by many entries, id passes follow: the id bits 18..0
-    // (bits 31..19 of ~id are 1 for every id below kMaxBlocks = 2^19) in 8, 8
-    // and 3 bits, with (imask, ival) the low-word bits fixed so far.
-    static_assert(kMaxBlocks == 1 << 19, "id digits cover 19 bits");
-    uint32_t lo = 0xffffffffu, hi_key = 0u;
-#pragma unroll
-    for (int i = 0; i < NT / kWave; i++) {
-        lo = min(lo, wkey[0][i]);
-        hi_key = max(hi_key, wkey[1][i]);
-    }
-    uint32_t span = hi_key - lo;
-    uint32_t imask = 0u, ival = 0u;
-    auto live = [&](uint64_t r) {
-        const uint32_t key = (uint32_t)(r >> 32);
-        return r != 0ull && key >= lo && key - lo <= span && ((uint32_t)r & imask) == ival;
-    };
-    uint32_t need = (uint32_t)k, cnt = 0;
-    bool ok = hi_key >= lo;  // some entry at all
-    int p = 0;
-    while (ok) {
-        const int s = span >= (uint32_t)kHistBins ? 32 - __clz((int)span) - kHistBits : 0;
-        uint32_t *h = hist[p & 1];
+    uint64_t rs = 0;
+    if (lists_select(R, nrows, t < W, (uint32_t)k, L, &rs)) {
 #pragma unroll
         for (int j = 0; j < kListLen; j++)
-            if (live(R[j]))
-                atomicAdd(&h[((uint32_t)(R[j] >> 32) - lo) >> s], 1u);
-        __syncthreads();
-        find_from_top_wg<NT>(h, need, S, wtot);
-        const uint32_t d = S.res[0];
-        if (d == 0xffffffffu) {  // fewer than k keys in the lists
-            ok = false;
-            break;
-        }
-        need -= S.res[1];
-        cnt = S.res[3];
-        // nobody reads h again in this pass; the next pass uses the other one
-        ((uint4 *)h)[t] = uint4{0, 0, 0, 0};
-        p++;
-        lo += d << s;
-        span = s == 0 ? 0u : min(span - (d << s), (1u << s) - 1u);
-        if (span == 0 || cnt <= (uint32_t)kSmallRank)
-            break;
-    }
-    if (ok && cnt > (uint32_t)kSmallRank) {
-        // one key, many entries: id digits
-        imask = 0xfff80000u;
-        ival = 0xfff80000u;
-        const int shifts[3] = {11, 3, 0};
-        const int widths[3] = {8, 8, 3};
-        for (int q = 0; q < 3; q++) {
-            const int w = widths[q], sh = shifts[q];
-            uint32_t *h = hist[p & 1];
-#pragma unroll
-            for (int j = 0; j < kListLen; j++)
-                if (live(R[j]))
-                    atomicAdd(&h[((uint32_t)R[j] >> sh) & ((1u << w) - 1u)], 1u);
-            __syncthreads();
-            find_from_top<NT, 256>(h, need, S);
-            const uint32_t d = S.res[0];
-            need -= S.res[1];
-            cnt = S.res[3];
-            if (t < 64)
-                ((uint4 *)h)[t] = uint4{0, 0, 0, 0};
-            p++;
-            imask |= ((1u << w) - 1u) << sh;
-            ival |= d << sh;
-            if (cnt <= (uint32_t)kSmallRank)
-                break;
-        }
-    }
-    if (ok) {
-        // the <= 64 live entries; R* is the one with `need - 1` of them above it
-#pragma unroll
-        for (int j = 0; j < kListLen; j++) {
-            if (live(R[j])) {
-                const uint32_t slot = atomicAdd(&S.cnt, 1u);
-                if (slot < (uint32_t)kSmallRank)
-                    cand[slot] = R[j];
+            if (R[j] >= rs) {
+                const uint32_t id = rank_id(R[j]);
+                if (id < (uint32_t)nb)
+                    set_bit(bitmap, id);
             }
-        }
         __syncthreads();
-        if (t < kWave) {
-            const uint64_t me = (uint32_t)t < cnt ? cand[t] : 0ull;
-            uint32_t above = 0;
-            for (uint32_t j = 0; j < cnt; j++)
-                above += cand[j] > me ? 1u : 0u;
-            const bool is_rs = (uint32_t)t < cnt && above == need - 1u;
-            if (is_rs)
-                rstar = me;
-            // 2. a full list whose last key is chosen may hide chosen rows
-            const uint64_t last = t < NT / kWave ? wlast[t] : 0ull;
-            const uint64_t rs = __shfl(me, __ffsll((unsigned long long)__ballot(is_rs)) - 1, kWave);
-            const bool hid = __ballot(last >= rs) != 0ull;
-            if (t == 0)
-                hidden = hid ? 1u : 0u;
-        }
+        compact_bitmap<NT>(bitmap, (uint32_t)nb, blk, (uint32_t)k, L.S);
+    } else {
         __syncthreads();
-        const uint64_t rs = rstar;
-        ok = hidden == 0u;
-        if (ok) {
-#pragma unroll
-            for (int j = 0; j < kListLen; j++)
-                if (R[j] >= rs) {
-                    const uint32_t id = rank_id(R[j]);
-                    if (id < (uint32_t)nb)
-                        set_bit(bitmap, id);
-                }
-            __syncthreads();
-            compact_bitmap<NT>(bitmap, (uint32_t)nb, blk, (uint32_t)k, S);
-        }
-    }
-    if (!ok) {
-        __syncthreads();
-        select_row_global<NT>(scores, (uint32_t)nb, k, blk, hist[0], cand, bitmap, S);
+        select_row_global<NT>(scores, (uint32_t)nb, k, blk, L.hist[0], cand, bitmap, L.S);
     }
     if (t == 0)
         n_sel[0] = k;
+}
+
+// Candidate lists from a score row, laid out as the decode scan lays them out:
+// work group w owns the runs of 4 rows 4(w + nwg m) .. 4(w + nwg m) + 3; its
+// rank keys go to LDS, and wave 0 takes the kListLen largest one at a time.
+constexpr int kListBuildThreads = 512;
+constexpr int kListBuildMaxRows = 4 * ((kMaxBlocks / 4 + kListWgs - 1) / kListWgs) + 4;
+
+__global__ __launch_bounds__(kListBuildThreads) void score_lists_kernel(
+    const float *__restrict__ scores, int32_t nb, CandLists cl)
+{
+    __shared__ uint64_t rk[kListBuildMaxRows];
+    __shared__ uint32_t n_own;
+    const int t = threadIdx.x;
+    const int64_t nwg = gridDim.x, w = blockIdx.x;
+    const int64_t runs = ((int64_t)nb + 3) / 4;
+    const int64_t my_runs = runs > w ? (runs - w + nwg - 1) / nwg : 0;
+    const int64_t n = min(my_runs * 4, (int64_t)kListBuildMaxRows);
+    for (int64_t i = t; i < n; i += kListBuildThreads) {
+        const int64_t r = 4 * (w + nwg * (i / 4)) + (i & 3);
+        rk[i] = r < nb ? rank_key(scores[r], (uint32_t)r) : 0ull;
+    }
+    if (t == 0) {
+        const int64_t last = 4 * (w + nwg * (my_runs - 1));  // first row of the last run
+        n_own = my_runs == 0 ? 0u : (uint32_t)(4 * (my_runs - 1) + min((int64_t)4, nb - last));
+    }
+    __syncthreads();
+    if (t < kWave) {
+        for (int j = 0; j < kListLen; j++) {
+            uint64_t best = 0ull;
+            int at = -1;
+            for (int64_t i = t; i < n; i += kWave)
+                if (rk[i] > best) {
+                    best = rk[i];
+                    at = (int)i;
+                }
+            const uint64_t m = wave_max_u64(best);
+            if (m != 0ull && best == m)
+                rk[at] = 0ull;  // the one lane holding it (rank keys are distinct)
+            if (t == 0)
+                cl.list[w * kListLen + j] = m;
+        }
+        if (t == 0)
+            cl.rows[w] = n_own;
+    }
 }
 
 __global__ void iota_kernel(int32_t *blk, int32_t n, int32_t *n_sel)
@@ -1187,7 +465,7 @@ hipError_t launch_reg(const float *scores, int32_t n_q, int32_t ld_or_nb, int32_
 int32_t topk_max_blocks() { return kMaxBlocks; }
 
 hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_t *blk,
-                              int32_t *n_sel, TopkWs ws, hipStream_t s)
+                              int32_t *n_sel, CandLists cl, hipStream_t s)
 {
     if (nb > kMaxBlocks)
         return hipErrorInvalidValue;
@@ -1196,18 +474,13 @@ hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_
         hipLaunchKernelGGL(iota_kernel, dim3(grid), dim3(kThreads), 0, s, blk, nb, n_sel);
         return hipGetLastError();
     }
-    const int32_t G = (nb + kFilterPerWg - 1) / kFilterPerWg;
-    int32_t head_log2 = 0;  // largest power of two with head * G <= kListMax
-    while (head_log2 < 10 && ((int64_t)2 << head_log2) * G <= kListMax)
-        head_log2++;
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(G), dim3(kThreads), 0, s, scores, nb, k, ws,
-                       1u << head_log2);
+    const int32_t runs = (nb + 3) / 4;
+    const int32_t nwg = runs < kListWgs ? runs : kListWgs;
+    hipLaunchKernelGGL(score_lists_kernel, dim3(nwg), dim3(kListBuildThreads), 0, s, scores, nb, cl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kFinalThreads), 0, s, scores, nb, k, blk,
-                       n_sel, ws, head_log2);
-    return hipGetLastError();
+    return launch_topk_lists(scores, nb, k, cl, nwg, blk, n_sel, s);
 }
 
 hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,
@@ -1220,7 +493,7 @@ hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLis
         hipLaunchKernelGGL(iota_kernel, dim3(grid), dim3(kThreads), 0, s, blk, nb, n_sel);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(topk_lists_kernel, dim3(1), dim3(kFinalThreads), 0, s, scores, nb, k, cl,
+    hipLaunchKernelGGL(topk_lists_kernel, dim3(1), dim3(kSelThreads), 0, s, scores, nb, k, cl,
                        n_lists, blk, n_sel);
     return hipGetLastError();
 }

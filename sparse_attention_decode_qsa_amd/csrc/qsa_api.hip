@@ -89,13 +89,10 @@ int check_cfg(const qsa_config *c)
     return QSA_OK;
 }
 
-// Workspace: a fixed prefix of words that every call leaves at zero (control
-// words, the decode histogram, attention tickets), then data regions whose size
-// depends on n_q and n_ctx.  The prefix offsets depend on cfg only, so calls with
-// different sizes may share one workspace.
+// Workspace layout: data regions whose sizes depend on (cfg, n_q, n_ctx).  No
+// call relies on what a previous call left there.
 struct Layout {
-    size_t ctrl, hist, tickets, zero_end;
-    size_t sure, cand, rcnt, lists, lrows, scores, blk, nsel, part, ksel, vsel, total;
+    size_t lists, lrows, scores, blk, nsel, part, ksel, vsel, total;
     int64_t ld;  // score row stride
 };
 
@@ -111,15 +108,8 @@ Layout layout(const qsa_config *c, int32_t n_q, int32_t n_ctx)
         off = round_up(off + bytes, 256);
         return o;
     };
-    L.ctrl = take(sizeof(uint32_t) * kCtrlWords);
-    L.hist = take(sizeof(uint32_t) * kHistBins);
-    L.tickets = take(sizeof(uint32_t) * (size_t)c->hkv);
-    L.zero_end = off;
     const int64_t nb = (int64_t)n_ctx / kBlockTokens + 1;
     L.ld = (int64_t)round_up((size_t)nb, 64);
-    L.sure = take(sizeof(int32_t) * (size_t)c->topk_blocks);
-    L.cand = take(sizeof(uint64_t) * round_up((size_t)nb, 1024));
-    L.rcnt = take(sizeof(uint32_t) * (round_up((size_t)nb, 1024) / 1024));
     L.lists = take(sizeof(uint64_t) * (size_t)kListWgs * kListLen);
     L.lrows = take(sizeof(uint32_t) * (size_t)kListWgs);
     L.scores = take(sizeof(float) * (size_t)n_q * (size_t)L.ld);
@@ -138,15 +128,9 @@ T *at(void *ws, size_t off)
     return (T *)((char *)ws + off);
 }
 
-TopkWs topk_ws(void *ws, const Layout &L)
+CandLists cand_lists(void *ws, const Layout &L)
 {
-    TopkWs t;
-    t.ctrl = at<uint32_t>(ws, L.ctrl);
-    t.hist = at<uint32_t>(ws, L.hist);
-    t.sure = at<int32_t>(ws, L.sure);
-    t.cand = at<uint64_t>(ws, L.cand);
-    t.rcnt = at<uint32_t>(ws, L.rcnt);
-    return t;
+    return CandLists{at<uint64_t>(ws, L.lists), at<uint32_t>(ws, L.lrows)};
 }
 
 int check_ws(const qsa_config *c, void *ws, size_t ws_bytes, int32_t n_q, int32_t n_ctx,
@@ -201,7 +185,6 @@ int attn_decode_launch(const qsa_config *c, AttnArgs a, int32_t cells, void *ws,
 {
     split_plan(cells, &a.splits, &a.chunks);
     a.part = at<float>(ws, L.part);
-    a.tickets = at<uint32_t>(ws, L.tickets);
     HIP_CHECK(launch_attn(a, c->d, c->dv, s));
     return QSA_OK;
 }
@@ -364,7 +347,7 @@ int qsa_topk_blocks(const qsa_config *cfg, const float *scores, int32_t n_q, int
             return r;
         const Layout L = layout(cfg, 1, pos0 + 1);
         HIP_CHECK(launch_topk_decode(scores, (pos0 + 1) / kBlockTokens, cfg->topk_blocks, blk,
-                                     n_sel, topk_ws(ws, L), s));
+                                     n_sel, cand_lists(ws, L), s));
         return QSA_OK;
     }
     HIP_CHECK(launch_topk_rows(scores, n_q, ld, pos0, cfg->topk_blocks, blk, n_sel, s));
@@ -524,20 +507,45 @@ int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_b
     // and scores the block it completes; every scan work group leaves its
     // best kListLen candidates
     float *scores = scores_out ? scores_out : at<float>(ws, L.scores);
-    const CandLists cl{at<uint64_t>(ws, L.lists), at<uint32_t>(ws, L.lrows)};
+    const CandLists cl = cand_lists(ws, L);
     int32_t n_lists = 0;
     HIP_CHECK(launch_score_decode(H(q_idx), H(Lb->k_pool), ap.b_lo, (int32_t)row, scores, &ap, &cl,
                                   &n_lists, s));
+
+    if (flags == QSA_STEP_FUSED_GATHER) {
+        // 3-5. top-k from the candidate lists and attention over the chosen
+        // cells (read straight from the caches) in one launch, then the combine
+        StepTail st;
+        st.cl = cl;
+        st.n_lists = n_lists;
+        st.scores = scores;
+        st.n_tokens = N;
+        st.k = k;
+        st.q = H(q);
+        st.k_cache = H(Lb->k_cache);
+        st.v_cache = H(Lb->v_cache);
+        st.hq = cfg->hq;
+        st.hkv = cfg->hkv;
+        st.d = cfg->d;
+        st.dv = cfg->dv;
+        st.scale = cfg->attn_scale;
+        st.part = at<float>(ws, L.part);
+        st.out = out;
+        st.blk_out = blk_out;
+        st.n_sel = nullptr;
+        HIP_CHECK(launch_step_tail(st, s));
+        return QSA_OK;
+    }
 
     // 3. top-k blocks (ascending ids) from the candidate lists
     int32_t *blk = blk_out ? blk_out : at<int32_t>(ws, L.blk);
     HIP_CHECK(launch_topk_lists(scores, nb, k, cl, n_lists, blk, at<int32_t>(ws, L.nsel), s));
 
-    // 4-5. attention over the chosen cells plus the tail
+    // 4-5. compact gather, then attention over the compact rows
     AttnArgs a = attn_base(cfg);
     a.q = H(q);
     a.out = out;
-    if (flags == QSA_STEP_COMPACT_GATHER) {
+    {
         h16 *ks = at<h16>(ws, L.ksel), *vs = at<h16>(ws, L.vsel);
         HIP_CHECK(launch_gather(blk, nsel, N, H(Lb->k_cache), H(Lb->v_cache), (int32_t)(kr / 8),
                                 (int32_t)(vr / 8), ks, vs, s));
@@ -545,13 +553,6 @@ int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_b
         a.vbase = vs;
         a.mode = kCellsCompact;
         a.n_cells = cells;
-    } else {
-        a.kbase = H(Lb->k_cache);
-        a.vbase = H(Lb->v_cache);
-        a.mode = kCellsBlocks;
-        a.blk = blk;
-        a.ldb = k;
-        a.pos0 = n_before;
     }
     return attn_decode_launch(cfg, a, cells, ws, L, s);
 }
@@ -642,8 +643,7 @@ size_t qsa_mla_workspace_size(int32_t hq, int32_t dv, int32_t list_cap)
     if (hq < 1 || dv < 1 || list_cap < 1)
         return 0;
     const size_t splits = ((size_t)list_cap + kAttnChunk - 1) / kAttnChunk;
-    size_t off = 256;                                        // ticket
-    off += round_up(sizeof(uint32_t) * 2048, 256);           // segment counts
+    size_t off = round_up(sizeof(uint32_t) * 2048, 256);    // segment counts
     off += round_up(sizeof(int32_t) * (size_t)list_cap, 256);  // list
     off += round_up(sizeof(float) * (size_t)hq * splits * (size_t)(dv + 2), 256);
     return off;
@@ -682,9 +682,8 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
                     ws_bytes, need);
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
-    uint32_t *ticket = (uint32_t *)w;
-    uint32_t *seg_cnt = (uint32_t *)(w + 256);
-    int32_t *list = (int32_t *)(w + 256 + round_up(sizeof(uint32_t) * 2048, 256));
+    uint32_t *seg_cnt = (uint32_t *)w;
+    int32_t *list = (int32_t *)(w + round_up(sizeof(uint32_t) * 2048, 256));
     float *part = (float *)((char *)list + round_up(sizeof(int32_t) * (size_t)list_cap, 256));
     if (list_out)
         list = list_out;
@@ -706,7 +705,6 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
     a.scale = scale;
     split_plan(list_cap, &a.splits, &a.chunks);
     a.part = part;
-    a.tickets = ticket;
     a.out = out;
     a.rows = 1;
     a.tok_bound = n;

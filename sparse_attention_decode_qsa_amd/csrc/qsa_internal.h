@@ -60,18 +60,10 @@ hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h
                                 int32_t row_elems, float *scores, int32_t ld, hipStream_t s);
 
 // ---- top-k (k_topk.hip) -----------------------------------------------------
-constexpr int kCtrlWords = 64;
-
-struct TopkWs {
-    uint32_t *ctrl;  // kCtrlWords control words (tickets, counters, threshold)
-    uint32_t *hist;  // kHistBins
-    int32_t *sure;   // up to k entries
-    uint64_t *cand;  // nb rounded up to 1024 entries (key << 32 | id), by regions of 1024
-    uint32_t *rcnt;  // entries per region
-};
-// Uses ws.cand and ws.rcnt only; keeps no state between calls.
+// One decode row: candidate lists built from the scores (in cl), then the list
+// selection.  Keeps no state between calls.
 hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_t *blk,
-                              int32_t *n_sel, TopkWs ws, hipStream_t s);
+                              int32_t *n_sel, CandLists cl, hipStream_t s);
 // Top-k of one row from the scan's candidate lists (n_lists of them); selects
 // from the whole score row when the lists cannot be shown to hold the top-k.
 hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,
@@ -111,12 +103,36 @@ struct AttnArgs {
     int32_t splits;         // work groups per (row, kv head)
     int32_t chunks;         // chunks of kAttnChunk cells per work group
     float *part;            // [rows][hq][splits][dv + 2] when splits > 1
-    uint32_t *tickets;      // [rows][hkv] when splits > 1
     float *out;             // [rows][hq][dv]
     int32_t rows;
     int32_t tok_bound;      // list: tokens must be < tok_bound (the mask length)
 };
 hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s);
+// Merge of split-K partials [hq][splits][dv + 2] into out [hq][dv].
+hipError_t launch_combine(const float *part, int32_t hq, int32_t splits, int32_t dv, float *out,
+                          hipStream_t s);
+
+// ---- decode-step tail (k_step.hip) -----------------------------------------
+// Top-k from the scan's candidate lists and attention over the chosen cells in
+// one launch, then the combine.
+constexpr int kMaxTopk = 1024;
+struct StepTail {
+    CandLists cl;
+    int32_t n_lists;
+    const float *scores;  // the score row (used when the lists are not enough)
+    int32_t n_tokens;     // context after the append
+    int32_t k;
+    const h16 *q;
+    const h16 *k_cache;
+    const h16 *v_cache;
+    int32_t hq, hkv, d, dv;
+    float scale;
+    float *part;          // [hq][splits][dv + 2]
+    float *out;           // [hq][dv]
+    int32_t *blk_out;     // optional: chosen ids, ascending
+    int32_t *n_sel;       // optional
+};
+hipError_t launch_step_tail(const StepTail &st, hipStream_t s);
 
 // ---- MLA list (k_mla.hip) ---------------------------------------------------
 constexpr int kListSeg = 4096;  // positions per list-building work group

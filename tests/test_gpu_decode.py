@@ -139,8 +139,6 @@ def test_topk_decode_bit_exact(gpu, kind, nb):
     got, n, ws = run_topk_decode(s, 512)
     assert n == 512
     assert np.array_equal(got, O.topk_sort(s, 512))
-    # the workspace is left cleared
-    assert not host(ws[:256 + 16384]).any()
 
 
 @pytest.mark.parametrize("nb,k", [(1, 512), (512, 512), (511, 512), (0, 4), (100, 99), (100, 1)])

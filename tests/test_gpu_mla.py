@@ -37,7 +37,6 @@ def test_mla_full_workload(gpu, runs):
     assert np.array_equal(lst[:nl], O.mask_list(I["mask"]))
     ref = O.mla_attn(I["q"], I["kv"], None, I["mask"], ref_list, 512, scale)
     assert_attn_close(out, ref)
-    assert not host(ws[:256]).any()  # the combine ticket is reset
 
 
 @pytest.mark.parametrize("hq", [1, 2, 4, 8, 16])
