@@ -30,9 +30,9 @@
  *    complete blocks; the tail is N mod 4 tokens; a decode step attends over
  *    4*min(k, nb) + (N mod 4) cells, a number the host can compute.
  *  - No entry point allocates device memory.  Scratch memory comes from a
- *    caller workspace of qsa_workspace_size() bytes that qsa_workspace_init()
- *    has cleared once; every call leaves the workspace cleared again.  Calls that
- *    share one workspace must not overlap in time (same stream, or synchronised).
+ *    caller workspace of qsa_workspace_size() bytes; no call depends on what an
+ *    earlier call left in it.  Calls that share one workspace must not overlap
+ *    in time (same stream, or synchronised).
  *  - Every call enqueues its kernels on `stream` and returns without waiting.
  *    Arguments are checked on the host first; on a bad argument nothing is
  *    enqueued and a negative status is returned.  After QSA_ERR_HIP the
@@ -106,7 +106,8 @@ int qsa_config_check(const qsa_config *cfg);
  */
 size_t qsa_workspace_size(const qsa_config *cfg, int32_t n_q, int32_t n_ctx);
 
-/* Clears a workspace (a fill kernel on `stream`).  Needed once after allocation. */
+/* Clears a workspace (a fill kernel on `stream`).  Optional: no call reads a
+ * workspace byte it has not written in the same call. */
 int qsa_workspace_init(void *ws, size_t ws_bytes, qsa_stream_t stream);
 
 /*
@@ -189,8 +190,12 @@ int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int3
  * n_before (the context grows to N = n_before + 1).  Appends k_idx_new [h_idx][d_idx]
  * to the indexer caches and k_new/v_new [hkv][d|dv] to the K/V caches, then
  * scores, selects and attends; out [hq][dv] fp32.  Optional outputs (NULL to
- * skip): scores_out [floor(N/4)] fp32 block scores, blk_out [k] chosen blocks.
- * flags: QSA_STEP_FUSED_GATHER or QSA_STEP_COMPACT_GATHER.
+ * skip): scores_out [floor(N/4)] fp32 block scores, blk_out [min(k, floor(N/4))]
+ * chosen blocks in ascending order.
+ * flags: QSA_STEP_FUSED_GATHER (the selection runs inside the attention launch,
+ * which reads the chosen cells straight from the caches) or
+ * QSA_STEP_COMPACT_GATHER (separate top-k and gather launches, then attention
+ * over the compact rows).
  */
 int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
                     const uint16_t *q_idx, const uint16_t *k_idx_new, const uint16_t *q,
