@@ -125,6 +125,23 @@ int qsa_pool_append(const qsa_config *cfg, const uint16_t *k_new, int32_t n_new,
                     int32_t n_before, uint16_t *k_raw, uint16_t *k_pool, const float *rms_w,
                     qsa_stream_t stream);
 
+/*
+ * Pooled-cache rebuild from the raw indexer cache (Qiita part 10, "incremental
+ * pooled-key cache（COMMON-004）": on a state load or a sequence edit the pooled
+ * rows are invalidated and rebuilt when needed).  Recomputes the pooled rows of
+ * blocks [b_from, floor(n_tokens/4)) from k_raw rows [4*b_from, n_tokens), as
+ * qsa_pool_append computes them (same device code, same bits); other rows are
+ * untouched.  Typical uses: after loading k_raw from a saved state (b_from = 0),
+ * or after editing tokens from position p on (b_from = p / 4).
+ * Rolling back rejected draft tokens needs no call: a pooled row is read only
+ * once its block is complete in the caller's token count, and the append that
+ * completes the block again recomputes it.
+ * Errors: INVALID (null k_raw/k_pool, n_tokens outside [0, cap_tokens], b_from
+ * outside [0, floor(n_tokens/4)]).
+ */
+int qsa_pool_rebuild(const qsa_config *cfg, const uint16_t *k_raw, uint16_t *k_pool,
+                     const float *rms_w, int32_t b_from, int32_t n_tokens, qsa_stream_t stream);
+
 /* Copies k_new/v_new [n_new][hkv][d|dv] to cache rows [n_before, n_before+n_new). */
 int qsa_kv_append(const qsa_config *cfg, const uint16_t *k_new, const uint16_t *v_new,
                   int32_t n_new, int32_t n_before, uint16_t *k_cache, uint16_t *v_cache,

@@ -28,7 +28,8 @@ QSA_STEP_COMPACT_GATHER = 1
 
 EXPORTS = [
     "qsa_status_string", "qsa_last_error", "qsa_config_check", "qsa_workspace_size",
-    "qsa_workspace_init", "qsa_pool_append", "qsa_kv_append", "qsa_index_score",
+    "qsa_workspace_init", "qsa_pool_append", "qsa_pool_rebuild", "qsa_kv_append",
+    "qsa_index_score",
     "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_attn", "qsa_prefill_attn",
     "qsa_decode_step", "qsa_prefill_step", "qsa_mla_workspace_size", "qsa_mla_sparse_attn",
 ]
@@ -72,6 +73,7 @@ def load():
         "qsa_workspace_size": (sz, [cfg, i32, i32]),
         "qsa_workspace_init": (C.c_int, [p, sz, p]),
         "qsa_pool_append": (C.c_int, [cfg, p, i32, i32, p, p, p, p]),
+        "qsa_pool_rebuild": (C.c_int, [cfg, p, p, p, i32, i32, p]),
         "qsa_kv_append": (C.c_int, [cfg, p, p, i32, i32, p, p, p]),
         "qsa_index_score": (C.c_int, [cfg, p, i32, i32, p, p, i32, p]),
         "qsa_topk_blocks": (C.c_int, [cfg, p, i32, i32, i32, p, p, p, sz, p]),
@@ -196,6 +198,14 @@ def qsa_pool_append(cfg: Config, k_new, n_before: int, k_raw, k_pool, rms_w=None
     _check(load().qsa_pool_append(C.byref(c), _ptr(k_new, H16, name="k_new"), n_new, n_before,
                                   _ptr(k_raw, H16, name="k_raw"), _ptr(k_pool, H16, name="k_pool"),
                                   _ptr(rms_w, torch.float32, name="rms_w"), _stream()))
+
+
+def qsa_pool_rebuild(cfg: Config, k_raw, k_pool, b_from: int, n_tokens: int, rms_w=None) -> None:
+    c = cfg.c()
+    _check(load().qsa_pool_rebuild(C.byref(c), _ptr(k_raw, H16, name="k_raw"),
+                                   _ptr(k_pool, H16, name="k_pool"),
+                                   _ptr(rms_w, torch.float32, name="rms_w"), b_from, n_tokens,
+                                   _stream()))
 
 
 def qsa_kv_append(cfg: Config, k_new, v_new, n_before: int, k_cache, v_cache) -> None:

@@ -267,6 +267,41 @@ int qsa_pool_append(const qsa_config *cfg, const uint16_t *k_new, int32_t n_new,
     return QSA_OK;
 }
 
+int qsa_pool_rebuild(const qsa_config *cfg, const uint16_t *k_raw, uint16_t *k_pool,
+                     const float *rms_w, int32_t b_from, int32_t n_tokens, qsa_stream_t stream)
+{
+    int r = check_cfg(cfg);
+    if (r)
+        return r;
+    if (n_tokens < 0 || n_tokens > cfg->cap_tokens)
+        return fail(QSA_ERR_INVALID, "qsa_pool_rebuild: n_tokens=%d outside [0, %d]", n_tokens,
+                    cfg->cap_tokens);
+    const int32_t nb = n_tokens / kBlockTokens;
+    if (b_from < 0 || b_from > nb)
+        return fail(QSA_ERR_INVALID, "qsa_pool_rebuild: b_from=%d outside [0, %d]", b_from, nb);
+    if (b_from == nb)
+        return QSA_OK;
+    NEED_PTR(k_raw);
+    NEED_PTR(k_pool);
+    OPT_PTR(rms_w);
+    // the append's pooling with every token taken from k_raw and nothing copied
+    AppendArgs a;
+    memset(&a, 0, sizeof(a));
+    a.k_new = H(k_raw);
+    a.n_before = n_tokens;
+    a.k_raw = H(const_cast<uint16_t *>(k_raw));
+    a.k_pool = H(k_pool);
+    a.rms_w = rms_w;
+    a.H = cfg->h_idx;
+    a.d = cfg->d_idx;
+    a.b_lo = b_from;
+    a.n_blocks = nb - b_from;
+    a.eps = cfg->rms_eps;
+    a.base = cfg->rope_base;
+    HIP_CHECK(launch_append(a, (hipStream_t)stream));
+    return QSA_OK;
+}
+
 int qsa_kv_append(const qsa_config *cfg, const uint16_t *k_new, const uint16_t *v_new,
                   int32_t n_new, int32_t n_before, uint16_t *k_cache, uint16_t *v_cache,
                   qsa_stream_t stream)

@@ -110,6 +110,14 @@ def test_entry_points_reject_bad_arguments_on_the_host(lib):
     assert lib.qsa_pool_append(cp, FAKE, -1, 0, FAKE, FAKE, None, None) == qb.QSA_ERR_INVALID
     # n_new == 0 is a no-op that succeeds without touching anything
     assert lib.qsa_pool_append(cp, None, 0, 0, None, None, None, None) == qb.QSA_OK
+    # rebuild: b_from outside [0, floor(n_tokens/4)], n_tokens past capacity, NULL caches;
+    # an empty range is a no-op
+    assert lib.qsa_pool_rebuild(cp, FAKE, FAKE, None, 26, 100, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_pool_rebuild(cp, FAKE, FAKE, None, -1, 100, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_pool_rebuild(cp, FAKE, FAKE, None, 0, 4097, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_pool_rebuild(cp, None, FAKE, None, 0, 100, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_pool_rebuild(cp, FAKE, MISALIGNED, None, 0, 100, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_pool_rebuild(cp, None, None, None, 25, 103, None) == qb.QSA_OK
     # score: ld too small
     assert lib.qsa_index_score(cp, FAKE, 1, 4000, FAKE, FAKE, 10, None) == qb.QSA_ERR_INVALID
     # top-k: workspace too small

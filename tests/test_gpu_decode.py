@@ -57,6 +57,61 @@ def test_incremental_append_is_bitwise_chunk_append(gpu):
     assert np.array_equal(pa, host(c.k_pool).view(np.uint16))
 
 
+# ------------------------------------------------------------------ cache lifecycle
+def test_pool_rebuild_after_state_load_and_edit(gpu):
+    # a state load (only the raw keys restored) and a sequence edit from token t on:
+    # rebuilding from block 0 / from block t // 4 gives the bits of a fresh append
+    H, d, n = 16, 128, 4 * 900 + 3
+    cfg = qb.Config(h_idx=H, d_idx=d, cap_tokens=4 * 904)
+    raw = synth.normal_f16(13, (n, H, d))
+    ref = qb.Layer(cfg)
+    qb.qsa_pool_append(cfg, dev(raw), 0, ref.k_raw, ref.k_pool)
+    loaded = qb.Layer(cfg)
+    loaded.k_raw[:n] = dev(raw)
+    loaded.k_pool.fill_(7.0)  # stale content from before the load
+    qb.qsa_pool_rebuild(cfg, loaded.k_raw, loaded.k_pool, 0, n)
+    nb = n // 4
+    assert np.array_equal(host(loaded.k_pool[:nb]).view(np.uint16),
+                          host(ref.k_pool[:nb]).view(np.uint16))
+    assert np.all(host(loaded.k_pool[nb:]) == 7.0)  # the incomplete block is not touched
+    # edit tokens [t, n) and rebuild from the block holding t
+    t = 4 * 517 + 2
+    edited = raw.copy()
+    edited[t:] = synth.normal_f16(14, (n - t, H, d))
+    loaded.k_raw[t:n] = dev(edited[t:])
+    qb.qsa_pool_rebuild(cfg, loaded.k_raw, loaded.k_pool, t // 4, n)
+    fresh = qb.Layer(cfg)
+    qb.qsa_pool_append(cfg, dev(edited), 0, fresh.k_raw, fresh.k_pool)
+    assert np.array_equal(host(loaded.k_pool[:nb]).view(np.uint16),
+                          host(fresh.k_pool[:nb]).view(np.uint16))
+    assert_pool_close(host(loaded.k_pool[:nb]), O.pool_rebuild(edited, n))
+
+
+def test_speculative_rollback_needs_no_rebuild(gpu):
+    # decode steps append 4 draft tokens that complete a block, the drafts are
+    # rejected (the count rolls back), other tokens are decoded in their place: the
+    # caches and every step's output equal those of a run that never saw the drafts
+    w = small(4 * 2000 + 1)
+    L, cfg, g, o = setup_decode(w)
+    n0 = L["n_prefix"]                        # 8000 tokens: block 1999 is complete
+    drafts = synth.normal_f16(70, (4, 16, 128))
+    ws = qb.workspace(cfg, 1, w.cap_tokens)
+    out = torch.empty((w.hq, w.dv), device="cuda")
+    for j in range(4):  # positions n0 .. n0 + 3; the last one completes block 2000
+        qb.qsa_decode_step(cfg, g, n0 + j, dev(L["q_idx"]), dev(drafts[j]), dev(L["q"]),
+                           dev(L["k_new"][j]), dev(L["v_new"][j]), out, ws)
+    assert host(g.k_pool[2000]).any()
+    # rejected: decode the accepted tokens from position n0 again
+    for step in range(4):
+        check_step(w, L, cfg, g, o, n0 + step, step, qb.QSA_STEP_FUSED_GATHER)
+    clean = qb.Layer(cfg)
+    qb.qsa_pool_append(cfg, dev(L["raw"]), 0, clean.k_raw, clean.k_pool)
+    qb.qsa_pool_append(cfg, dev(L["k_idx_new"]), n0, clean.k_raw, clean.k_pool)
+    nb = (n0 + 4) // 4
+    assert np.array_equal(host(g.k_pool[:nb]).view(np.uint16),
+                          host(clean.k_pool[:nb]).view(np.uint16))
+
+
 # ------------------------------------------------------------------ a2 scores
 @pytest.mark.parametrize("H,d,nb", [(16, 128, 3001), (4, 64, 1024), (16, 128, 1), (2, 64, 333),
                                     (8, 128, 2047), (32, 128, 100)])
