@@ -136,23 +136,39 @@ def bench_decode(args):
         torch.cuda.synchronize()
         log(f"[setup] layer {li} ready ({time.time() - t0:.1f}s)")
     n0 = host0["n_prefix"]
-    ws = qb.workspace(cfg, 1, w.cap_tokens, dev)
+    rows = args.rows
+    ws = qb.workspace(cfg, rows, w.cap_tokens, dev)
     flags = qb.QSA_STEP_COMPACT_GATHER if args.compact_gather else qb.QSA_STEP_FUSED_GATHER
+    # positions cycle over the 4 new tokens of each layer (rows > 1: verification
+    # steps over tokens j .. j + rows - 1, every row with the layer's queries)
+    n_pos = 4 - rows + 1
+    if rows > 1:
+        for st in layers:
+            st["q_idx_r"] = st["q_idx"].unsqueeze(0).repeat(rows, 1, 1).contiguous()
+            st["q_r"] = st["q"].unsqueeze(0).repeat(rows, 1, 1).contiguous()
+            st["out_r"] = torch.empty((rows, w.hq, w.dv), dtype=torch.float32, device=dev)
 
     def token(j):
         for st in layers:
-            qb.qsa_decode_step(cfg, st["layer"], n0 + j, st["q_idx"], st["k_idx_new"][j], st["q"],
-                               st["k_new"][j], st["v_new"][j], st["out"], ws, flags=flags)
+            if rows == 1:
+                qb.qsa_decode_step(cfg, st["layer"], n0 + j, st["q_idx"], st["k_idx_new"][j],
+                                   st["q"], st["k_new"][j], st["v_new"][j], st["out"], ws,
+                                   flags=flags)
+            else:
+                qb.qsa_decode_multi(cfg, st["layer"], n0 + j, st["q_idx_r"],
+                                    st["k_idx_new"][j:j + rows], st["q_r"],
+                                    st["k_new"][j:j + rows], st["v_new"][j:j + rows],
+                                    st["out_r"], ws)
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for j in range(4):
+        for j in range(n_pos):
             token(j)          # eager: also sets kernel attributes before any capture
     stream.synchronize()
 
     graphs = []
     if not args.eager:
-        for j in range(4):
+        for j in range(n_pos):
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr, stream=stream):
                 token(j)
@@ -163,9 +179,9 @@ def bench_decode(args):
         with torch.cuda.stream(stream):
             for i in range(i0, i0 + n):
                 if graphs:
-                    graphs[i % 4].replay()
+                    graphs[i % n_pos].replay()
                 else:
-                    token(i % 4)
+                    token(i % n_pos)
 
     run_tokens(0, args.warmup)
     stream.synchronize()
@@ -206,11 +222,15 @@ def bench_decode(args):
 
     # whole-step algorithmic bandwidth, averaged over the 4-step position cycle
     per = []
-    for j in range(4):
-        N = w.n_tokens + j
-        nbj = N // 4
-        cells = 4 * min(w.topk, nbj) + N % 4
-        per.append(sum(decode_bytes(w, nbj, cells)))
+    for j in range(n_pos):
+        b = []
+        for r in range(rows):
+            N = w.n_tokens + j + r
+            nbj = N // 4
+            cells = 4 * min(w.topk, nbj) + N % 4
+            b.append(decode_bytes(w, nbj, cells))
+        # the pooled cache is streamed once per step, whatever the number of rows
+        per.append(b[-1][0] + sum(sum(x[1:]) for x in b))
     step_bytes = float(np.mean(per))
     step_s = (ms / 1e3) / (args.steps * n_layers)
     step_gbps = step_bytes / step_s / 1e9
@@ -252,8 +272,20 @@ def bench_decode(args):
             "us_per_layer_step": round(step_s * 1e6, 3),
         },
     }
+    if rows > 1:
+        res["metric"] = f"QSA layer verification steps/s ({rows} query rows) at 256k ctx"
+        res["unit"] = "layer-verify-steps/s"
+        res["config"]["rows"] = rows
+        res["config"]["step"] = (f"one verification step = all layers, serially, each appending "
+                                 f"and attending {rows} query rows (qsa_decode_multi)")
+        res["config"]["query_rows_per_s"] = round(layer_steps_s * rows, 2)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = run_cpu_baseline(w, host0, args.cpu_budget)
+        cb = run_cpu_baseline(w, host0, args.cpu_budget)
+        if rows > 1:  # the oracle checks rows one decode step at a time
+            cb["value"] /= rows
+            cb["unit"] = "layer-verify-steps/s"
+            cb["sample"] += f"; a verification step is {rows} of them"
+        res["cpu_baseline"] = cb
     return res
 
 
@@ -449,6 +481,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
     ap.add_argument("--eager", action="store_true", help="launch per call instead of graphs")
     ap.add_argument("--compact-gather", action="store_true")
+    ap.add_argument("--rows", type=int, default=1, choices=[1, 2, 3, 4],
+                    help="query rows per layer step (> 1: speculative-draft verification "
+                         "steps, qsa_decode_multi)")
     ap.add_argument("--kernel-reps", type=int, default=240)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)

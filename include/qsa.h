@@ -221,6 +221,28 @@ int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_be
                     qsa_stream_t stream);
 
 /*
+ * Multi-query decode step for checking speculative draft tokens (Qiita part 12,
+ * 「MTPを入れたらPPが遅くなるのは仕方がないのか？」: the target model checks the
+ * draft's tokens together; its setup table runs DraftMax = 2, so a step carries
+ * up to 3 tokens).  Appends the n_q tokens at positions [n_before, n_before + n_q)
+ * to all four caches; row r then runs steps 2-5 causally with N_r = n_before + r + 1
+ * visible tokens, its own top-k and its own cells.  The pooled cache is streamed
+ * once for all rows.  The result equals n_q qsa_decode_step calls in order.
+ * n_q in [1, 4]; q_idx [n_q][h_idx][d_idx], k_idx_new [n_q][h_idx][d_idx],
+ * q [n_q][hq][d], k_new/v_new [n_q][hkv][d|dv], out [n_q][hq][dv] fp32.
+ * Optional: scores_out [n_q][ld_scores] (ld_scores >= floor((n_before + n_q)/4);
+ * row r defined for b < floor(N_r/4)), blk_out [n_q][k] (row r: min(k, floor(N_r/4))
+ * ids, ascending).  Rejected rows need no undo: see qsa_pool_rebuild.
+ * Errors: INVALID (n_q outside [1, 4], ld_scores too small, null or misaligned
+ * pointers), CAPACITY (n_before + n_q > cap_tokens, workspace too small).
+ */
+int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
+                     int32_t n_q, const uint16_t *q_idx, const uint16_t *k_idx_new,
+                     const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, float *out,
+                     float *scores_out, int32_t ld_scores, int32_t *blk_out, void *ws,
+                     size_t ws_bytes, qsa_stream_t stream);
+
+/*
  * One prefill chunk of one layer: appends n_new tokens at positions
  * [n_before, n_before + n_new) to all four caches, then every chunk row runs
  * steps 2-5 causally (row r sees N_r = n_before + r + 1 tokens).

@@ -29,9 +29,9 @@ QSA_STEP_COMPACT_GATHER = 1
 EXPORTS = [
     "qsa_status_string", "qsa_last_error", "qsa_config_check", "qsa_workspace_size",
     "qsa_workspace_init", "qsa_pool_append", "qsa_pool_rebuild", "qsa_kv_append",
-    "qsa_index_score",
-    "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_attn", "qsa_prefill_attn",
-    "qsa_decode_step", "qsa_prefill_step", "qsa_mla_workspace_size", "qsa_mla_sparse_attn",
+    "qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_attn",
+    "qsa_prefill_attn", "qsa_decode_step", "qsa_decode_multi", "qsa_prefill_step",
+    "qsa_mla_workspace_size", "qsa_mla_sparse_attn",
 ]
 
 
@@ -82,6 +82,8 @@ def load():
         "qsa_prefill_attn": (C.c_int, [cfg, p, i32, i32, p, i32, p, p, p, p, sz, p]),
         "qsa_decode_step": (C.c_int, [cfg, C.POINTER(qsa_layer_bufs), i32, p, p, p, p, p, p, p,
                                       p, u32, p, sz, p]),
+        "qsa_decode_multi": (C.c_int, [cfg, C.POINTER(qsa_layer_bufs), i32, i32, p, p, p, p, p,
+                                       p, p, i32, p, p, sz, p]),
         "qsa_prefill_step": (C.c_int, [cfg, C.POINTER(qsa_layer_bufs), i32, i32, p, p, p, p, p,
                                        p, p, i32, p, p, sz, p]),
         "qsa_mla_workspace_size": (sz, [i32, i32, i32]),
@@ -265,6 +267,20 @@ def qsa_decode_step(cfg: Config, layer: Layer, n_before: int, q_idx, k_idx_new, 
                                   _ptr(scores_out, torch.float32, name="scores_out"),
                                   _ptr(blk_out, torch.int32, name="blk_out"), flags, _ptr(ws),
                                   ws.numel(), _stream()))
+
+
+def qsa_decode_multi(cfg: Config, layer: Layer, n_before: int, q_idx, k_idx_new, q, k_new, v_new,
+                     out, ws, scores_out=None, ld_scores: int = 0, blk_out=None) -> None:
+    c = cfg.c()
+    b = layer.bufs()
+    _check(load().qsa_decode_multi(C.byref(c), C.byref(b), n_before, q_idx.shape[0],
+                                   _ptr(q_idx, H16, name="q_idx"),
+                                   _ptr(k_idx_new, H16, name="k_idx_new"), _ptr(q, H16, name="q"),
+                                   _ptr(k_new, H16, name="k_new"), _ptr(v_new, H16, name="v_new"),
+                                   _ptr(out, torch.float32, name="out"),
+                                   _ptr(scores_out, torch.float32, name="scores_out"), ld_scores,
+                                   _ptr(blk_out, torch.int32, name="blk_out"), _ptr(ws), ws.numel(),
+                                   _stream()))
 
 
 def qsa_prefill_step(cfg: Config, layer: Layer, n_before: int, q_idx, k_idx_new, q, k_new, v_new,

@@ -440,12 +440,12 @@ hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_combine(const float *part, int32_t hq, int32_t splits, int32_t dv, float *out,
-                          hipStream_t s)
+hipError_t launch_combine(const float *part, int32_t hq, int32_t splits, int32_t dv, int32_t rows,
+                          float *out, hipStream_t s)
 {
-    if (splits < 1 || splits > kAttnMaxSplits)
+    if (splits < 1 || splits > kAttnMaxSplits || rows < 1)
         return hipErrorInvalidValue;
-    const dim3 grid((uint32_t)hq, 1);
+    const dim3 grid((uint32_t)hq, (uint32_t)rows);
     switch (dv) {
     case 64:
         hipLaunchKernelGGL((attn_combine_kernel<64>), grid, dim3(kCombThreads), 0, s, part, hq,

@@ -60,23 +60,28 @@ __device__ __forceinline__ void list_insert(uint64_t (&top)[kListLen], uint64_t 
     }
 }
 
-template <int ROWC, int U, int NT, bool STEP>
+// NQ queries (rows of q, ROWC 16-byte chunks each) score every row read once;
+// query i's scores go to scores[i * ld + b].  APPEND: work group 0 runs the
+// append.  LISTS (one query): candidate lists in the epilogue.
+template <int ROWC, int U, int NT, int NQ, bool APPEND, bool LISTS>
 __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict__ q,
                                                           const h16 *__restrict__ pool,
                                                           int32_t nb, float *__restrict__ scores,
-                                                          AppendArgs ap, CandLists cl)
+                                                          int32_t ld, AppendArgs ap, CandLists cl)
 {
     constexpr int NW = NT / kWave;
     constexpr int LPR = ROWC < kWave ? ROWC : kWave;  // lanes per row
     constexpr int CPL = ROWC / LPR;                   // chunks per lane per row
     constexpr int RPW = kWave / LPR;                  // rows per wave per group
-    static_assert(!STEP || NW * kListLen <= kWave, "one merged entry per lane of wave 0");
+    static_assert(!LISTS || (APPEND && NQ == 1), "candidate lists: the one-query decode step");
+    static_assert(!LISTS || NW * kListLen <= kWave, "one merged entry per lane of wave 0");
+    static_assert(NQ >= 1 && NQ <= NW, "one wave per query for the appended row");
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int sub = lane % LPR;
     const int rsub = lane / LPR;
 
-    if (STEP && blockIdx.x == 0) {
+    if (APPEND && blockIdx.x == 0) {
         // append work group (dispatched first): [d/2] (cos, sin) pairs, then the pooled row
         extern __shared__ __align__(16) unsigned char lds[];
         f32x2 *cs = (f32x2 *)lds;
@@ -86,34 +91,38 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
         if (ap.n_blocks == 1) {
             append_pool<NT>(ap, ap.b_lo, 1, cs, row);
             __syncthreads();
-            if (wave == 0) {
-                const float sc = score_row_lds<ROWC>(q, row);
+            if (wave < NQ) {
+                const float sc = score_row_lds<ROWC>(q + (int64_t)wave * ROWC * 8, row);
                 if (lane == 0)
-                    scores[ap.b_lo] = sc;
+                    scores[(int64_t)wave * ld + ap.b_lo] = sc;
                 mine = rank_key(sc, (uint32_t)ap.b_lo);
             }
         }
-        // its list: the new block (if any), then empty slots
-        if (wave == 0 && lane < kListLen)
-            cl.list[lane] = lane == 0 ? mine : 0ull;
-        if (threadIdx.x == 0)
-            cl.rows[0] = (uint32_t)ap.n_blocks;
+        if (LISTS) {
+            // its list: the new block (if any), then empty slots
+            if (wave == 0 && lane < kListLen)
+                cl.list[lane] = lane == 0 ? mine : 0ull;
+            if (threadIdx.x == 0)
+                cl.rows[0] = (uint32_t)ap.n_blocks;
+        }
         return;
     }
 
-    __shared__ uint64_t wtop[STEP ? NW * kListLen : 1];
+    __shared__ uint64_t wtop[LISTS ? NW * kListLen : 1];
     __shared__ uint32_t wrows[NW];
     __shared__ uint32_t wdone;
-    if (STEP) {
+    if (LISTS) {
         if (threadIdx.x == 0)
             wdone = 0;
         __syncthreads();
     }
 
-    h16x8 qv[CPL];
+    h16x8 qv[NQ][CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; j++)
-        qv[j] = ((const h16x8 *)q)[sub + LPR * j];
+    for (int qi = 0; qi < NQ; qi++)
+#pragma unroll
+        for (int j = 0; j < CPL; j++)
+            qv[qi][j] = ((const h16x8 *)q)[qi * ROWC + sub + LPR * j];
 
     const int64_t groups = ((int64_t)nb + RPW - 1) / RPW;
     // scan wave index: runs of 4 consecutive row groups per work group (16 KiB
@@ -121,9 +130,9 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
     // not), the runs of one round spread over the work groups, so a run of
     // high-scoring neighbours puts at most 4 rows into any candidate list
     constexpr int kRun = NW < 4 ? NW : 4;
-    const int64_t nwg = (int64_t)gridDim.x - (STEP ? 1 : 0);
+    const int64_t nwg = (int64_t)gridDim.x - (APPEND ? 1 : 0);
     const int64_t gw =
-        ((int64_t)(wave / kRun) * nwg + (blockIdx.x - (STEP ? 1 : 0))) * kRun + wave % kRun;
+        ((int64_t)(wave / kRun) * nwg + (blockIdx.x - (APPEND ? 1 : 0))) * kRun + wave % kRun;
     const int64_t tw = nwg * NW;
     const h16x8 *rows = (const h16x8 *)pool;
     uint64_t top[kListLen];
@@ -151,12 +160,17 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
         for (int u = 0; u < U; u++) {
             float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < CPL; j++)
-                acc = dot8(qv[j], kv[u][j], acc);
-            acc = group_sum<LPR>(acc);
-            if (sub == 0 && r[u] < nb)
-                scores[r[u]] = acc;
-            if (STEP) {
+            for (int qi = 0; qi < NQ; qi++) {
+                float a = 0.f;
+#pragma unroll
+                for (int j = 0; j < CPL; j++)
+                    a = dot8(qv[qi][j], kv[u][j], a);
+                a = group_sum<LPR>(a);
+                if (sub == 0 && r[u] < nb)
+                    scores[(int64_t)qi * ld + r[u]] = a;
+                acc = a;
+            }
+            if (LISTS) {
                 // the RPW rows of this group, one at a time, as wave-uniform values
 #pragma unroll
                 for (int rs = 0; rs < RPW; rs++) {
@@ -172,7 +186,7 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
         }
     }
 
-    if (STEP) {
+    if (LISTS) {
         // no barrier: each wave posts its list and counts itself done; the last
         // wave of the work group merges (earlier waves just end)
         if (lane == 0) {
@@ -232,16 +246,49 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
     }
 }
 
-template <int ROWC>
-hipError_t launch_rowc(const h16 *q, const h16 *pool, int32_t nb, float *scores,
-                       const AppendArgs *ap, const CandLists *cl, int32_t *n_lists, hipStream_t s)
+template <int ROWC, int NQ>
+hipError_t launch_step(const h16 *q, const h16 *pool, int32_t nb, float *scores, int32_t ld,
+                       const AppendArgs &ap, const CandLists *cl, int32_t *n_lists, hipStream_t s)
 {
     constexpr int U = ROWC >= 128 ? 2 : 4;
     constexpr int LPR = ROWC < kWave ? ROWC : kWave;
     constexpr int RPW = kWave / LPR;
+    constexpr int NW = kStepThreads / kWave;
     const int64_t groups = ((int64_t)nb + RPW - 1) / RPW;
+    // one scan work group per 8 row groups (so every wave starts with a group), at
+    // most kListWgs - 1 of them: the lists, the append work group's included, fit
+    // one per thread of the top-k selection
+    int64_t grid = (groups + NW - 1) / NW;
+    if (grid > kListWgs - 1)
+        grid = kListWgs - 1;
+    if (grid < 1)
+        grid = 1;
+    const size_t lds = sizeof(f32x2) * (size_t)(ap.d / 2) + sizeof(h16) * (size_t)ROWC * 8;
+    if (cl) {
+        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kStepThreads, 1, true, true>),
+                           dim3((uint32_t)grid + 1), dim3(kStepThreads), lds, s, q, pool, nb,
+                           scores, ld, ap, *cl);
+        *n_lists = (int32_t)grid + 1;
+    } else {
+        const CandLists nol{};
+        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kStepThreads, NQ, true, false>),
+                           dim3((uint32_t)grid + 1), dim3(kStepThreads), lds, s, q, pool, nb,
+                           scores, ld, ap, nol);
+    }
+    return hipGetLastError();
+}
+
+template <int ROWC>
+hipError_t launch_rowc(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb, float *scores,
+                       int32_t ld, const AppendArgs *ap, const CandLists *cl, int32_t *n_lists,
+                       hipStream_t s)
+{
     if (!ap) {
+        constexpr int U = ROWC >= 128 ? 2 : 4;
+        constexpr int LPR = ROWC < kWave ? ROWC : kWave;
+        constexpr int RPW = kWave / LPR;
         constexpr int NW = kThreads / kWave;
+        const int64_t groups = ((int64_t)nb + RPW - 1) / RPW;
         int64_t grid = (groups + (int64_t)NW * U - 1) / ((int64_t)NW * U);
         if (grid > 2048)
             grid = 2048;
@@ -249,47 +296,41 @@ hipError_t launch_rowc(const h16 *q, const h16 *pool, int32_t nb, float *scores,
             grid = 1;
         const AppendArgs none{};
         const CandLists nol{};
-        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kThreads, false>), dim3((uint32_t)grid),
-                           dim3(kThreads), 0, s, q, pool, nb, scores, none, nol);
-    } else {
-        // one scan work group per 8 row groups (so every wave starts with a
-        // group), at most kListWgs - 1 of them: the lists, the append
-        // work group's included, fit one per thread of the top-k kernel
-        constexpr int NW = kStepThreads / kWave;
-        int64_t grid = (groups + NW - 1) / NW;
-        if (grid > kListWgs - 1)
-            grid = kListWgs - 1;
-        if (grid < 1)
-            grid = 1;
-        const size_t lds = sizeof(f32x2) * (size_t)(ap->d / 2) + sizeof(h16) * (size_t)ROWC * 8;
-        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kStepThreads, true>),
-                           dim3((uint32_t)grid + 1), dim3(kStepThreads), lds, s, q, pool, nb,
-                           scores, *ap, *cl);
-        *n_lists = (int32_t)grid + 1;
+        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kThreads, 1, false, false>),
+                           dim3((uint32_t)grid), dim3(kThreads), 0, s, q, pool, nb, scores, ld,
+                           none, nol);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    switch (n_q) {
+    case 1: return launch_step<ROWC, 1>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
+    case 2: return launch_step<ROWC, 2>(q, pool, nb, scores, ld, *ap, nullptr, n_lists, s);
+    case 3: return launch_step<ROWC, 3>(q, pool, nb, scores, ld, *ap, nullptr, n_lists, s);
+    case 4: return launch_step<ROWC, 4>(q, pool, nb, scores, ld, *ap, nullptr, n_lists, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_score_decode(const h16 *q, const h16 *pool, int32_t nb, int32_t row_elems,
-                               float *scores, const AppendArgs *ap, const CandLists *cl,
-                               int32_t *n_lists, hipStream_t s)
+hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb,
+                               int32_t row_elems, float *scores, int32_t ld, const AppendArgs *ap,
+                               const CandLists *cl, int32_t *n_lists, hipStream_t s)
 {
     if (nb <= 0 && !ap)
         return hipSuccess;
-    // the fused append builds at most one pooled row, of the block right after
-    // the scanned ones, in the layout the scan reads
-    if (ap && (!cl || !n_lists || ap->n_blocks > 1 || (ap->n_blocks == 1 && ap->b_lo != nb) ||
-               (int64_t)ap->H * ap->d != row_elems))
+    // the fused append builds at most one pooled row, of the block right after the
+    // scanned ones, in the layout the scan reads; candidate lists for one query only
+    if (n_q < 1 || n_q > 4 || (!ap && n_q != 1) || (cl && (n_q != 1 || !n_lists)) ||
+        (ap && (ap->n_blocks > 1 || (ap->n_blocks == 1 && ap->b_lo != nb) ||
+                (int64_t)ap->H * ap->d != row_elems)))
         return hipErrorInvalidValue;
     switch (row_elems / 8) {
-    case 16: return launch_rowc<16>(q, pool, nb, scores, ap, cl, n_lists, s);
-    case 32: return launch_rowc<32>(q, pool, nb, scores, ap, cl, n_lists, s);
-    case 64: return launch_rowc<64>(q, pool, nb, scores, ap, cl, n_lists, s);
-    case 128: return launch_rowc<128>(q, pool, nb, scores, ap, cl, n_lists, s);
-    case 256: return launch_rowc<256>(q, pool, nb, scores, ap, cl, n_lists, s);
-    case 512: return launch_rowc<512>(q, pool, nb, scores, ap, cl, n_lists, s);
+    case 16: return launch_rowc<16>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
+    case 32: return launch_rowc<32>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
+    case 64: return launch_rowc<64>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
+    case 128: return launch_rowc<128>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
+    case 256: return launch_rowc<256>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
+    case 512: return launch_rowc<512>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -4,7 +4,7 @@
 // gather（COMMON-005）": attention over those cells; the COMMON-006 section:
 // selection in the block domain).
 //
-// Grid: (split, KV head), 1024 threads.  Every work group first selects the
+// Grid: (split, KV head, query row), 1024 threads.  Every work group first selects the
 // same top-k blocks from the decode scan's candidate lists (lists_select; the
 // whole score row if the lists are not enough), in the deterministic order of
 // the selection (attention does not depend on the order of its cells); the
@@ -18,8 +18,10 @@
 // microseconds of LDS work but saves a kernel boundary and a round trip through
 // global memory for the chosen ids.
 //
-// Work group (0, 0) also writes blk_out (ascending ids, through an LDS bitmap)
-// and n_sel when asked for.
+// Work group (0, 0, r) also writes row r's blk_out (ascending ids, through an
+// LDS bitmap) when asked for.  Rows of a multi-query step see N_r = pos0 + r + 1
+// tokens, each its own selection; splits past a row's cells leave a partial the
+// combine weighs 0.
 #include "qsa_select.h"
 
 namespace qsa {
@@ -29,20 +31,20 @@ constexpr int kNT = kSelThreads;  // 16 waves
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct TailArgs {
-    CandLists cl;
+    CandLists cl;         // row r's lists at list + r * kListWgs * kListLen, rows + r * kListWgs
     int32_t n_lists;
-    const float *scores;  // the score row (fallback selection)
-    int32_t n_tokens;     // N: the context after the step's append
+    const float *scores;  // [rows][ld] score rows (fallback selection)
+    int32_t ld;
+    int32_t pos0;         // row r is the token at position pos0 + r: N_r = pos0 + r + 1
     int32_t k;
-    const h16 *q;         // [hq][D]
+    const h16 *q;         // [rows][hq][D]
     const h16 *kc;        // [N][hkv][D]
     const h16 *vc;        // [N][hkv][DV]
     int32_t hq, hkv;
     float scale;
-    int32_t splits;       // ceil(cells / 64)
-    float *part;          // [hq][splits][DV + 2]
-    int32_t *blk_out;     // optional
-    int32_t *n_sel;       // optional
+    int32_t splits;       // ceil(cells / 64) of the row with the most cells
+    float *part;          // [rows][hq][splits][DV + 2]
+    int32_t *blk_out;     // optional, [rows][k]
 };
 
 template <int G, int D, int DV>
@@ -89,16 +91,30 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
 
     __shared__ TailLds<G, D, DV> sm;
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-    const int split = blockIdx.x, g = blockIdx.y;
-    const int32_t N = a.n_tokens, nb = N / kBlockTokens;
+    const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
+    const int32_t N = a.pos0 + row + 1, nb = N / kBlockTokens;
     const int32_t nsel = nb < a.k ? nb : a.k;
     const int32_t cells = kBlockTokens * nsel + (N - kBlockTokens * nb);
+    float *part = a.part + (int64_t)row * a.hq * a.splits * (DV + 2);
+    if (split * kAttnChunk >= cells) {
+        // past this row's cells (rows of one call differ by up to 3): a partial
+        // that the combine weighs 0
+        for (int o = t; o < G * (DV + 2); o += kNT) {
+            const int h = o / (DV + 2), j = o % (DV + 2);
+            part[(((int64_t)g * G + h) * a.splits + split) * (DV + 2) + j] = j == 0 ? -INFINITY : 0.f;
+        }
+        return;
+    }
+    const float *scores = a.scores + (int64_t)row * a.ld;
+    CandLists cl = a.cl;
+    cl.list += (int64_t)row * kListWgs * kListLen;
+    cl.rows += (int64_t)row * kListWgs;
     const int32_t c_lo = split * kAttnChunk;       // this split's cells
     const int32_t b_lo = c_lo / kBlockTokens;      // its chosen-block positions
     const int32_t b_hi = b_lo + kAttnChunk / kBlockTokens;
 
     // the query rows of this KV head (independent of the selection)
-    const h16 *qrow = a.q + (int64_t)g * G * D;
+    const h16 *qrow = a.q + ((int64_t)row * a.hq + (int64_t)g * G) * D;
     for (int i = t; i < G * D / 8; i += kNT)
         ((h16x8 *)sm.qs)[i] = ((const h16x8 *)qrow)[i];
     // the split's tail cells (the incomplete block, after the chosen ones)
@@ -120,6 +136,7 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
 
     // ---- 1. selection
     const bool want_blk = a.blk_out && blockIdx.x == 0 && blockIdx.y == 0;
+    int32_t *blk_out = a.blk_out ? a.blk_out + (int64_t)row * a.k : nullptr;
     if (nb <= a.k) {
         for (int32_t i = t; i < nb; i += kNT) {
             place(i, i);
@@ -129,7 +146,7 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
     } else {
         uint64_t R[kListLen];
         uint32_t nrows;
-        load_list(a.cl, a.n_lists, R, &nrows);
+        load_list(cl, a.n_lists, R, &nrows);
         uint64_t rs = 0;
         if (lists_select(R, nrows, t < a.n_lists, (uint32_t)a.k, sm.L, &rs)) {
             uint32_t c = 0;
@@ -159,7 +176,7 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
                 }
         } else {
             __syncthreads();
-            select_row_global<kNT>(a.scores, (uint32_t)nb, a.k, sm.ids, sm.L.hist[0],
+            select_row_global<kNT>(scores, (uint32_t)nb, a.k, sm.ids, sm.L.hist[0],
                                    sm.u.sel.cand, sm.u.sel.bitmap, sm.L.S);
             __syncthreads();
             for (int32_t i = t; i < nsel; i += kNT)
@@ -169,14 +186,12 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
     __syncthreads();
 
     if (want_blk) {
-        if (a.n_sel && t == 0)
-            a.n_sel[0] = nsel;
         zero_words<kNT>(sm.u.sel.bitmap, ((uint32_t)nb + 31) / 32);
         __syncthreads();
         for (int32_t i = t; i < nsel; i += kNT)
             set_bit(sm.u.sel.bitmap, (uint32_t)sm.ids[i]);
         __syncthreads();
-        compact_bitmap<kNT>(sm.u.sel.bitmap, (uint32_t)nb, a.blk_out, (uint32_t)a.k, sm.L.S);
+        compact_bitmap<kNT>(sm.u.sel.bitmap, (uint32_t)nb, blk_out, (uint32_t)a.k, sm.L.S);
         __syncthreads();  // the bitmap shares LDS with the attention arrays
     }
 
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
             for (int u = 0; u < 4; u++)
                 acc += p4[u] * (float)sm.u.att.vs[(c4 + u) * DV + d];
         }
-        float *pb = a.part + (((int64_t)g * G + h) * a.splits + split) * (DV + 2);
+        float *pb = part + (((int64_t)g * G + h) * a.splits + split) * (DV + 2);
         if (d == 0) {
             pb[0] = sm.u.att.ml[h][0];
             pb[1] = sm.u.att.ml[h][1];
@@ -249,9 +264,9 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
 }
 
 template <int D, int DV>
-hipError_t launch_d(const TailArgs &a, int G, hipStream_t s)
+hipError_t launch_d(const TailArgs &a, int G, int rows, hipStream_t s)
 {
-    const dim3 grid((uint32_t)a.splits, (uint32_t)a.hkv);
+    const dim3 grid((uint32_t)a.splits, (uint32_t)a.hkv, (uint32_t)rows);
     switch (G) {
     case 1: hipLaunchKernelGGL((step_tail_kernel<1, D, DV>), grid, dim3(kNT), 0, s, a); break;
     case 2: hipLaunchKernelGGL((step_tail_kernel<2, D, DV>), grid, dim3(kNT), 0, s, a); break;
@@ -267,14 +282,17 @@ hipError_t launch_d(const TailArgs &a, int G, hipStream_t s)
 
 hipError_t launch_step_tail(const StepTail &st, hipStream_t s)
 {
-    if (st.n_tokens < 1 || st.k < 1 || st.k > kMaxTopk || st.n_tokens / kBlockTokens > kMaxBlocks ||
-        st.n_lists < 1 || st.n_lists > kListWgs || st.hq % st.hkv)
+    const int32_t n_last = st.pos0 + st.rows;  // tokens seen by the last row
+    if (st.rows < 1 || st.pos0 < 0 || st.k < 1 || st.k > kMaxTopk ||
+        n_last / kBlockTokens > kMaxBlocks || st.n_lists < 1 || st.n_lists > kListWgs ||
+        st.hq % st.hkv)
         return hipErrorInvalidValue;
     TailArgs a;
     a.cl = st.cl;
     a.n_lists = st.n_lists;
     a.scores = st.scores;
-    a.n_tokens = st.n_tokens;
+    a.ld = st.ld;
+    a.pos0 = st.pos0;
     a.k = st.k;
     a.q = st.q;
     a.kc = st.k_cache;
@@ -282,25 +300,28 @@ hipError_t launch_step_tail(const StepTail &st, hipStream_t s)
     a.hq = st.hq;
     a.hkv = st.hkv;
     a.scale = st.scale;
-    const int32_t nb = st.n_tokens / kBlockTokens;
-    const int32_t cells = kBlockTokens * (nb < st.k ? nb : st.k) + st.n_tokens % kBlockTokens;
-    a.splits = (cells + kAttnChunk - 1) / kAttnChunk;
+    int32_t max_cells = 0;
+    for (int32_t r = 0; r < st.rows; r++) {
+        const int32_t n = st.pos0 + r + 1, nb = n / kBlockTokens;
+        const int32_t c = kBlockTokens * (nb < st.k ? nb : st.k) + n % kBlockTokens;
+        max_cells = c > max_cells ? c : max_cells;
+    }
+    a.splits = (max_cells + kAttnChunk - 1) / kAttnChunk;
     if (a.splits > kAttnMaxSplits)
         return hipErrorInvalidValue;
     a.part = st.part;
     a.blk_out = st.blk_out;
-    a.n_sel = st.n_sel;
     const int G = st.hq / st.hkv;
     hipError_t e;
     if (st.d == 128 && st.dv == 128)
-        e = launch_d<128, 128>(a, G, s);
+        e = launch_d<128, 128>(a, G, st.rows, s);
     else if (st.d == 64 && st.dv == 64)
-        e = launch_d<64, 64>(a, G, s);
+        e = launch_d<64, 64>(a, G, st.rows, s);
     else
         return hipErrorInvalidValue;
     if (e != hipSuccess)
         return e;
-    return launch_combine(st.part, st.hq, a.splits, st.dv, st.out, s);
+    return launch_combine(st.part, st.hq, a.splits, st.dv, st.rows, st.out, s);
 }
 
 }  // namespace qsa

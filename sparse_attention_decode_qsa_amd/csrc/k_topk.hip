@@ -390,13 +390,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_lists_kernel(const float *__
 constexpr int kListBuildThreads = 512;
 constexpr int kListBuildMaxRows = 4 * ((kMaxBlocks / 4 + kListWgs - 1) / kListWgs) + 4;
 
+// Row r = blockIdx.y of the score array (stride ld) sees nb_r = (pos0 + r + 1) / 4
+// blocks; its lists go to cl.list + r * kListWgs * kListLen, cl.rows + r * kListWgs.
 __global__ __launch_bounds__(kListBuildThreads) void score_lists_kernel(
-    const float *__restrict__ scores, int32_t nb, CandLists cl)
+    const float *__restrict__ scores, int32_t ld, int32_t pos0, CandLists cl)
 {
     __shared__ uint64_t rk[kListBuildMaxRows];
     __shared__ uint32_t n_own;
     const int t = threadIdx.x;
     const int64_t nwg = gridDim.x, w = blockIdx.x;
+    const int32_t row = blockIdx.y;
+    const int32_t nb = (pos0 + row + 1) / kBlockTokens;
+    scores += (int64_t)row * ld;
+    cl.list += (int64_t)row * kListWgs * kListLen;
+    cl.rows += (int64_t)row * kListWgs;
     const int64_t runs = ((int64_t)nb + 3) / 4;
     const int64_t my_runs = runs > w ? (runs - w + nwg - 1) / nwg : 0;
     const int64_t n = min(my_runs * 4, (int64_t)kListBuildMaxRows);
@@ -474,13 +481,25 @@ hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_
         hipLaunchKernelGGL(iota_kernel, dim3(grid), dim3(kThreads), 0, s, blk, nb, n_sel);
         return hipGetLastError();
     }
-    const int32_t runs = (nb + 3) / 4;
-    const int32_t nwg = runs < kListWgs ? runs : kListWgs;
-    hipLaunchKernelGGL(score_lists_kernel, dim3(nwg), dim3(kListBuildThreads), 0, s, scores, nb, cl);
-    hipError_t e = hipGetLastError();
+    int32_t nwg = 0;
+    hipError_t e = launch_score_lists(scores, 1, nb, kBlockTokens * nb - 1, cl, &nwg, s);
     if (e != hipSuccess)
         return e;
     return launch_topk_lists(scores, nb, k, cl, nwg, blk, n_sel, s);
+}
+
+hipError_t launch_score_lists(const float *scores, int32_t rows, int32_t ld, int32_t pos0,
+                              CandLists cl, int32_t *n_lists, hipStream_t s)
+{
+    const int32_t nb_max = (pos0 + rows) / kBlockTokens;
+    if (rows < 1 || nb_max > kMaxBlocks)
+        return hipErrorInvalidValue;
+    const int32_t runs = (nb_max + 3) / 4;
+    const int32_t nwg = runs < 1 ? 1 : (runs < kListWgs ? runs : kListWgs);
+    hipLaunchKernelGGL(score_lists_kernel, dim3((uint32_t)nwg, (uint32_t)rows),
+                       dim3(kListBuildThreads), 0, s, scores, ld, pos0, cl);
+    *n_lists = nwg;
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,

@@ -109,13 +109,14 @@ Layout layout(const qsa_config *c, int32_t n_q, int32_t n_ctx)
         return o;
     };
     const int64_t nb = (int64_t)n_ctx / kBlockTokens + 1;
+    const size_t nd = (size_t)(n_q < kMaxDecodeRows ? n_q : kMaxDecodeRows);  // decode rows
     L.ld = (int64_t)round_up((size_t)nb, 64);
-    L.lists = take(sizeof(uint64_t) * (size_t)kListWgs * kListLen);
-    L.lrows = take(sizeof(uint32_t) * (size_t)kListWgs);
+    L.lists = take(sizeof(uint64_t) * nd * kListWgs * kListLen);
+    L.lrows = take(sizeof(uint32_t) * nd * kListWgs);
     L.scores = take(sizeof(float) * (size_t)n_q * (size_t)L.ld);
     L.blk = take(sizeof(int32_t) * (size_t)n_q * (size_t)c->topk_blocks);
     L.nsel = take(sizeof(int32_t) * (size_t)n_q);
-    L.part = take(sizeof(float) * (size_t)c->hq * (size_t)max_splits(c) * (size_t)(c->dv + 2));
+    L.part = take(sizeof(float) * nd * c->hq * (size_t)max_splits(c) * (size_t)(c->dv + 2));
     L.ksel = take(sizeof(uint16_t) * (size_t)max_cells(c) * c->hkv * c->d);
     L.vsel = take(sizeof(uint16_t) * (size_t)max_cells(c) * c->hkv * c->dv);
     L.total = off;
@@ -187,6 +188,137 @@ int attn_decode_launch(const qsa_config *c, AttnArgs a, int32_t cells, void *ws,
     a.part = at<float>(ws, L.part);
     HIP_CHECK(launch_attn(a, c->d, c->dv, s));
     return QSA_OK;
+}
+
+// One or more decode query rows (the tokens at n_before .. n_before + n_q - 1).
+int decode_impl(const char *fn, const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_before,
+                int32_t n_q, const uint16_t *q_idx, const uint16_t *k_idx_new, const uint16_t *q,
+                const uint16_t *k_new, const uint16_t *v_new, float *out, float *scores_out,
+                int32_t ld_scores, int32_t *blk_out, uint32_t flags, void *ws, size_t ws_bytes,
+                qsa_stream_t stream)
+{
+    int r = check_cfg(cfg);
+    if (r)
+        return r;
+    if (!Lb)
+        return fail(QSA_ERR_INVALID, "%s: layer buffers are NULL", fn);
+    if (n_before < 0)
+        return fail(QSA_ERR_INVALID, "%s: n_before=%d", fn, n_before);
+    if (n_q < 1 || n_q > kMaxDecodeRows)
+        return fail(QSA_ERR_INVALID, "%s: n_q=%d outside [1, %d]", fn, n_q, kMaxDecodeRows);
+    if ((int64_t)n_before + n_q > cfg->cap_tokens)
+        return fail(QSA_ERR_CAPACITY, "%s: position %d beyond cap_tokens %d", fn,
+                    n_before + n_q - 1, cfg->cap_tokens);
+    if (flags > QSA_STEP_COMPACT_GATHER)
+        return fail(QSA_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+    if (flags == QSA_STEP_COMPACT_GATHER && n_q != 1)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: the compact gather takes one query row", fn);
+    NEED_PTR(Lb->k_raw);
+    NEED_PTR(Lb->k_pool);
+    NEED_PTR(Lb->k_cache);
+    NEED_PTR(Lb->v_cache);
+    OPT_PTR(Lb->rms_w);
+    NEED_PTR(q_idx);
+    NEED_PTR(k_idx_new);
+    NEED_PTR(q);
+    NEED_PTR(k_new);
+    NEED_PTR(v_new);
+    NEED_PTR(out);
+    OPT_PTR(scores_out);
+    OPT_PTR(blk_out);
+    const int32_t N = n_before + n_q;  // tokens seen by the last row
+    const int32_t nb = N / kBlockTokens;
+    if (scores_out && n_q > 1 && ld_scores < nb)
+        return fail(QSA_ERR_INVALID, "%s: ld_scores %d < %d blocks", fn, ld_scores, nb);
+    if ((r = check_ws(cfg, ws, ws_bytes, n_q, N, fn)))
+        return r;
+    const Layout L = layout(cfg, n_q, N);
+    hipStream_t s = (hipStream_t)stream;
+
+    const int64_t row = (int64_t)cfg->h_idx * cfg->d_idx;
+    const int64_t kr = (int64_t)cfg->hkv * cfg->d, vr = (int64_t)cfg->hkv * cfg->dv;
+    const int32_t k = cfg->topk_blocks;
+
+    // 1. append: raw indexer rows, K rows, V rows, pooled row of the block completed
+    // (at most one for up to 4 new tokens)
+    AppendArgs ap;
+    memset(&ap, 0, sizeof(ap));
+    ap.seg[0] = CopySeg{k_idx_new, Lb->k_raw + n_before * row, n_q * row / 8};
+    ap.seg[1] = CopySeg{k_new, Lb->k_cache + n_before * kr, n_q * kr / 8};
+    ap.seg[2] = CopySeg{v_new, Lb->v_cache + n_before * vr, n_q * vr / 8};
+    ap.k_new = H(k_idx_new);
+    ap.n_before = n_before;
+    ap.k_raw = H(Lb->k_raw);
+    ap.k_pool = H(Lb->k_pool);
+    ap.rms_w = Lb->rms_w;
+    ap.H = cfg->h_idx;
+    ap.d = cfg->d_idx;
+    ap.b_lo = n_before / kBlockTokens;
+    ap.n_blocks = nb - ap.b_lo;
+    ap.eps = cfg->rms_eps;
+    ap.base = cfg->rope_base;
+
+    // 2. scores of every query row over the blocks complete before the call; the
+    // append runs in the same launch and scores the block it completes.  One row:
+    // every scan work group leaves its best kListLen candidates; several rows:
+    // the candidate lists are built from the score rows by a second launch
+    float *scores = scores_out ? scores_out : at<float>(ws, L.scores);
+    const int32_t ld = scores_out ? (n_q > 1 ? ld_scores : 0) : (int32_t)L.ld;
+    const CandLists cl = cand_lists(ws, L);
+    int32_t n_lists = 0;
+    if (n_q == 1) {
+        HIP_CHECK(launch_score_decode(H(q_idx), 1, H(Lb->k_pool), ap.b_lo, (int32_t)row, scores,
+                                      ld, &ap, &cl, &n_lists, s));
+    } else {
+        HIP_CHECK(launch_score_decode(H(q_idx), n_q, H(Lb->k_pool), ap.b_lo, (int32_t)row, scores,
+                                      ld, &ap, nullptr, nullptr, s));
+        HIP_CHECK(launch_score_lists(scores, n_q, ld, n_before, cl, &n_lists, s));
+    }
+
+    if (flags == QSA_STEP_FUSED_GATHER) {
+        // 3-5. top-k from the candidate lists and attention over the chosen
+        // cells (read straight from the caches) in one launch, then the combine
+        StepTail st;
+        st.cl = cl;
+        st.n_lists = n_lists;
+        st.scores = scores;
+        st.ld = ld;
+        st.pos0 = n_before;
+        st.rows = n_q;
+        st.k = k;
+        st.q = H(q);
+        st.k_cache = H(Lb->k_cache);
+        st.v_cache = H(Lb->v_cache);
+        st.hq = cfg->hq;
+        st.hkv = cfg->hkv;
+        st.d = cfg->d;
+        st.dv = cfg->dv;
+        st.scale = cfg->attn_scale;
+        st.part = at<float>(ws, L.part);
+        st.out = out;
+        st.blk_out = blk_out;
+        HIP_CHECK(launch_step_tail(st, s));
+        return QSA_OK;
+    }
+
+    // 3. top-k blocks (ascending ids) from the candidate lists
+    const int32_t nsel = nb < k ? nb : k;
+    const int32_t cells = kBlockTokens * nsel + N % kBlockTokens;
+    int32_t *blk = blk_out ? blk_out : at<int32_t>(ws, L.blk);
+    HIP_CHECK(launch_topk_lists(scores, nb, k, cl, n_lists, blk, at<int32_t>(ws, L.nsel), s));
+
+    // 4-5. compact gather, then attention over the compact rows
+    AttnArgs a = attn_base(cfg);
+    a.q = H(q);
+    a.out = out;
+    h16 *ks = at<h16>(ws, L.ksel), *vs = at<h16>(ws, L.vsel);
+    HIP_CHECK(launch_gather(blk, nsel, N, H(Lb->k_cache), H(Lb->v_cache), (int32_t)(kr / 8),
+                            (int32_t)(vr / 8), ks, vs, s));
+    a.kbase = ks;
+    a.vbase = vs;
+    a.mode = kCellsCompact;
+    a.n_cells = cells;
+    return attn_decode_launch(cfg, a, cells, ws, L, s);
 }
 
 }  // namespace
@@ -349,8 +481,8 @@ int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, i
     NEED_PTR(scores);
     const int32_t row = cfg->h_idx * cfg->d_idx;
     if (n_q == 1) {
-        HIP_CHECK(launch_score_decode(H(q_idx), H(k_pool), (pos0 + 1) / kBlockTokens, row, scores,
-                                      nullptr, nullptr, nullptr, (hipStream_t)stream));
+        HIP_CHECK(launch_score_decode(H(q_idx), 1, H(k_pool), (pos0 + 1) / kBlockTokens, row,
+                                      scores, 0, nullptr, nullptr, nullptr, (hipStream_t)stream));
         return QSA_OK;
     }
     if (ld % 4)
@@ -482,114 +614,19 @@ int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_b
                     int32_t *blk_out, uint32_t flags, void *ws, size_t ws_bytes,
                     qsa_stream_t stream)
 {
-    int r = check_cfg(cfg);
-    if (r)
-        return r;
-    if (!Lb)
-        return fail(QSA_ERR_INVALID, "qsa_decode_step: layer buffers are NULL");
-    if (n_before < 0)
-        return fail(QSA_ERR_INVALID, "qsa_decode_step: n_before=%d", n_before);
-    if ((int64_t)n_before + 1 > cfg->cap_tokens)
-        return fail(QSA_ERR_CAPACITY, "qsa_decode_step: position %d beyond cap_tokens %d",
-                    n_before, cfg->cap_tokens);
-    if (flags > QSA_STEP_COMPACT_GATHER)
-        return fail(QSA_ERR_INVALID, "qsa_decode_step: unknown flags 0x%x", flags);
-    NEED_PTR(Lb->k_raw);
-    NEED_PTR(Lb->k_pool);
-    NEED_PTR(Lb->k_cache);
-    NEED_PTR(Lb->v_cache);
-    OPT_PTR(Lb->rms_w);
-    NEED_PTR(q_idx);
-    NEED_PTR(k_idx_new);
-    NEED_PTR(q);
-    NEED_PTR(k_new);
-    NEED_PTR(v_new);
-    NEED_PTR(out);
-    OPT_PTR(scores_out);
-    OPT_PTR(blk_out);
-    const int32_t N = n_before + 1;
-    if ((r = check_ws(cfg, ws, ws_bytes, 1, N, __func__)))
-        return r;
-    const Layout L = layout(cfg, 1, N);
-    hipStream_t s = (hipStream_t)stream;
+    return decode_impl(__func__, cfg, Lb, n_before, 1, q_idx, k_idx_new, q, k_new, v_new, out,
+                       scores_out, 0, blk_out, flags, ws, ws_bytes, stream);
+}
 
-    const int64_t row = (int64_t)cfg->h_idx * cfg->d_idx;
-    const int64_t kr = (int64_t)cfg->hkv * cfg->d, vr = (int64_t)cfg->hkv * cfg->dv;
-    const int32_t nb = N / kBlockTokens;
-    const int32_t k = cfg->topk_blocks;
-    const int32_t nsel = nb < k ? nb : k;
-    const int32_t cells = kBlockTokens * nsel + N % kBlockTokens;
-
-    // 1. append: raw indexer row, K row, V row, pooled row of the block completed
-    AppendArgs ap;
-    memset(&ap, 0, sizeof(ap));
-    ap.seg[0] = CopySeg{k_idx_new, Lb->k_raw + n_before * row, row / 8};
-    ap.seg[1] = CopySeg{k_new, Lb->k_cache + n_before * kr, kr / 8};
-    ap.seg[2] = CopySeg{v_new, Lb->v_cache + n_before * vr, vr / 8};
-    ap.k_new = H(k_idx_new);
-    ap.n_before = n_before;
-    ap.k_raw = H(Lb->k_raw);
-    ap.k_pool = H(Lb->k_pool);
-    ap.rms_w = Lb->rms_w;
-    ap.H = cfg->h_idx;
-    ap.d = cfg->d_idx;
-    ap.b_lo = n_before / kBlockTokens;
-    ap.n_blocks = nb - ap.b_lo;
-    ap.eps = cfg->rms_eps;
-    ap.base = cfg->rope_base;
-
-    // 2. scores over the nb complete blocks; the append runs in the same launch
-    // and scores the block it completes; every scan work group leaves its
-    // best kListLen candidates
-    float *scores = scores_out ? scores_out : at<float>(ws, L.scores);
-    const CandLists cl = cand_lists(ws, L);
-    int32_t n_lists = 0;
-    HIP_CHECK(launch_score_decode(H(q_idx), H(Lb->k_pool), ap.b_lo, (int32_t)row, scores, &ap, &cl,
-                                  &n_lists, s));
-
-    if (flags == QSA_STEP_FUSED_GATHER) {
-        // 3-5. top-k from the candidate lists and attention over the chosen
-        // cells (read straight from the caches) in one launch, then the combine
-        StepTail st;
-        st.cl = cl;
-        st.n_lists = n_lists;
-        st.scores = scores;
-        st.n_tokens = N;
-        st.k = k;
-        st.q = H(q);
-        st.k_cache = H(Lb->k_cache);
-        st.v_cache = H(Lb->v_cache);
-        st.hq = cfg->hq;
-        st.hkv = cfg->hkv;
-        st.d = cfg->d;
-        st.dv = cfg->dv;
-        st.scale = cfg->attn_scale;
-        st.part = at<float>(ws, L.part);
-        st.out = out;
-        st.blk_out = blk_out;
-        st.n_sel = nullptr;
-        HIP_CHECK(launch_step_tail(st, s));
-        return QSA_OK;
-    }
-
-    // 3. top-k blocks (ascending ids) from the candidate lists
-    int32_t *blk = blk_out ? blk_out : at<int32_t>(ws, L.blk);
-    HIP_CHECK(launch_topk_lists(scores, nb, k, cl, n_lists, blk, at<int32_t>(ws, L.nsel), s));
-
-    // 4-5. compact gather, then attention over the compact rows
-    AttnArgs a = attn_base(cfg);
-    a.q = H(q);
-    a.out = out;
-    {
-        h16 *ks = at<h16>(ws, L.ksel), *vs = at<h16>(ws, L.vsel);
-        HIP_CHECK(launch_gather(blk, nsel, N, H(Lb->k_cache), H(Lb->v_cache), (int32_t)(kr / 8),
-                                (int32_t)(vr / 8), ks, vs, s));
-        a.kbase = ks;
-        a.vbase = vs;
-        a.mode = kCellsCompact;
-        a.n_cells = cells;
-    }
-    return attn_decode_launch(cfg, a, cells, ws, L, s);
+int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_before,
+                     int32_t n_q, const uint16_t *q_idx, const uint16_t *k_idx_new,
+                     const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, float *out,
+                     float *scores_out, int32_t ld_scores, int32_t *blk_out, void *ws,
+                     size_t ws_bytes, qsa_stream_t stream)
+{
+    return decode_impl(__func__, cfg, Lb, n_before, n_q, q_idx, k_idx_new, q, k_new, v_new, out,
+                       scores_out, ld_scores, blk_out, QSA_STEP_FUSED_GATHER, ws, ws_bytes,
+                       stream);
 }
 
 int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_before,

@@ -49,13 +49,15 @@ struct CandLists {
 };
 
 // ---- scores (k_score.hip) ---------------------------------------------------
-// Stand-alone scan (qsa_index_score, n_q = 1): scores[0, nb).
-// Decode-step scan (ap and cl non-NULL): the append work runs in the same launch
-// (at most one completed block, block nb; scores[nb] is then written too) and
-// every work group writes its candidate list; *n_lists gets the list count.
-hipError_t launch_score_decode(const h16 *q, const h16 *pool, int32_t nb, int32_t row_elems,
-                               float *scores, const AppendArgs *ap, const CandLists *cl,
-                               int32_t *n_lists, hipStream_t s);
+// Stand-alone scan (qsa_index_score, ap NULL, n_q = 1): scores[0, nb).
+// Decode-step scan (ap non-NULL): the append work runs in the same launch (at
+// most one completed block, block nb; its scores are written too); n_q queries
+// (rows of q) score every row read once, query i into scores[i * ld ..]; with
+// cl (n_q = 1 only) every work group also writes its candidate list and
+// *n_lists gets the list count.
+hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb,
+                               int32_t row_elems, float *scores, int32_t ld, const AppendArgs *ap,
+                               const CandLists *cl, int32_t *n_lists, hipStream_t s);
 hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h16 *pool,
                                 int32_t row_elems, float *scores, int32_t ld, hipStream_t s);
 
@@ -64,6 +66,11 @@ hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h
 // selection.  Keeps no state between calls.
 hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_t *blk,
                               int32_t *n_sel, CandLists cl, hipStream_t s);
+// Candidate lists of `rows` score rows (stride ld; row r sees (pos0 + r + 1) / 4
+// blocks), laid out as the decode scan lays them out, row r's at
+// cl.list + r * kListWgs * kListLen; *n_lists gets the lists per row.
+hipError_t launch_score_lists(const float *scores, int32_t rows, int32_t ld, int32_t pos0,
+                              CandLists cl, int32_t *n_lists, hipStream_t s);
 // Top-k of one row from the scan's candidate lists (n_lists of them); selects
 // from the whole score row when the lists cannot be shown to hold the top-k.
 hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,
@@ -108,29 +115,31 @@ struct AttnArgs {
     int32_t tok_bound;      // list: tokens must be < tok_bound (the mask length)
 };
 hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s);
-// Merge of split-K partials [hq][splits][dv + 2] into out [hq][dv].
-hipError_t launch_combine(const float *part, int32_t hq, int32_t splits, int32_t dv, float *out,
-                          hipStream_t s);
+// Merge of split-K partials [rows][hq][splits][dv + 2] into out [rows][hq][dv].
+hipError_t launch_combine(const float *part, int32_t hq, int32_t splits, int32_t dv, int32_t rows,
+                          float *out, hipStream_t s);
 
 // ---- decode-step tail (k_step.hip) -----------------------------------------
 // Top-k from the scan's candidate lists and attention over the chosen cells in
 // one launch, then the combine.
 constexpr int kMaxTopk = 1024;
+constexpr int kMaxDecodeRows = 4;  // query rows of one multi-query decode step
 struct StepTail {
-    CandLists cl;
+    CandLists cl;         // row r's lists at r * kListWgs * kListLen (rows at r * kListWgs)
     int32_t n_lists;
-    const float *scores;  // the score row (used when the lists are not enough)
-    int32_t n_tokens;     // context after the append
+    const float *scores;  // [rows][ld] score rows (used when the lists are not enough)
+    int32_t ld;
+    int32_t pos0;         // row r is the token at position pos0 + r
+    int32_t rows;
     int32_t k;
-    const h16 *q;
+    const h16 *q;         // [rows][hq][d]
     const h16 *k_cache;
     const h16 *v_cache;
     int32_t hq, hkv, d, dv;
     float scale;
-    float *part;          // [hq][splits][dv + 2]
-    float *out;           // [hq][dv]
-    int32_t *blk_out;     // optional: chosen ids, ascending
-    int32_t *n_sel;       // optional
+    float *part;          // [rows][hq][splits][dv + 2]
+    float *out;           // [rows][hq][dv]
+    int32_t *blk_out;     // optional: [rows][k] chosen ids, ascending
 };
 hipError_t launch_step_tail(const StepTail &st, hipStream_t s);
 

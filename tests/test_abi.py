@@ -141,6 +141,15 @@ def test_entry_points_reject_bad_arguments_on_the_host(lib):
     assert lib.qsa_decode_step(cp, C.byref(b), 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                None, 0, FAKE, 16, None) == qb.QSA_ERR_CAPACITY
     assert b"workspace" in lib.qsa_last_error()
+    # multi-query decode: n_q outside [1, 4], rows past capacity, ld_scores too small
+    assert lib.qsa_decode_multi(cp, C.byref(b), 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                0, None, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_decode_multi(cp, C.byref(b), 10, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                0, None, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_decode_multi(cp, C.byref(b), 4094, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                None, 0, None, FAKE, 1 << 30, None) == qb.QSA_ERR_CAPACITY
+    assert lib.qsa_decode_multi(cp, C.byref(b), 1000, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, 200, None, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
 
 
 def test_mla_preconditions(lib):

@@ -410,3 +410,74 @@ def test_decode_step_clustered_scores(gpu, pattern):
     assert np.array_equal(b_gpu, ref["blk"])
     ref_out = O.attn_cells(q, K, V, O.cells(b_gpu, n_before + 1), w.scale)
     assert_attn_close(host(out), ref_out)
+
+
+# ------------------------------------------------------------------ f3 multi-query decode
+@pytest.mark.parametrize("n_tokens,n_q", [(4 * 3000 + 1, 3), (4 * 3000 + 3, 3), (4 * 3000, 2),
+                                          (4 * 3000 + 2, 4), (2049, 3), (6, 4)])
+def test_decode_multi_equals_sequential_steps(gpu, n_tokens, n_q):
+    # n_q rows appended and attended in one call; row r against the oracle's decode
+    # step at position n_before + r (n_q oracle steps in order on the same caches)
+    w = small(n_tokens)
+    L, cfg, g, o = setup_decode(w)
+    n0 = L["n_prefix"]
+    r = np.random.default_rng(n_tokens * 10 + n_q)
+    q_idx = synth.normal_f16(80, (n_q, 16, 128))
+    q = synth.normal_f16(81, (n_q, 32, 128))
+    k_idx_new = synth.normal_f16(82, (n_q, 16, 128))
+    k_new = synth.normal_f16(83, (n_q, 4, 128))
+    v_new = synth.normal_f16(84, (n_q, 4, 128))
+    nb_last = (n0 + n_q) // 4
+    ld = nb_last + 5
+    out = torch.empty((n_q, 32, 128), device="cuda")
+    scores = torch.full((n_q, ld), 123.0, device="cuda")
+    blk = torch.full((n_q, w.topk), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, n_q, w.cap_tokens)
+    qb.qsa_decode_multi(cfg, g, n0, dev(q_idx), dev(k_idx_new), dev(q), dev(k_new), dev(v_new),
+                        out, ws, scores_out=scores, ld_scores=ld, blk_out=blk)
+    s_all, b_all, o_all = host(scores), host(blk), host(out)
+    for row in range(n_q):
+        ref = O.decode_step(shape_of(w), o.raw, o.pooled, o.k, o.v, n0 + row, q_idx[row],
+                            k_idx_new[row], q[row], k_new[row], v_new[row])
+        nb = (n0 + row + 1) // 4
+        s_gpu = s_all[row][:nb]
+        if nb:
+            assert np.max(np.abs(s_gpu - ref["scores64"])) <= \
+                SCORE_REL * np.max(np.abs(ref["scores64"]))
+        nsel = min(w.topk, nb)
+        b_gpu = b_all[row][:nsel]
+        assert np.array_equal(b_gpu, O.topk_sort(s_gpu, w.topk))
+        ref_out = O.attn_cells(q[row], o.k, o.v, O.cells(b_gpu, n0 + row + 1), w.scale)
+        assert_attn_close(o_all[row], ref_out)
+    # the caches hold all n_q new tokens, pooled rows included
+    nb = (n0 + n_q) // 4
+    assert_pool_close(host(g.k_pool[:nb]), o.pooled[:nb])
+    assert np.array_equal(host(g.k_raw[n0:n0 + n_q]).view(np.uint16), k_idx_new.view(np.uint16))
+
+
+def test_decode_multi_255181_planted(gpu):
+    # the 256k workload with three rows: every row finds the planted blocks
+    w = synth.WORKLOADS["decode_255181"]
+    L, cfg, g, o = setup_decode(w)
+    n0 = L["n_prefix"]
+    n_q = 3
+    q_idx = np.stack([L["q_idx"]] * n_q)
+    q = np.stack([L["q"]] * n_q)
+    out = torch.empty((n_q, 32, 128), device="cuda")
+    blk = torch.full((n_q, w.topk), -1, dtype=torch.int32, device="cuda")
+    ld = (n0 + n_q) // 4 + 1
+    scores = torch.empty((n_q, ld), device="cuda")
+    ws = qb.workspace(cfg, n_q, w.cap_tokens)
+    qb.qsa_decode_multi(cfg, g, n0, dev(q_idx), dev(L["k_idx_new"][:n_q]), dev(q),
+                        dev(L["k_new"][:n_q]), dev(L["v_new"][:n_q]), out, ws, scores_out=scores,
+                        ld_scores=ld, blk_out=blk)
+    for row in range(n_q):
+        ref = O.decode_step(shape_of(w), o.raw, o.pooled, o.k, o.v, n0 + row, q_idx[row],
+                            L["k_idx_new"][row], q[row], L["k_new"][row], L["v_new"][row])
+        nb = (n0 + row + 1) // 4
+        s_gpu = host(scores[row])[:nb]
+        b_gpu = host(blk[row])
+        assert np.array_equal(b_gpu, O.topk_sort(s_gpu, w.topk))
+        assert set(L["planted"].tolist()) <= set(b_gpu.tolist())
+        ref_out = O.attn_cells(q[row], o.k, o.v, O.cells(b_gpu, n0 + row + 1), w.scale)
+        assert_attn_close(host(out[row]), ref_out)
