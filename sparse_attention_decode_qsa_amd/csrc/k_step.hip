@@ -28,6 +28,7 @@ namespace qsa {
 namespace {
 
 constexpr int kNT = kSelThreads;  // 16 waves
+constexpr int kMaxChunks = 4;      // 64-cell chunks per split
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct TailArgs {
@@ -42,7 +43,8 @@ struct TailArgs {
     const h16 *vc;        // [N][hkv][DV]
     int32_t hq, hkv;
     float scale;
-    int32_t splits;       // ceil(cells / 64) of the row with the most cells
+    int32_t chunks;       // 64-cell chunks per split
+    int32_t splits;       // ceil(cells / (64 chunks)) of the row with the most cells
     float *part;          // [rows][hq][splits][DV + 2]
     int32_t *blk_out;     // optional, [rows][k]
 };
@@ -57,13 +59,13 @@ struct alignas(16) TailLds {
         struct {
             alignas(16) h16 vs[kAttnChunk * DV];
             alignas(16) float ps[G][kAttnChunk];
-            float ml[G][2];
+            float ml[G][3];  // running max, running sum, rescale of the last chunk
         } att;
     } u;
     ListSelLds L;
     alignas(16) h16 qs[G * D];
     alignas(16) int32_t ids[kMaxTopk];
-    alignas(16) int32_t toks[kAttnChunk];
+    alignas(16) int32_t toks[kMaxChunks * kAttnChunk];
     uint32_t wsum[kNT / kWave];
 };
 
@@ -96,7 +98,9 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
     const int32_t nsel = nb < a.k ? nb : a.k;
     const int32_t cells = kBlockTokens * nsel + (N - kBlockTokens * nb);
     float *part = a.part + (int64_t)row * a.hq * a.splits * (DV + 2);
-    if (split * kAttnChunk >= cells) {
+    const int chunks = a.chunks;
+    const int32_t c_lo = split * chunks * kAttnChunk;  // this split's cells
+    if (c_lo >= cells) {
         // past this row's cells (rows of one call differ by up to 3): a partial
         // that the combine weighs 0
         for (int o = t; o < G * (DV + 2); o += kNT) {
@@ -109,18 +113,17 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
     CandLists cl = a.cl;
     cl.list += (int64_t)row * kListWgs * kListLen;
     cl.rows += (int64_t)row * kListWgs;
-    const int32_t c_lo = split * kAttnChunk;       // this split's cells
-    const int32_t b_lo = c_lo / kBlockTokens;      // its chosen-block positions
-    const int32_t b_hi = b_lo + kAttnChunk / kBlockTokens;
+    const int32_t b_lo = c_lo / kBlockTokens;  // its chosen-block positions
+    const int32_t b_hi = b_lo + chunks * kAttnChunk / kBlockTokens;
 
     // the query rows of this KV head (independent of the selection)
     const h16 *qrow = a.q + ((int64_t)row * a.hq + (int64_t)g * G) * D;
     for (int i = t; i < G * D / 8; i += kNT)
         ((h16x8 *)sm.qs)[i] = ((const h16x8 *)qrow)[i];
     // the split's tail cells (the incomplete block, after the chosen ones)
-    if (t < kAttnChunk) {
-        const int32_t c = c_lo + t;
-        sm.toks[t] = (c >= kBlockTokens * nsel && c < cells)
+    for (int i = t; i < chunks * kAttnChunk; i += kNT) {
+        const int32_t c = c_lo + i;
+        sm.toks[i] = (c >= kBlockTokens * nsel && c < cells)
                          ? kBlockTokens * nb + (c - kBlockTokens * nsel)
                          : -1;
     }
@@ -195,71 +198,101 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
         __syncthreads();  // the bitmap shares LDS with the attention arrays
     }
 
-    // ---- 2. attention over the split's 64 cells for KV head g
+    // ---- 2. attention over the split's chunks of 64 cells for KV head g, with
+    // an online softmax across chunks (running max and sum per head in LDS,
+    // kept by wave h; the output of (head, dim) in a register of its thread)
+    constexpr int OPT = (G * DV + kNT - 1) / kNT;  // outputs per thread
     const int64_t k_tok = (int64_t)a.hkv * D, v_tok = (int64_t)a.hkv * DV;
-    // K: thread (cell, piece); V: thread (cell, piece); both loads in flight
     const int kc = t / PK, kp = t % PK;
     const int vc = t / PV, vp = t % PV;
     const bool k_on = kc < kAttnChunk, v_on = vc < kAttnChunk;
-    const int32_t ktok = k_on ? sm.toks[kc] : -1;
-    const int32_t vtok = v_on ? sm.toks[vc] : -1;
-    h16x8 kv = h16x8{0, 0, 0, 0, 0, 0, 0, 0}, vv = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (ktok >= 0)
-        kv = *(const h16x8 *)(a.kc + (int64_t)ktok * k_tok + (int64_t)g * D + kp * 8);
-    if (vtok >= 0)
-        vv = *(const h16x8 *)(a.vc + (int64_t)vtok * v_tok + (int64_t)g * DV + vp * 8);
     const float sl2 = a.scale * kLog2e;
-    {
-        float acc[G];
+    float oacc[OPT];
 #pragma unroll
-        for (int h = 0; h < G; h++)
-            acc[h] = dot8(*(const h16x8 *)&sm.qs[h * D + kp * 8], kv, 0.f);
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            acc[h] = row_group_sum<PK>(acc[h]);
-        if (k_on && kp == 0) {
+    for (int i = 0; i < OPT; i++)
+        oacc[i] = 0.f;
+    if (wave < G && lane == 0) {
+        sm.u.att.ml[wave][0] = -INFINITY;
+        sm.u.att.ml[wave][1] = 0.f;
+    }
+    for (int ch = 0; ch < chunks; ch++) {
+        // K: thread (cell, piece); V: thread (cell, piece); both loads in flight
+        const int32_t ktok = k_on ? sm.toks[ch * kAttnChunk + kc] : -1;
+        const int32_t vtok = v_on ? sm.toks[ch * kAttnChunk + vc] : -1;
+        h16x8 kv = h16x8{0, 0, 0, 0, 0, 0, 0, 0}, vv = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (ktok >= 0)
+            kv = *(const h16x8 *)(a.kc + (int64_t)ktok * k_tok + (int64_t)g * D + kp * 8);
+        if (vtok >= 0)
+            vv = *(const h16x8 *)(a.vc + (int64_t)vtok * v_tok + (int64_t)g * DV + vp * 8);
+        {
+            float acc[G];
 #pragma unroll
             for (int h = 0; h < G; h++)
-                sm.u.att.ps[h][kc] = ktok >= 0 ? acc[h] * sl2 : -INFINITY;
-        }
-    }
-    if (v_on)
-        *(h16x8 *)&sm.u.att.vs[vc * DV + vp * 8] = vv;
-    __syncthreads();
-
-    // softmax of head `wave` over the 64 cells (lane = cell); every split has
-    // at least one cell, so the maximum is finite
-    if (wave < G) {
-        const float s = sm.u.att.ps[wave][lane];
-        const float m = wave_max(s);
-        const float p = (s == -INFINITY) ? 0.f : exp2f(s - m);
-        sm.u.att.ps[wave][lane] = p;
-        const float l = wave_sum(p);
-        if (lane == 0) {
-            sm.u.att.ml[wave][0] = m;
-            sm.u.att.ml[wave][1] = l;
-        }
-    }
-    __syncthreads();
-
-    // thread (head, dim): o = sum over cells of p x v; cells past the end have
-    // p = 0 and zeroed V rows
-    for (int o = t; o < G * DV; o += kNT) {
-        const int h = o / DV, d = o % DV;
-        float acc = 0.f;
-#pragma unroll 4
-        for (int c4 = 0; c4 < kAttnChunk; c4 += 4) {
-            const f32x4 p4 = *(const f32x4 *)&sm.u.att.ps[h][c4];
+                acc[h] = dot8(*(const h16x8 *)&sm.qs[h * D + kp * 8], kv, 0.f);
 #pragma unroll
-            for (int u = 0; u < 4; u++)
-                acc += p4[u] * (float)sm.u.att.vs[(c4 + u) * DV + d];
+            for (int h = 0; h < G; h++)
+                acc[h] = row_group_sum<PK>(acc[h]);
+            if (k_on && kp == 0) {
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    sm.u.att.ps[h][kc] = ktok >= 0 ? acc[h] * sl2 : -INFINITY;
+            }
         }
-        float *pb = part + (((int64_t)g * G + h) * a.splits + split) * (DV + 2);
-        if (d == 0) {
-            pb[0] = sm.u.att.ml[h][0];
-            pb[1] = sm.u.att.ml[h][1];
+        if (v_on)
+            *(h16x8 *)&sm.u.att.vs[vc * DV + vp * 8] = vv;
+        __syncthreads();
+
+        // softmax of head `wave` over the chunk (lane = cell).  The first chunk of
+        // a split always holds a cell, so the running maximum is finite from then on
+        if (wave < G) {
+            const float s = sm.u.att.ps[wave][lane];
+            const float m_old = sm.u.att.ml[wave][0];
+            const float m = fmaxf(m_old, wave_max(s));
+            const float alpha = exp2f(m_old - m);  // 0 for the first chunk
+            const float p = (s == -INFINITY) ? 0.f : exp2f(s - m);
+            sm.u.att.ps[wave][lane] = p;
+            const float l = sm.u.att.ml[wave][1] * alpha + wave_sum(p);
+            if (lane == 0) {
+                sm.u.att.ml[wave][0] = m;
+                sm.u.att.ml[wave][1] = l;
+                sm.u.att.ml[wave][2] = alpha;
+            }
         }
-        pb[2 + d] = acc;
+        __syncthreads();
+
+        // thread (head, dim): o = o * alpha + sum over cells of p x v; cells past
+        // the end have p = 0 and zeroed V rows
+#pragma unroll
+        for (int i = 0; i < OPT; i++) {
+            const int o = t + i * kNT;
+            if (o < G * DV) {
+                const int h = o / DV, d = o % DV;
+                float acc = oacc[i] * sm.u.att.ml[h][2];
+#pragma unroll 4
+                for (int c4 = 0; c4 < kAttnChunk; c4 += 4) {
+                    const f32x4 p4 = *(const f32x4 *)&sm.u.att.ps[h][c4];
+#pragma unroll
+                    for (int u = 0; u < 4; u++)
+                        acc += p4[u] * (float)sm.u.att.vs[(c4 + u) * DV + d];
+                }
+                oacc[i] = acc;
+            }
+        }
+        if (ch + 1 < chunks)
+            __syncthreads();  // the next chunk overwrites ps and vs
+    }
+#pragma unroll
+    for (int i = 0; i < OPT; i++) {
+        const int o = t + i * kNT;
+        if (o < G * DV) {
+            const int h = o / DV, d = o % DV;
+            float *pb = part + (((int64_t)g * G + h) * a.splits + split) * (DV + 2);
+            if (d == 0) {
+                pb[0] = sm.u.att.ml[h][0];
+                pb[1] = sm.u.att.ml[h][1];
+            }
+            pb[2 + d] = oacc[i];
+        }
     }
 }
 
@@ -306,7 +339,13 @@ hipError_t launch_step_tail(const StepTail &st, hipStream_t s)
         const int32_t c = kBlockTokens * (nb < st.k ? nb : st.k) + n % kBlockTokens;
         max_cells = c > max_cells ? c : max_cells;
     }
-    a.splits = (max_cells + kAttnChunk - 1) / kAttnChunk;
+    // one 64-cell chunk per split, unless that would take more than one round of
+    // work groups (one per CU, 256 CUs): then longer splits
+    const int32_t n_chunks = (max_cells + kAttnChunk - 1) / kAttnChunk;
+    const int64_t wgs = (int64_t)n_chunks * st.hkv * st.rows;
+    a.chunks = (int32_t)((wgs + 255) / 256);
+    a.chunks = a.chunks < 1 ? 1 : (a.chunks > kMaxChunks ? kMaxChunks : a.chunks);
+    a.splits = (n_chunks + a.chunks - 1) / a.chunks;
     if (a.splits > kAttnMaxSplits)
         return hipErrorInvalidValue;
     a.part = st.part;

@@ -481,3 +481,48 @@ def test_decode_multi_255181_planted(gpu):
         assert set(L["planted"].tolist()) <= set(b_gpu.tolist())
         ref_out = O.attn_cells(q[row], o.k, o.v, O.cells(b_gpu, n0 + row + 1), w.scale)
         assert_attn_close(host(out[row]), ref_out)
+
+
+def test_decode_step_at_maximum_capacity(gpu):
+    # the largest context the library takes (cap_tokens <= 2^21): 524,270 complete
+    # blocks and a tail of 3; sampled pooled rows, every score, the top-k and the
+    # output against the oracle
+    n_tokens = 4 * 524270 + 3
+    w = small(n_tokens)
+    assert w.cap_tokens <= 1 << 21
+    cfg = cfg_of(w)
+    n0 = n_tokens - 1
+    raw = synth.normal_f16(90, (n0, 16, 128))
+    K = synth.normal_f16(91, (n_tokens, 4, 128))
+    V = synth.normal_f16(92, (n_tokens, 4, 128))
+    q_idx = synth.normal_f16(93, (16, 128))
+    q = synth.normal_f16(94, (32, 128))
+    k_idx_new = synth.normal_f16(95, (16, 128))
+    g = qb.Layer(cfg)
+    qb.qsa_pool_append(cfg, dev(raw), 0, g.k_raw, g.k_pool)
+    g.k_cache[:n0] = dev(K[:n0])
+    g.v_cache[:n0] = dev(V[:n0])
+    nb = n_tokens // 4
+    out = torch.empty((32, 128), device="cuda")
+    scores = torch.empty(nb, device="cuda")
+    blk = torch.full((512,), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, 1, w.cap_tokens)
+    qb.qsa_decode_step(cfg, g, n0, dev(q_idx), dev(k_idx_new), dev(q), dev(K[n0]), dev(V[n0]),
+                       out, ws, scores_out=scores, blk_out=blk)
+    # pooled rows: the last blocks and a seeded sample, against the oracle's pooling
+    rows = np.unique(np.concatenate([np.arange(nb - 4, nb),
+                                     np.random.default_rng(9).choice(nb, 300, replace=False)]))
+    got = host(g.k_pool[torch.from_numpy(rows).cuda()])
+    ref = np.stack([O.pool_block(raw[4 * b:4 * b + 4], O.block_pos(b)) for b in rows])
+    assert_pool_close(got, ref)
+    # scores against the oracle's scan of the GPU's own pooled rows
+    P = host(g.k_pool[:nb])
+    s64, _ = O.index_score(q_idx, P, nb)
+    bound = SCORE_ABS_REL * (np.abs(P.astype(np.float64).reshape(nb, -1)) @
+                             np.abs(q_idx.astype(np.float64).ravel()))
+    s_gpu = host(scores)
+    assert np.all(np.abs(s_gpu - s64) <= bound)
+    b_gpu = host(blk)
+    assert np.array_equal(b_gpu, O.topk_sort(s_gpu, 512))
+    ref_out = O.attn_cells(q, K, V, O.cells(b_gpu, n_tokens), w.scale)
+    assert_attn_close(host(out), ref_out)
