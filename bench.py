@@ -19,7 +19,11 @@ Reported:
 
 Other workloads (one JSON line each, same keys): prefill_1024_at_126253 (prefill
 chunk tokens/s; roofline = MFMA scoring against the f16 dense peak, plus the
-attention's K/V GB/s) and mla_list_262144 (list-attention calls/s, latency-bound).
+attention's K/V GB/s for the per-row form and the bytes / MFMA rate of the
+grouped-union form; --per-row makes the step use the per-row form),
+prefill_1024_at_126253_corr (the same caches with indexer queries correlated from
+row to row, so that nearby rows choose overlapping blocks) and mla_list_262144
+(list-attention calls/s, latency-bound).
 """
 from __future__ import annotations
 
@@ -344,9 +348,11 @@ def bench_prefill(args):
     ws = qb.workspace(cfg, n_q, depth + n_q, dev)
     stream = torch.cuda.Stream()
 
+    flags = qb.QSA_PREFILL_PER_ROW if args.per_row else qb.QSA_PREFILL_GROUPED_UNION
+
     def step():
         qb.qsa_prefill_step(cfg, g, depth, q_idx, raw_new, q, k_new, v_new, out, ws,
-                            scores_out=scores, ld_scores=ld, blk_out=blk)
+                            scores_out=scores, ld_scores=ld, blk_out=blk, flags=flags)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -358,28 +364,63 @@ def bench_prefill(args):
                                                          ld=ld), args.steps)
     topk_us = _timed(stream, lambda: qb.qsa_topk_blocks(cfg, scores, n_q, ld, depth, blk, nsel,
                                                         ws), args.steps)
-    attn_us = _timed(stream, lambda: qb.qsa_prefill_attn(cfg, q, depth, blk, w.topk, g.k_cache,
-                                                         g.v_cache, out, ws), args.steps)
+    attn_row_us = _timed(stream, lambda: qb.qsa_prefill_attn(
+        cfg, q, depth, blk, w.topk, g.k_cache, g.v_cache, out, ws), args.steps)
+    attn_union_us = _timed(stream, lambda: qb.qsa_prefill_attn(
+        cfg, q, depth, blk, w.topk, g.k_cache, g.v_cache, out, ws,
+        flags=qb.QSA_PREFILL_GROUPED_UNION), args.steps)
+    attn_us = attn_row_us if args.per_row else attn_union_us
     nbs = [(depth + r + 1) // 4 for r in range(n_q)]
     flop = 2.0 * w.h_idx * w.d_idx * float(sum(nbs))
     cells = [4 * min(w.topk, nb) + (depth + r + 1) % 4 for r, nb in enumerate(nbs)]
     kv_bytes = float(sum(cells)) * w.hkv * (w.d + w.dv) * 2
     tflops = flop / (score_us * 1e-6) / 1e12
+    # the union form: blocks per group of 128 / (hq / hkv) rows, K/V bytes it streams
+    # (each union block and the tail span once per group) and the MFMA work it does
+    # (128 queries x every streamed cell, QK^T and PV, per KV head)
+    G = 128 // (w.hq // w.hkv)
+    b_host = blk.cpu().numpy()
+    ublocks, ucells = [], 0
+    for r0 in range(0, n_q, G):
+        r1 = min(n_q, r0 + G)
+        ids = np.unique(np.concatenate([b_host[r, :min(w.topk, nbs[r])] for r in range(r0, r1)]))
+        t0c = 4 * nbs[r0]
+        t1c = depth + r1
+        tail_blocks = (t1c - 1) // 4 - t0c // 4 + 1 if t1c > t0c else 0
+        ublocks.append(ids.size)
+        ucells += 4 * (ids.size + tail_blocks)
+    u_bytes = float(ucells) * w.hkv * (w.d + w.dv) * 2
+    u_flop = 2.0 * 2.0 * 128 * float(ucells) * w.d * w.hkv
     res = _contract(
         "QSA prefill chunk tokens/s (1024 queries at depth 126,253)", n_q / (step_us * 1e-6),
         "tokens/s", args.steps, args.warmup, step_us / 1e3, "f16",
         {"workload": w.name, "depth": depth, "n_q": n_q, "indexer": f"{w.h_idx}x{w.d_idx}",
-         "topk_blocks": w.topk, "attention": f"{w.hq}/{w.hkv}x{w.d}", "launch": "eager"},
+         "topk_blocks": w.topk, "attention": f"{w.hq}/{w.hkv}x{w.d}", "launch": "eager",
+         "indexer_query_rows": (f"AR(1) over rows, rho {w.q_corr}" if w.q_corr
+                                else "independent"),
+         "attention_form": "per-row" if args.per_row else "grouped union"},
         {"bound": "mfma", "kernel": "score_prefill_kernel", "achieved": round(tflops, 2),
          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
          "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
          "algorithmic_flop_per_launch": flop, "avg_launch_us": round(score_us, 2)})
     res["stages_us"] = {"step": round(step_us, 2), "score": round(score_us, 2),
-                        "topk": round(topk_us, 2), "attn": round(attn_us, 2)}
-    res["attention_hbm"] = {"bound": "hbm", "algorithmic_bytes": kv_bytes,
-                            "achieved": round(kv_bytes / (attn_us * 1e-6) / 1e9, 1),
+                        "topk": round(topk_us, 2), "attn": round(attn_us, 2),
+                        "attn_per_row": round(attn_row_us, 2),
+                        "attn_grouped_union": round(attn_union_us, 2)}
+    res["attention_hbm"] = {"form": "per-row", "bound": "hbm", "algorithmic_bytes": kv_bytes,
+                            "achieved": round(kv_bytes / (attn_row_us * 1e-6) / 1e9, 1),
                             "unit": "GB/s", "peak": HBM_PEAK_GBPS,
-                            "frac": round(kv_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+                            "frac": round(kv_bytes / (attn_row_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                          4)}
+    res["attention_union"] = {
+        "form": "grouped union", "rows_per_group": G,
+        "union_blocks_per_group": round(float(np.mean(ublocks)), 1),
+        "union_over_k": round(float(np.mean(ublocks)) / w.topk, 3),
+        "kv_bytes_streamed": u_bytes,
+        "hbm_achieved_gbps": round(u_bytes / (attn_union_us * 1e-6) / 1e9, 1),
+        "mfma_flop": u_flop,
+        "mfma_achieved_tflops": round(u_flop / (attn_union_us * 1e-6) / 1e12, 2),
+        "mfma_frac": round(u_flop / (attn_union_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(w, I, args.cpu_budget)
     return res
@@ -477,13 +518,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_255181",
                     choices=["decode_255181", "decode_61789", "tiny_decode_4k",
-                             "prefill_1024_at_126253", "mla_list_262144"])
+                             "prefill_1024_at_126253", "prefill_1024_at_126253_corr",
+                             "mla_list_262144"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
     ap.add_argument("--eager", action="store_true", help="launch per call instead of graphs")
     ap.add_argument("--compact-gather", action="store_true")
     ap.add_argument("--rows", type=int, default=1, choices=[1, 2, 3, 4],
                     help="query rows per layer step (> 1: speculative-draft verification "
                          "steps, qsa_decode_multi)")
+    ap.add_argument("--per-row", action="store_true",
+                    help="prefill: per-row attention instead of the grouped-union form")
     ap.add_argument("--kernel-reps", type=int, default=240)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)

@@ -61,6 +61,12 @@ extern "C" {
 #define QSA_STEP_COMPACT_GATHER 1u  /* copy chosen K/V to a compact buffer first, then
                                        attend over it (the COMMON-005 arrangement) */
 
+/* Prefill flags. */
+#define QSA_PREFILL_PER_ROW 0u        /* each row's attention reads its own cells */
+#define QSA_PREFILL_GROUPED_UNION 1u  /* groups of 128 / (hq/hkv) consecutive rows read the
+                                         union of their chosen blocks once (see
+                                         qsa_prefill_attn) */
+
 /* A hipStream_t; NULL is the null stream. */
 typedef void *qsa_stream_t;
 
@@ -193,14 +199,25 @@ int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint16_t *k_
 
 /*
  * Attention of a chunk of n_q query rows (row r at position pos0 + r), each over
- * its own cells: the blocks blk[r*ldb .. + n_sel_r) (n_sel_r = min(k, nb_r)) and its
- * tail, read directly from the caches.  The caches must already hold every token
- * up to pos0 + n_q - 1.
+ * its own cells: the blocks blk[r*ldb .. + n_sel_r) (n_sel_r = min(k, nb_r), each
+ * row's ids ascending and distinct) and its tail, read directly from the caches.
+ * The caches must already hold every token up to pos0 + n_q - 1.
+ * flags: QSA_PREFILL_PER_ROW (one pass per row; ws may be NULL) or
+ * QSA_PREFILL_GROUPED_UNION (the pages' "QSA grouped-union" prompt-processing
+ * switch, Qiita part 10, opening paragraphs and the union ON/OFF table of
+ * 「Vulkan版のプロファイリングでTGが遅くなった原因を調べる」; its steps are not given,
+ * and the reading here keeps the result: groups of 128 / (hq/hkv) consecutive rows
+ * stream the union of their chosen blocks and their tails once, on the matrix
+ * cores, with a per-row mask so that every row attends to exactly its own cells;
+ * the output equals the per-row form up to fp32 summation order and binary16
+ * rounding of the softmax weights).  The union form needs hq/hkv in {4, 8, 16},
+ * d = dv = 128 and (128 / (hq/hkv)) * topk_blocks <= 16384 (else
+ * QSA_ERR_UNSUPPORTED) and a workspace of qsa_workspace_size(cfg, n_q, pos0 + n_q).
  */
 int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int32_t pos0,
                      const int32_t *blk, int32_t ldb, const uint16_t *k_cache,
-                     const uint16_t *v_cache, float *out, void *ws, size_t ws_bytes,
-                     qsa_stream_t stream);
+                     const uint16_t *v_cache, float *out, uint32_t flags, void *ws,
+                     size_t ws_bytes, qsa_stream_t stream);
 
 /*
  * One decode step of one layer: steps 1-5 above for the token at position
@@ -248,12 +265,13 @@ int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_b
  * steps 2-5 causally (row r sees N_r = n_before + r + 1 tokens).
  * q_idx [n_new][h_idx][d_idx], q [n_new][hq][d], out [n_new][hq][dv].
  * Optional outputs: scores_out [n_new][ld_scores], blk_out [n_new][k].
+ * flags: QSA_PREFILL_PER_ROW or QSA_PREFILL_GROUPED_UNION, as for qsa_prefill_attn.
  */
 int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
                      int32_t n_new, const uint16_t *q_idx, const uint16_t *k_idx_new,
                      const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, float *out,
-                     float *scores_out, int32_t ld_scores, int32_t *blk_out, void *ws,
-                     size_t ws_bytes, qsa_stream_t stream);
+                     float *scores_out, int32_t ld_scores, int32_t *blk_out, uint32_t flags,
+                     void *ws, size_t ws_bytes, qsa_stream_t stream);
 
 /*
  * MLA-style list attention (devotd.net news on the llama.cpp CDNA sparse path,

@@ -25,6 +25,8 @@ QSA_ERR_UNSUPPORTED = -3
 QSA_ERR_HIP = -4
 QSA_STEP_FUSED_GATHER = 0
 QSA_STEP_COMPACT_GATHER = 1
+QSA_PREFILL_PER_ROW = 0
+QSA_PREFILL_GROUPED_UNION = 1
 
 EXPORTS = [
     "qsa_status_string", "qsa_last_error", "qsa_config_check", "qsa_workspace_size",
@@ -79,13 +81,13 @@ def load():
         "qsa_topk_blocks": (C.c_int, [cfg, p, i32, i32, i32, p, p, p, sz, p]),
         "qsa_gather_kv": (C.c_int, [cfg, p, i32, i32, p, p, p, p, p]),
         "qsa_sparse_attn": (C.c_int, [cfg, p, p, p, i32, p, p, sz, p]),
-        "qsa_prefill_attn": (C.c_int, [cfg, p, i32, i32, p, i32, p, p, p, p, sz, p]),
+        "qsa_prefill_attn": (C.c_int, [cfg, p, i32, i32, p, i32, p, p, p, u32, p, sz, p]),
         "qsa_decode_step": (C.c_int, [cfg, C.POINTER(qsa_layer_bufs), i32, p, p, p, p, p, p, p,
                                       p, u32, p, sz, p]),
         "qsa_decode_multi": (C.c_int, [cfg, C.POINTER(qsa_layer_bufs), i32, i32, p, p, p, p, p,
                                        p, p, i32, p, p, sz, p]),
         "qsa_prefill_step": (C.c_int, [cfg, C.POINTER(qsa_layer_bufs), i32, i32, p, p, p, p, p,
-                                       p, p, i32, p, p, sz, p]),
+                                       p, p, i32, p, u32, p, sz, p]),
         "qsa_mla_workspace_size": (sz, [i32, i32, i32]),
         "qsa_mla_sparse_attn": (C.c_int, [p, i32, p, p, i32, i32, p, i32, i32, C.c_float, p, p,
                                           p, p, sz, p]),
@@ -248,12 +250,13 @@ def qsa_sparse_attn(cfg: Config, q, k_sel, v_sel, n_cells: int, out, ws) -> None
                                   _ptr(ws), ws.numel(), _stream()))
 
 
-def qsa_prefill_attn(cfg: Config, q, pos0: int, blk, ldb: int, k_cache, v_cache, out, ws) -> None:
+def qsa_prefill_attn(cfg: Config, q, pos0: int, blk, ldb: int, k_cache, v_cache, out, ws,
+                     flags: int = QSA_PREFILL_PER_ROW) -> None:
     c = cfg.c()
     _check(load().qsa_prefill_attn(C.byref(c), _ptr(q, H16, name="q"), q.shape[0], pos0,
                                    _ptr(blk, torch.int32, name="blk"), ldb, _ptr(k_cache, H16),
                                    _ptr(v_cache, H16), _ptr(out, torch.float32, name="out"),
-                                   _ptr(ws), ws.numel(), _stream()))
+                                   flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
 
 
 def qsa_decode_step(cfg: Config, layer: Layer, n_before: int, q_idx, k_idx_new, q, k_new, v_new,
@@ -284,14 +287,16 @@ def qsa_decode_multi(cfg: Config, layer: Layer, n_before: int, q_idx, k_idx_new,
 
 
 def qsa_prefill_step(cfg: Config, layer: Layer, n_before: int, q_idx, k_idx_new, q, k_new, v_new,
-                     out, ws, scores_out=None, ld_scores: int = 0, blk_out=None) -> None:
+                     out, ws, scores_out=None, ld_scores: int = 0, blk_out=None,
+                     flags: int = QSA_PREFILL_PER_ROW) -> None:
     c = cfg.c()
     b = layer.bufs()
     _check(load().qsa_prefill_step(C.byref(c), C.byref(b), n_before, q_idx.shape[0],
                                    _ptr(q_idx, H16), _ptr(k_idx_new, H16), _ptr(q, H16),
                                    _ptr(k_new, H16), _ptr(v_new, H16), _ptr(out, torch.float32),
                                    _ptr(scores_out, torch.float32), ld_scores,
-                                   _ptr(blk_out, torch.int32), _ptr(ws), ws.numel(), _stream()))
+                                   _ptr(blk_out, torch.int32), flags, _ptr(ws), ws.numel(),
+                                   _stream()))
 
 
 def qsa_mla_workspace_size(hq: int, dv: int, list_cap: int) -> int:

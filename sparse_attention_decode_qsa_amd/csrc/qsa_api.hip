@@ -92,7 +92,7 @@ int check_cfg(const qsa_config *c)
 // Workspace layout: data regions whose sizes depend on (cfg, n_q, n_ctx).  No
 // call relies on what a previous call left there.
 struct Layout {
-    size_t lists, lrows, scores, blk, nsel, part, ksel, vsel, total;
+    size_t lists, lrows, scores, blk, nsel, part, ksel, vsel, uid, umask, nu, upart, total;
     int64_t ld;  // score row stride
 };
 
@@ -119,6 +119,19 @@ Layout layout(const qsa_config *c, int32_t n_q, int32_t n_ctx)
     L.part = take(sizeof(float) * nd * c->hq * (size_t)max_splits(c) * (size_t)(c->dv + 2));
     L.ksel = take(sizeof(uint16_t) * (size_t)max_cells(c) * c->hkv * c->d);
     L.vsel = take(sizeof(uint16_t) * (size_t)max_cells(c) * c->hkv * c->dv);
+    // grouped-union prefill attention: union lists, row masks, partials
+    size_t groups = 0, cap_u = 0, usplits = 0;
+    if (union_supported(c->hq, c->hkv, c->d, c->dv, c->topk_blocks)) {
+        const int32_t G = union_group_rows(c->hq, c->hkv);
+        groups = (size_t)((n_q + G - 1) / G);
+        cap_u = (size_t)G * c->topk_blocks;
+        const int32_t sp = union_splits(n_q, c->hq, c->hkv);
+        usplits = sp > 1 ? (size_t)sp : 0;
+    }
+    L.uid = take(sizeof(int32_t) * groups * cap_u);
+    L.umask = take(sizeof(uint32_t) * groups * cap_u);
+    L.nu = take(sizeof(int32_t) * groups);
+    L.upart = take(sizeof(float) * (size_t)n_q * c->hq * usplits * (size_t)(c->dv + 2));
     L.total = off;
     return L;
 }
@@ -573,10 +586,65 @@ int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint16_t *k_
     return attn_decode_launch(cfg, a, n_cells, ws, L, (hipStream_t)stream);
 }
 
+// Attention of a prefill chunk over each row's chosen blocks and tail: per row, or
+// (QSA_PREFILL_GROUPED_UNION) per group of rows over the union of their blocks.
+hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32_t n_q, int32_t pos0,
+                               const int32_t *blk, int32_t ldb, const h16 *kc, const h16 *vc,
+                               float *out, uint32_t flags, void *ws, const Layout &L,
+                               hipStream_t s)
+{
+    if (flags & QSA_PREFILL_GROUPED_UNION) {
+        UnionArgs u;
+        u.q = q;
+        u.blk = blk;
+        u.ldb = ldb;
+        u.k_cache = kc;
+        u.v_cache = vc;
+        u.n_q = n_q;
+        u.pos0 = pos0;
+        u.k = cfg->topk_blocks;
+        u.hq = cfg->hq;
+        u.hkv = cfg->hkv;
+        u.scale = cfg->attn_scale;
+        u.splits = union_splits(n_q, cfg->hq, cfg->hkv);
+        u.uid = at<int32_t>(ws, L.uid);
+        u.umask = at<uint32_t>(ws, L.umask);
+        u.n_u = at<int32_t>(ws, L.nu);
+        u.part = at<float>(ws, L.upart);
+        u.out = out;
+        return launch_union_attn(u, s);
+    }
+    AttnArgs a = attn_base(cfg);
+    a.q = q;
+    a.kbase = kc;
+    a.vbase = vc;
+    a.mode = kCellsBlocks;
+    a.blk = blk;
+    a.ldb = ldb;
+    a.pos0 = pos0;
+    a.rows = n_q;
+    a.splits = 1;
+    a.chunks = max_splits(cfg);
+    a.out = out;
+    return launch_attn(a, cfg->d, cfg->dv, s);
+}
+
+int check_prefill_flags(const qsa_config *cfg, uint32_t flags, const char *fn)
+{
+    if (flags & ~QSA_PREFILL_GROUPED_UNION)
+        return fail(QSA_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+    if ((flags & QSA_PREFILL_GROUPED_UNION) &&
+        !union_supported(cfg->hq, cfg->hkv, cfg->d, cfg->dv, cfg->topk_blocks))
+        return fail(QSA_ERR_UNSUPPORTED,
+                    "%s: grouped union needs hq/hkv in {4, 8, 16}, d = dv = 128 and "
+                    "(128 / (hq/hkv)) * topk_blocks <= %d", fn, kUnionCap);
+    return QSA_OK;
+}
+
 int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int32_t pos0,
                      const int32_t *blk, int32_t ldb, const uint16_t *k_cache,
-                     const uint16_t *v_cache, float *out, void *ws, size_t ws_bytes,
-                     qsa_stream_t stream)
+                     const uint16_t *v_cache, float *out, uint32_t flags, void *ws,
+                     size_t ws_bytes, qsa_stream_t stream)
 {
     int r = check_cfg(cfg);
     if (r)
@@ -590,21 +658,15 @@ int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int3
     NEED_PTR(k_cache);
     NEED_PTR(v_cache);
     NEED_PTR(out);
-    (void)ws;
-    (void)ws_bytes;
-    AttnArgs a = attn_base(cfg);
-    a.q = H(q);
-    a.kbase = H(k_cache);
-    a.vbase = H(v_cache);
-    a.mode = kCellsBlocks;
-    a.blk = blk;
-    a.ldb = ldb;
-    a.pos0 = pos0;
-    a.rows = n_q;
-    a.splits = 1;
-    a.chunks = max_splits(cfg);
-    a.out = out;
-    HIP_CHECK(launch_attn(a, cfg->d, cfg->dv, (hipStream_t)stream));
+    if ((r = check_prefill_flags(cfg, flags, __func__)))
+        return r;
+    // the per-row form needs no workspace
+    const bool uni = (flags & QSA_PREFILL_GROUPED_UNION) != 0;
+    if (uni && (r = check_ws(cfg, ws, ws_bytes, n_q, pos0 + n_q, __func__)))
+        return r;
+    const Layout L = layout(cfg, n_q, pos0 + n_q);
+    HIP_CHECK(prefill_attn_launch(cfg, H(q), n_q, pos0, blk, ldb, H(k_cache), H(v_cache), out,
+                                  flags, ws, L, (hipStream_t)stream));
     return QSA_OK;
 }
 
@@ -632,14 +694,16 @@ int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_
 int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_before,
                      int32_t n_new, const uint16_t *q_idx, const uint16_t *k_idx_new,
                      const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, float *out,
-                     float *scores_out, int32_t ld_scores, int32_t *blk_out, void *ws,
-                     size_t ws_bytes, qsa_stream_t stream)
+                     float *scores_out, int32_t ld_scores, int32_t *blk_out, uint32_t flags,
+                     void *ws, size_t ws_bytes, qsa_stream_t stream)
 {
     int r = check_cfg(cfg);
     if (r)
         return r;
     if (!Lb)
         return fail(QSA_ERR_INVALID, "qsa_prefill_step: layer buffers are NULL");
+    if ((r = check_prefill_flags(cfg, flags, __func__)))
+        return r;
     if (n_before < 0 || n_new < 1)
         return fail(QSA_ERR_INVALID, "qsa_prefill_step: n_before=%d n_new=%d", n_before, n_new);
     if ((int64_t)n_before + n_new > cfg->cap_tokens)
@@ -694,19 +758,8 @@ int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_
     int32_t *blk = blk_out ? blk_out : at<int32_t>(ws, L.blk);
     HIP_CHECK(launch_topk_rows(scores, n_new, ld, n_before, cfg->topk_blocks, blk,
                                at<int32_t>(ws, L.nsel), s));
-    AttnArgs a = attn_base(cfg);
-    a.q = H(q);
-    a.kbase = H(Lb->k_cache);
-    a.vbase = H(Lb->v_cache);
-    a.mode = kCellsBlocks;
-    a.blk = blk;
-    a.ldb = cfg->topk_blocks;
-    a.pos0 = n_before;
-    a.rows = n_new;
-    a.splits = 1;
-    a.chunks = max_splits(cfg);
-    a.out = out;
-    HIP_CHECK(launch_attn(a, cfg->d, cfg->dv, s));
+    HIP_CHECK(prefill_attn_launch(cfg, H(q), n_new, n_before, blk, cfg->topk_blocks,
+                                  H(Lb->k_cache), H(Lb->v_cache), out, flags, ws, L, s));
     return QSA_OK;
 }
 

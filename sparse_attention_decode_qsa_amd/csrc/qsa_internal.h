@@ -143,6 +143,31 @@ struct StepTail {
 };
 hipError_t launch_step_tail(const StepTail &st, hipStream_t s);
 
+// ---- grouped-union prefill attention (k_union.hip) ----------------------------
+// Consecutive query rows (128 / (hq / hkv) of them) share one pass over the union
+// of their chosen blocks; each row keeps exactly its own cells through a mask.
+constexpr int kUnionCap = 16384;      // union slots per group (rows x k)
+constexpr int kUnionMaxSplits = 8;
+constexpr int kUnionTargetWgs = 1024;
+struct UnionArgs {
+    const h16 *q;           // [n_q][hq][128]
+    const int32_t *blk;     // [n_q][ldb] chosen ids per row, ascending
+    int32_t ldb;
+    const h16 *k_cache, *v_cache;
+    int32_t n_q, pos0, k, hq, hkv;
+    float scale;
+    int32_t splits;         // union_splits()
+    int32_t *uid;           // [groups][rows * k]
+    uint32_t *umask;        // [groups][rows * k]
+    int32_t *n_u;           // [groups]
+    float *part;            // [n_q][hq][splits][130] when splits > 1
+    float *out;             // [n_q][hq][128]
+};
+bool union_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k);
+int32_t union_group_rows(int32_t hq, int32_t hkv);
+int32_t union_splits(int32_t n_q, int32_t hq, int32_t hkv);
+hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s);
+
 // ---- MLA list (k_mla.hip) ---------------------------------------------------
 constexpr int kListSeg = 4096;  // positions per list-building work group
 hipError_t launch_mask_list(const h16 *mask, int32_t n, int32_t list_cap, uint32_t *seg_cnt,

@@ -12,7 +12,9 @@ Stream layout: an array of n values is drawn in chunks of ``CHUNK`` values; chun
 comes from ``PCG64(SeedSequence(seed).spawn(n_chunks)[i])``.  The result does not
 depend on how many threads fill it.
 
-The one piece of arithmetic here beyond drawing numbers is ``_rotate`` used for the
+Beyond drawing numbers there are two pieces of arithmetic.  ``correlated_rows`` mixes
+the indexer-query rows of the correlated prefill workload (a first-order
+autoregression over rows).  ``_rotate`` is used for the
 "planted" blocks of the 255k decode workload: the 4 raw keys of a planted block are
 the indexer query rotated back by the half-split RoPE angle of the block's
 position, so that after pooling, normalisation and RoPE the block lines up with the
@@ -93,6 +95,7 @@ class Workload:
     planted: int = 0
     n_q: int = 1
     list_len: int = 0
+    q_corr: float = 0.0   # prefill: lag-1 correlation of consecutive indexer-query rows
     extra: dict = field(default_factory=dict)
 
     @property
@@ -111,6 +114,9 @@ WORKLOADS = {
     "decode_61789": Workload("decode_61789", 2, "decode", 61789, n_layers=12),
     "decode_255181": Workload("decode_255181", 3, "decode", 255181, n_layers=12, planted=8),
     "prefill_1024_at_126253": Workload("prefill_1024_at_126253", 4, "prefill", 126253, n_q=1024),
+    # the same caches, with indexer queries that drift slowly from row to row
+    "prefill_1024_at_126253_corr": Workload("prefill_1024_at_126253_corr", 4, "prefill", 126253,
+                                            n_q=1024, q_corr=0.99),
     "mla_list_262144": Workload("mla_list_262144", 5, "mla", 262144, hq=16, hkv=1, d=576, dv=512,
                                 list_len=2048),
 }
@@ -169,8 +175,22 @@ def prefill_inputs(w: Workload, layer: int = 0) -> dict:
     k = normal_f16(seed_for(w.cid, layer, T_K), (n_all, w.hkv, w.d))
     v = normal_f16(seed_for(w.cid, layer, T_V), (n_all, w.hkv, w.dv))
     q_idx = normal_f16(seed_for(w.cid, layer, T_QIDX), (w.n_q, w.h_idx, w.d_idx))
+    if w.q_corr:
+        q_idx = correlated_rows(q_idx, w.q_corr)
     q = normal_f16(seed_for(w.cid, layer, T_Q), (w.n_q, w.hq, w.d))
     return dict(raw=raw, k=k, v=v, q_idx=q_idx, q=q, depth=w.n_tokens)
+
+
+def correlated_rows(z: np.ndarray, rho: float) -> np.ndarray:
+    """Rows x_0 = z_0, x_r = rho x_(r-1) + sqrt(1 - rho^2) z_r (fp64, then rounded to
+    binary16): every row stays N(0, 1) and rows i apart correlate by rho^i, so that
+    nearby query rows choose overlapping blocks."""
+    x = np.empty(z.shape, np.float64)
+    x[0] = z[0]
+    c = np.sqrt(1.0 - rho * rho)
+    for r in range(1, z.shape[0]):
+        x[r] = rho * x[r - 1] + c * z[r].astype(np.float64)
+    return x.astype(np.float16)
 
 
 def mla_inputs(w: Workload, runs: bool = False) -> dict:

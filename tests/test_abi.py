@@ -150,6 +150,24 @@ def test_entry_points_reject_bad_arguments_on_the_host(lib):
                                 None, 0, None, FAKE, 1 << 30, None) == qb.QSA_ERR_CAPACITY
     assert lib.qsa_decode_multi(cp, C.byref(b), 1000, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, 200, None, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
+    # prefill attention / step: unknown flags, the union form's shape limits and workspace
+    U = qb.QSA_PREFILL_GROUPED_UNION
+    assert lib.qsa_prefill_attn(cp, FAKE, 8, 100, FAKE, 512, FAKE, FAKE, FAKE, 6, FAKE, 1 << 30,
+                                None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_prefill_attn(cp, FAKE, 8, 100, FAKE, 512, FAKE, FAKE, FAKE, U, FAKE, 64,
+                                None) == qb.QSA_ERR_CAPACITY
+    assert lib.qsa_prefill_attn(cp, FAKE, 8, 100, FAKE, 512, FAKE, FAKE, FAKE, U, None, 1 << 30,
+                                None) == qb.QSA_ERR_INVALID
+    for kw in (dict(d=64, dv=64), dict(hq=8, hkv=4), dict(hq=32, hkv=1),
+               dict(hq=16, hkv=4, topk_blocks=1024)):
+        c2 = cfg(cap_tokens=4096, **kw).c()
+        assert lib.qsa_prefill_attn(C.byref(c2), FAKE, 8, 100, FAKE, c2.topk_blocks, FAKE, FAKE,
+                                    FAKE, U, FAKE, 1 << 30, None) == qb.QSA_ERR_UNSUPPORTED, kw
+        assert lib.qsa_prefill_step(C.byref(c2), C.byref(b), 100, 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, None, 0, None, U, FAKE, 1 << 30, None) == \
+            qb.QSA_ERR_UNSUPPORTED, kw
+    assert lib.qsa_prefill_step(cp, C.byref(b), 100, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                0, None, 2, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
 
 
 def test_mla_preconditions(lib):

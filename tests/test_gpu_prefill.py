@@ -107,7 +107,7 @@ def test_topk_rows_large_rows(gpu, n_q, pos0):
         assert np.array_equal(b[i], O.topk_sort(S[i, :nb], k)), i
 
 
-def prefill_case(w, layer=0):
+def prefill_case(w, layer=0, flags=qb.QSA_PREFILL_PER_ROW):
     I = synth.prefill_inputs(w, layer)
     depth, n_q = I["depth"], w.n_q
     cfg = cfg_of(w)
@@ -123,7 +123,7 @@ def prefill_case(w, layer=0):
     ws = qb.workspace(cfg, n_q, depth + n_q)
     qb.qsa_prefill_step(cfg, g, depth, dev(I["q_idx"]), dev(I["raw"][depth:]), dev(I["q"]),
                         dev(I["k"][depth:]), dev(I["v"][depth:]), out, ws, scores_out=scores,
-                        ld_scores=ld, blk_out=blk)
+                        ld_scores=ld, blk_out=blk, flags=flags)
     return I, cfg, g, host(out), host(scores), host(blk)
 
 
@@ -189,3 +189,94 @@ def test_prefill_step_full_size_sampled(gpu):
     r = np.random.default_rng(8)
     rows = sorted({0, 1, w.n_q - 1, *r.choice(w.n_q, 9, replace=False).tolist()})
     check_prefill_rows(w, I, g, out, scores, blk, rows)
+
+
+# ---------------------------------------------------------------- grouped-union form
+UNION = qb.QSA_PREFILL_GROUPED_UNION
+
+
+@pytest.mark.parametrize("q_corr", [0.0, 0.99])
+def test_prefill_step_union_small(gpu, q_corr):
+    # every row of a 300-row chunk (18 groups of 16 rows and a ragged group of 12)
+    w = synth.Workload("prefill_small", 6, "prefill", 4 * 700 + 1, n_q=300, q_corr=q_corr)
+    I, cfg, g, out, scores, blk = prefill_case(w, flags=UNION)
+    check_prefill_rows(w, I, g, out, scores, blk, range(w.n_q))
+
+
+def union_direct(hq, hkv, k, pos0, n_q, seed, shared=0.5, ldb_pad=0):
+    """qsa_prefill_attn on chosen-block lists drawn here (a share of each group's
+    blocks common to its rows), union form against the oracle for every row."""
+    d = dv = 128
+    n_all = pos0 + n_q
+    cap = (n_all + 64) // 4 * 4
+    cfg = qb.Config(topk_blocks=k, hq=hq, hkv=hkv, d=d, dv=dv, cap_tokens=cap)
+    K = synth.normal_f16(seed, (n_all, hkv, d))
+    V = synth.normal_f16(seed + 1, (n_all, hkv, dv))
+    Q = synth.normal_f16(seed + 2, (n_q, hq, d))
+    r = np.random.default_rng(seed)
+    ldb = k + ldb_pad
+    B = np.full((n_q, ldb), -7, np.int32)  # past n_sel: never read
+    common = None
+    for i in range(n_q):
+        nb = (pos0 + i + 1) // 4
+        ns = min(k, nb)
+        if ns == nb:
+            ids = np.arange(nb)
+        else:
+            if common is None or i % 8 == 0:
+                common = r.choice(nb, size=int(ns * shared), replace=False)
+            rest = np.setdiff1d(np.arange(nb), common)
+            ids = np.concatenate([common, r.choice(rest, size=ns - common.size, replace=False)])
+        B[i, :ns] = np.sort(ids)
+    kc = torch.zeros((cap, hkv, d), dtype=torch.float16, device="cuda")
+    vc = torch.zeros((cap, hkv, dv), dtype=torch.float16, device="cuda")
+    kc[:n_all], vc[:n_all] = dev(K), dev(V)
+    ws = qb.workspace(cfg, n_q, n_all)
+    out = torch.full((n_q, hq, dv), 5.0, device="cuda")
+    qb.qsa_prefill_attn(cfg, dev(Q), pos0, dev(B), ldb, kc, vc, out, ws, flags=UNION)
+    got = host(out)
+    scale = 1.0 / np.sqrt(d)
+    for i in range(n_q):
+        nb = (pos0 + i + 1) // 4
+        cl = O.cells(B[i, :min(k, nb)], pos0 + i + 1)
+        ref = O.attn_cells(Q[i], K, V, cl, scale)
+        assert_attn_close(got[i], ref, f"row {i}")
+    return B
+
+
+@pytest.mark.parametrize("hq,hkv,k,pos0,n_q", [
+    (32, 4, 64, 3, 70),      # first rows see every block (nb <= k), empty and full tails
+    (32, 4, 64, 257, 33),    # two full groups and a 1-row group
+    (16, 4, 64, 1001, 45),   # 4 query heads per KV head: groups of 32 rows
+    (32, 2, 64, 2002, 20),   # 16 query heads per KV head: groups of 8 rows
+    (8, 1, 512, 9000, 17),   # k = 512, one KV head
+    (32, 4, 512, 5000, 1),   # a single row
+])
+def test_prefill_attn_union_shapes(gpu, hq, hkv, k, pos0, n_q):
+    union_direct(hq, hkv, k, pos0, n_q, 70 + n_q, ldb_pad=3)
+
+
+def test_prefill_attn_union_past_one_bitmap_window(gpu):
+    # block ids on both sides of 2^18 (the union build's bitmap window)
+    union_direct(8, 1, 512, 4 * ((1 << 18) + (1 << 16)) + 1001, 18, 90, shared=0.25)
+
+
+def test_prefill_attn_union_no_overlap(gpu):
+    # rows with disjoint choices: the union holds rows x k blocks
+    union_direct(32, 4, 64, 40000, 16, 91, shared=0.0)
+
+
+@pytest.mark.parametrize("name", ["prefill_1024_at_126253", "prefill_1024_at_126253_corr"])
+def test_prefill_step_union_full_size_sampled(gpu, name):
+    w = synth.WORKLOADS[name]
+    I, cfg, g, out, scores, blk = prefill_case(w, flags=UNION)
+    r = np.random.default_rng(18)
+    rows = sorted({0, 1, 15, 16, w.n_q - 1, *r.choice(w.n_q, 7, replace=False).tolist()})
+    check_prefill_rows(w, I, g, out, scores, blk, rows)
+    # every row against the per-row form on the same chosen blocks
+    ref = torch.empty_like(dev(out))
+    qb.qsa_prefill_attn(cfg, dev(I["q"]), I["depth"], dev(blk), w.topk, g.k_cache, g.v_cache, ref,
+                        None)
+    ref = host(ref)
+    err = np.max(np.abs(out - ref), axis=(1, 2))
+    assert np.all(err <= 2e-3 * np.max(np.abs(ref), axis=(1, 2))), int(np.argmax(err))
