@@ -37,7 +37,7 @@ constexpr int kUBThreads = 1024;
 constexpr int kWinBlocks = 1 << 18;  // bitmap window of the union build
 constexpr int kWinWords = kWinBlocks / 32;
 
-constexpr int kUAThreads = 256;   // 4 waves
+constexpr int kSetThreads = 256;  // 4 waves: one set of 128 queries
 constexpr int kTB = 16;           // blocks per tile
 constexpr int kTC = kTB * kBlockTokens;  // cells per tile
 constexpr int kDim = 128;         // D = DV
@@ -124,13 +124,30 @@ __global__ __launch_bounds__(kUBThreads) void union_build_kernel(
         n_u[g] = (int32_t)base;
 }
 
-struct alignas(16) UnionAttnLds {
+struct alignas(16) UnionTile {
     alignas(16) h16 ks[kTC * KP];    // K tile, [cell][d]
     alignas(16) h16 vt[kDim * VP];   // V tile transposed, [dv][cell]
     int32_t bid[kTB];                // block id of each tile block, -1 past the end
-    uint32_t bmask[kTB];             // union block: rows that chose it
+    uint32_t bmask[kTB];             // union block: rows that chose it; 0 otherwise
     int32_t btail[kTB];              // 1 for a block of the tail span
 };
+template <int SETS>
+struct alignas(16) UnionTiles {
+    UnionTile buf[SETS][2];          // per set: the tile being read and the next one
+};
+struct alignas(16) UnionMerge {      // set 1's state, for set 0 to merge
+    f32x4 o[4][16][kWave];
+    float m[4][2][kWave];
+    float l[4][2][kWave];
+};
+template <int SETS>
+union UnionAttnLds {
+    UnionTiles<SETS> tiles;
+    UnionMerge merge;
+};
+
+constexpr int kPartStride = kUnionPartStride;  // (m, l, -, -) then o: 16-byte aligned
+static_assert(kPartStride == 4 + kDim, "partial row layout");
 
 struct UnionAttnArgs {
     const h16 *q;           // [n_q][hq][128]
@@ -142,16 +159,20 @@ struct UnionAttnArgs {
     int32_t n_q, pos0, hq, hkv;
     float scale;
     int32_t splits;
-    float *part;            // [n_q][hq][splits][130] when splits > 1
+    float *part;            // [n_q][hq][splits][kPartStride] when splits > 1
     float *out;             // [n_q][hq][128]
 };
 
-template <int GQA>
-__global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs a)
+// SETS wave sets of 4 waves per work group take alternate tiles and merge through
+// LDS at the end (SETS = 2), or each work group is one set (SETS = 1).
+template <int GQA, int SETS>
+__global__ __launch_bounds__(kSetThreads * SETS, 3 - SETS) void union_attn_kernel(UnionAttnArgs a)
 {
     constexpr int G = 128 / GQA;  // rows per group
-    __shared__ UnionAttnLds sm;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    constexpr int kUASets = SETS;
+    __shared__ UnionAttnLds<SETS> sm;
+    const int lane = threadIdx.x & 63;
+    const int set = threadIdx.x >> 8, t = threadIdx.x & 255, wave = t >> 6;  // within the set
     const int n = lane & 15, g4 = lane >> 4;
     const int32_t g = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
     const int32_t r0 = g * G;
@@ -169,20 +190,6 @@ __global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs
     const int32_t tb = min(n_tiles, split * tps), te = min(n_tiles, tb + tps);
     const int32_t *ug = a.uid + (int64_t)g * a.cap_u;
     const uint32_t *mg = a.umask + (int64_t)g * a.cap_u;
-
-    auto block_of = [&](int32_t v, uint32_t &mask, int32_t &tail) -> int32_t {
-        mask = 0u;
-        tail = 0;
-        if (v < nu) {
-            mask = mg[v];
-            return ug[v];
-        }
-        if (v < n_virt) {
-            tail = 1;
-            return t0 / kBlockTokens + (v - nu);
-        }
-        return -1;
-    };
 
     // this lane's two queries (nb = 0, 1): m = 32 wave + 16 nb + n
     int32_t qrow[2];
@@ -206,49 +213,56 @@ __global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs
         tail_lo[nb] = ((p_last[nb] + 1) / kBlockTokens) * kBlockTokens;
     }
 
-    // staging registers: K (cell t/4, 32 dims), V (block t/16, 8 dims x 4 cells)
-    const int kcell = t >> 2, kpart = (t & 3) * 32;
-    const int vblk = t >> 4, vch = (t & 15) * 8;
-    h16x8 kr[4], vr[4];
-    uint32_t meta_mask = 0u;
-    int32_t meta_id = -1, meta_tail = 0;
-    auto gload = [&](int32_t tile) {
-        const int32_t vbase = tile * kTB;
-        uint32_t mk;
-        int32_t tl;
-        {
-            const int32_t id = block_of(vbase + (kcell >> 2), mk, tl);
-            const int32_t c = id * kBlockTokens + (kcell & 3);
-            const bool ok = id >= 0 && c < t1;
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                kr[j] = ok ? *(const h16x8 *)(a.kc + (int64_t)c * kt + (int64_t)h * kDim + kpart + 8 * j)
-                           : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        {
-            const int32_t id = block_of(vbase + vblk, mk, tl);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int32_t c = id * kBlockTokens + e;
-                vr[e] = (id >= 0 && c < t1)
-                            ? *(const h16x8 *)(a.vc + (int64_t)c * kt + (int64_t)h * kDim + vch)
-                            : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-        if (t < kTB)
-            meta_id = block_of(vbase + t, meta_mask, meta_tail);
+    // Thread t stages block t / 16 of a tile: K cell t / 4 (32 dims) and V dims
+    // 8 (t % 16) .. + 8 of the block's 4 cells; (t % 16) == 0 writes the block's
+    // entry.  The block's id and mask are fetched two tiles ahead, its K/V one
+    // tile ahead.
+    const int vb = t >> 4;
+    const int kpart = (t & 15) * 8;  // K and V: 16 lanes cover one 256-byte cell row
+    const int vch = (t & 15) * 8;
+    struct Meta {
+        int32_t id;
+        uint32_t mask;
+        int32_t tail;
     };
-    auto sstore = [&]() {
+    auto meta_of = [&](int32_t tile) -> Meta {
+        const int32_t v = tile * kTB + vb;
+        if (v < nu)
+            return Meta{ug[v], mg[v], 0};
+        if (v < n_virt)
+            return Meta{t0 / kBlockTokens + (v - nu), 0u, 1};
+        return Meta{-1, 0u, 0};
+    };
+    h16x8 kr[4], vr[4];
+    Meta staged{-1, 0u, 0};
+    auto kv_load = [&](const Meta &m) {
+        staged = m;
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            *(h16x8 *)&sm.ks[kcell * KP + kpart + 8 * j] = kr[j];
+        for (int e = 0; e < 4; e++) {
+            const int32_t ce = m.id * kBlockTokens + e;
+            kr[e] = (m.id >= 0 && ce < t1)
+                        ? *(const h16x8 *)(a.kc + (int64_t)ce * kt + (int64_t)h * kDim + kpart)
+                        : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int32_t ce = m.id * kBlockTokens + e;
+            vr[e] = (m.id >= 0 && ce < t1)
+                        ? *(const h16x8 *)(a.vc + (int64_t)ce * kt + (int64_t)h * kDim + vch)
+                        : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    };
+    auto sstore = [&](UnionTile &T) {
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            *(h16x8 *)&T.ks[(vb * 4 + e) * KP + kpart] = kr[e];
 #pragma unroll
         for (int i = 0; i < 8; i++)
-            *(h16x4 *)&sm.vt[(vch + i) * VP + vblk * 4] = h16x4{vr[0][i], vr[1][i], vr[2][i], vr[3][i]};
-        if (t < kTB) {
-            sm.bid[t] = meta_id;
-            sm.bmask[t] = meta_mask;
-            sm.btail[t] = meta_tail;
+            *(h16x4 *)&T.vt[(vch + i) * VP + vb * 4] = h16x4{vr[0][i], vr[1][i], vr[2][i], vr[3][i]};
+        if ((t & 15) == 0) {
+            T.bid[vb] = staged.id;
+            T.bmask[vb] = staged.mask;
+            T.btail[vb] = staged.tail;
         }
     };
 
@@ -261,14 +275,28 @@ __global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
     const float sl2 = a.scale * kLog2e;
 
-    if (tb < te)
-        gload(tb);
-    for (int32_t tile = tb; tile < te; tile++) {
-        __syncthreads();
-        sstore();
-        __syncthreads();
-        if (tile + 1 < te)
-            gload(tile + 1);
+    // set s takes tiles tb + s, tb + s + 2, ...; both sets pass the same barriers
+    UnionTile *buf = sm.tiles.buf[set];
+    const int32_t first = tb + set;
+    Meta ahead{-1, 0u, 0};
+    if (first < te) {
+        kv_load(meta_of(first));
+        if (first + kUASets < te)
+            ahead = meta_of(first + kUASets);
+        sstore(buf[0]);
+    }
+    __syncthreads();
+    if (first + kUASets < te) {
+        kv_load(ahead);
+        if (first + 2 * kUASets < te)
+            ahead = meta_of(first + 2 * kUASets);
+    }
+    const int32_t n_iter = (te - tb + kUASets - 1) / kUASets;
+    for (int32_t j = 0; j < n_iter; j++) {
+        const int32_t tile = first + kUASets * j;
+        if (tile < te) {
+        const UnionTile &T = buf[j & 1];
+        const bool has_tail = (tile + 1) * kTB > nu && ntb > 0;  // uniform
 
         // S^T = K Q^T: lane holds cells 16 mb + 4 g4 + e of queries n (+16 nb)
         f32x4 sacc[2][4];
@@ -281,7 +309,7 @@ __global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs
         for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
             for (int mb = 0; mb < 4; mb++) {
-                const h16x8 kf = *(const h16x8 *)&sm.ks[(16 * mb + n) * KP + 32 * ks + 8 * g4];
+                const h16x8 kf = *(const h16x8 *)&T.ks[(16 * mb + n) * KP + 32 * ks + 8 * g4];
 #pragma unroll
                 for (int nb = 0; nb < 2; nb++)
                     sacc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[nb][ks], sacc[nb][mb],
@@ -289,50 +317,62 @@ __global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs
             }
         }
 
-        // mask, online softmax, P in the k-slot order of the PV product
-        int32_t bid[4], btl[4];
+        // mask (per block; per cell only in a tile holding the tail span), online
+        // softmax, P in the k-slot order of the PV product
         uint32_t bmk[4];
 #pragma unroll
-        for (int mb = 0; mb < 4; mb++) {
-            bid[mb] = sm.bid[4 * mb + g4];
-            bmk[mb] = sm.bmask[4 * mb + g4];
-            btl[mb] = sm.btail[4 * mb + g4];
-        }
+        for (int mb = 0; mb < 4; mb++)
+            bmk[mb] = T.bmask[4 * mb + g4];
         h16x8 pf[2][2];
+        bool rescale = false;
+        float alpha[2];
 #pragma unroll
         for (int nb = 0; nb < 2; nb++) {
             float s[4][4];
-            float tmax = -INFINITY;
 #pragma unroll
             for (int mb = 0; mb < 4; mb++) {
+                const bool vis = ((bmk[mb] >> qrow[nb]) & 1u) != 0u;
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int32_t c = bid[mb] * kBlockTokens + e;
-                    const bool vis = bid[mb] >= 0 &&
-                                     (btl[mb] ? (c >= tail_lo[nb] && c <= p_last[nb])
-                                              : ((bmk[mb] >> qrow[nb]) & 1u) != 0u);
-                    s[mb][e] = vis ? sacc[nb][mb][e] * sl2 : -INFINITY;
-                    tmax = fmaxf(tmax, s[mb][e]);
+                for (int e = 0; e < 4; e++)
+                    s[mb][e] = vis ? sacc[nb][mb][e] : -INFINITY;
+            }
+            if (has_tail) {
+#pragma unroll
+                for (int mb = 0; mb < 4; mb++) {
+                    if (T.btail[4 * mb + g4]) {
+                        const int32_t c0 = T.bid[4 * mb + g4] * kBlockTokens;
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            s[mb][e] = (c0 + e >= tail_lo[nb] && c0 + e <= p_last[nb])
+                                           ? sacc[nb][mb][e]
+                                           : -INFINITY;
+                    }
                 }
             }
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    tmax = fmaxf(tmax, s[mb][e]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-            const float mnew = fmaxf(m_run[nb], tmax);
-            const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run[nb] - mnew);
+            // scores are scaled inside the exponent: p = 2^(s * sl2 - m)
+            const float mnew = fmaxf(m_run[nb], tmax * sl2);
+            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+            alpha[nb] = __builtin_amdgcn_exp2f(m_run[nb] - mref);
+            rescale |= mnew != m_run[nb];
             float psum = 0.f;
 #pragma unroll
             for (int mb = 0; mb < 4; mb++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const float p = (s[mb][e] == -INFINITY) ? 0.f : exp2f(s[mb][e] - mnew);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][e], sl2, -mref));
                     s[mb][e] = p;
                     psum += p;
                 }
-            l_run[nb] = l_run[nb] * alpha + psum;
+            l_run[nb] = l_run[nb] * alpha[nb] + psum;
             m_run[nb] = mnew;
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                oacc[nb][i] *= alpha;
 #pragma unroll
             for (int kc = 0; kc < 2; kc++)
                 pf[nb][kc] = h16x8{(h16)s[2 * kc][0],     (h16)s[2 * kc][1],
@@ -340,13 +380,21 @@ __global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs
                                    (h16)s[2 * kc + 1][0], (h16)s[2 * kc + 1][1],
                                    (h16)s[2 * kc + 1][2], (h16)s[2 * kc + 1][3]};
         }
+        // O is rescaled only when some lane's running maximum moved
+        if (__any(rescale)) {
+#pragma unroll
+            for (int nb = 0; nb < 2; nb++)
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    oacc[nb][i] *= alpha[nb];
+        }
 
         // O^T += V^T P^T: lane holds dv 16 i + 4 g4 + e of queries n (+16 nb)
 #pragma unroll
         for (int i = 0; i < 8; i++) {
 #pragma unroll
             for (int kc = 0; kc < 2; kc++) {
-                const h16 *vp = &sm.vt[(16 * i + n) * VP + 32 * kc + 4 * g4];
+                const h16 *vp = &T.vt[(16 * i + n) * VP + 32 * kc + 4 * g4];
                 const h16x4 lo = *(const h16x4 *)vp;
                 const h16x4 hi = *(const h16x4 *)(vp + 16);
                 const h16x8 vf = h16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -356,14 +404,61 @@ __global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs
                                                                         0, 0, 0);
             }
         }
+
+        }
+        // this set's next tile into its other buffer, then one barrier; then the
+        // loads of the tile after it
+        if (tile + kUASets < te)
+            sstore(buf[(j + 1) & 1]);
+        __syncthreads();
+        if (tile + 2 * kUASets < te) {
+            kv_load(ahead);
+            if (tile + 3 * kUASets < te)
+                ahead = meta_of(tile + 3 * kUASets);
+        }
     }
 
     // the four lane groups hold different cells of the same queries
+    float l_tot[2];
 #pragma unroll
     for (int nb = 0; nb < 2; nb++) {
         float l = l_run[nb];
         l += __shfl_xor(l, 16, kWave);
         l += __shfl_xor(l, 32, kWave);
+        l_tot[nb] = l;
+    }
+    // set 1 hands its state to set 0 through LDS (the tiles are no longer read)
+    if (SETS == 2 && set == 1) {
+#pragma unroll
+        for (int nb = 0; nb < 2; nb++) {
+            sm.merge.m[wave][nb][lane] = m_run[nb];
+            sm.merge.l[wave][nb][lane] = l_tot[nb];
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                sm.merge.o[wave][nb * 8 + i][lane] = oacc[nb][i];
+        }
+    }
+    if (SETS == 2) {
+        __syncthreads();
+        if (set == 1)
+            return;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2 && SETS == 2; nb++) {
+        const float m1 = sm.merge.m[wave][nb][lane];
+        const float mm = fmaxf(m_run[nb], m1);
+        const float mref = (mm == -INFINITY) ? 0.f : mm;
+        const float a0 = __builtin_amdgcn_exp2f(m_run[nb] - mref);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - mref);
+        l_tot[nb] = a0 * l_tot[nb] + a1 * sm.merge.l[wave][nb][lane];
+        m_run[nb] = mm;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            oacc[nb][i] = a0 * oacc[nb][i] + a1 * sm.merge.o[wave][nb * 8 + i][lane];
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; nb++) {
+        const float l = l_tot[nb];
         if (qrow[nb] >= nr)
             continue;
         const int m = 32 * wave + 16 * nb + n;
@@ -374,17 +469,40 @@ __global__ __launch_bounds__(kUAThreads, 2) void union_attn_kernel(UnionAttnArgs
             for (int i = 0; i < 8; i++)
                 *(f32x4 *)(a.out + qh * kDim + 16 * i + 4 * g4) = oacc[nb][i] * inv;
         } else {
-            float *pb = a.part + (qh * a.splits + split) * (kDim + 2);
-            if (g4 == 0) {
-                pb[0] = m_run[nb];
-                pb[1] = l;
-            }
+            float *pb = a.part + (qh * a.splits + split) * kPartStride;
+            if (g4 == 0)
+                *(f32x4 *)pb = f32x4{m_run[nb], l, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 8; i++)
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    pb[2 + 16 * i + 4 * g4 + e] = oacc[nb][i][e];
+                *(f32x4 *)(pb + 4 + 16 * i + 4 * g4) = oacc[nb][i];
         }
+    }
+}
+
+// Merge of the split partials of a prefill chunk: one work group per row, a
+// thread per (query head, 4 output dims); weights w_s = 2^(m_s - M).
+constexpr int kUCombThreads = 256;
+__global__ __launch_bounds__(kUCombThreads) void union_combine_kernel(const float *__restrict__ part,
+                                                                     int32_t hq, int32_t S,
+                                                                     float *__restrict__ out)
+{
+    const int64_t row = blockIdx.x;
+    for (int idx = threadIdx.x; idx < hq * (kDim / 4); idx += kUCombThreads) {
+        const int h = idx / (kDim / 4), c = idx % (kDim / 4);
+        const float *pb = part + (row * hq + h) * S * kPartStride;
+        float M = -INFINITY;
+        for (int sp = 0; sp < S; sp++)
+            M = fmaxf(M, pb[sp * kPartStride]);
+        const float mref = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f;
+        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < S; sp++) {
+            const f32x4 ml = *(const f32x4 *)(pb + sp * kPartStride);
+            const float w = __builtin_amdgcn_exp2f(ml[0] - mref);
+            L += w * ml[1];
+            o += w * *(const f32x4 *)(pb + sp * kPartStride + 4 + 4 * c);
+        }
+        *(f32x4 *)(out + (row * hq + h) * kDim + 4 * c) = o * (1.f / L);
     }
 }
 
@@ -437,16 +555,19 @@ hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s)
     a.part = u.part;
     a.out = u.out;
     const dim3 grid((uint32_t)groups, (uint32_t)u.hkv, (uint32_t)u.splits);
+    const dim3 block(kSetThreads * kUnionSets);
     switch (u.hq / u.hkv) {
-    case 4: hipLaunchKernelGGL(union_attn_kernel<4>, grid, dim3(kUAThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(union_attn_kernel<8>, grid, dim3(kUAThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL(union_attn_kernel<16>, grid, dim3(kUAThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((union_attn_kernel<4, kUnionSets>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((union_attn_kernel<8, kUnionSets>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((union_attn_kernel<16, kUnionSets>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();
     if (e != hipSuccess || u.splits == 1)
         return e;
-    return launch_combine(u.part, u.hq, u.splits, kDim, u.n_q, u.out, s);
+    hipLaunchKernelGGL(union_combine_kernel, dim3((uint32_t)u.n_q), dim3(kUCombThreads), 0, s,
+                       u.part, u.hq, u.splits, u.out);
+    return hipGetLastError();
 }
 
 }  // namespace qsa

@@ -131,7 +131,7 @@ Layout layout(const qsa_config *c, int32_t n_q, int32_t n_ctx)
     L.uid = take(sizeof(int32_t) * groups * cap_u);
     L.umask = take(sizeof(uint32_t) * groups * cap_u);
     L.nu = take(sizeof(int32_t) * groups);
-    L.upart = take(sizeof(float) * (size_t)n_q * c->hq * usplits * (size_t)(c->dv + 2));
+    L.upart = take(sizeof(float) * (size_t)n_q * c->hq * usplits * (size_t)kUnionPartStride);
     L.total = off;
     return L;
 }

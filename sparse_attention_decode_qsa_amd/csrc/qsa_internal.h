@@ -148,7 +148,9 @@ hipError_t launch_step_tail(const StepTail &st, hipStream_t s);
 // of their chosen blocks; each row keeps exactly its own cells through a mask.
 constexpr int kUnionCap = 16384;      // union slots per group (rows x k)
 constexpr int kUnionMaxSplits = 8;
-constexpr int kUnionTargetWgs = 1024;
+constexpr int kUnionSets = 1;         // 4-wave sets per work group
+constexpr int kUnionTargetWgs = 512;  // work groups per launch the splits aim for
+constexpr int kUnionPartStride = 132; // floats per split partial: (m, l, -, -) + 128 dims
 struct UnionArgs {
     const h16 *q;           // [n_q][hq][128]
     const int32_t *blk;     // [n_q][ldb] chosen ids per row, ascending
@@ -160,7 +162,7 @@ struct UnionArgs {
     int32_t *uid;           // [groups][rows * k]
     uint32_t *umask;        // [groups][rows * k]
     int32_t *n_u;           // [groups]
-    float *part;            // [n_q][hq][splits][130] when splits > 1
+    float *part;            // [n_q][hq][splits][kUnionPartStride] when splits > 1
     float *out;             // [n_q][hq][128]
 };
 bool union_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k);
