@@ -17,11 +17,12 @@
 // scan, so the score is bit-identical to scanning the appended cache.  The
 // scan work groups only read rows of blocks that were complete before.
 //
-// In the decode step every wave also keeps the kListLen best (score, id) pairs
-// of the rows it scored, as wave-uniform 64-bit rank keys; the last wave of the
-// work group to finish picks the kListLen best of their union (in any order)
-// and writes them, so the top-k launch reads a few thousand candidates instead
-// of the whole row.
+// In the decode step every wave also keeps, per query row, the kListLen best
+// (score, id) pairs of the rows it scored as 64-bit rank keys spread over 8 lanes
+// (one entry per lane); the last wave of the work group to finish picks, per
+// query row, the kListLen best of their union (in any order) and writes them, so
+// the top-k reads a few thousand candidates per query row instead of the whole
+// score row.
 #include "qsa_append.h"
 
 namespace qsa {
@@ -46,23 +47,27 @@ __device__ __forceinline__ float score_row_lds(const h16 *q, const h16 *row)
     return group_sum<LPR>(acc);
 }
 
-// Inserts x into the descending list top[0..kListLen).
-__device__ __forceinline__ void list_insert(uint64_t (&top)[kListLen], uint64_t x)
+// A wave's candidate lists live across its lanes: lane 8 g + i holds entry i of
+// query g's descending list of kListLen rank keys (0 = empty).  Inserting x (the
+// key of query g's score, the same in the 8 lanes of group g): slot i keeps its
+// entry if x does not outrank it, else takes x or, when x also outranks the entry
+// above, that entry (a shift down by one, through a DPP row shift).
+static_assert(kListLen == 8, "8 lanes per list");
+constexpr int kDppRowShr1 = 0x111;  // row_shr:1
+__device__ __forceinline__ uint64_t lane_list_insert(uint64_t v, uint64_t x, int slot)
 {
-    if (x > top[kListLen - 1]) {
-        top[kListLen - 1] = x;
-#pragma unroll
-        for (int i = kListLen - 1; i > 0; i--) {
-            const uint64_t a = top[i - 1], b = top[i];
-            top[i - 1] = a > b ? a : b;
-            top[i] = a > b ? b : a;
-        }
-    }
+    const uint32_t plo =
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, kDppRowShr1, 0xf, 0xf, false);
+    const uint32_t phi =
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), kDppRowShr1, 0xf, 0xf, false);
+    const uint64_t above = slot == 0 ? ~0ull : (((uint64_t)phi << 32) | plo);
+    return x > v ? (x > above ? above : x) : v;
 }
 
 // NQ queries (rows of q, ROWC 16-byte chunks each) score every row read once;
 // query i's scores go to scores[i * ld + b].  APPEND: work group 0 runs the
-// append.  LISTS (one query): candidate lists in the epilogue.
+// append.  LISTS: candidate lists in the epilogue, one per query row (row i's at
+// cl.list + i * kListWgs * kListLen, its row counts at cl.rows + i * kListWgs).
 template <int ROWC, int U, int NT, int NQ, bool APPEND, bool LISTS>
 __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict__ q,
                                                           const h16 *__restrict__ pool,
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
     constexpr int LPR = ROWC < kWave ? ROWC : kWave;  // lanes per row
     constexpr int CPL = ROWC / LPR;                   // chunks per lane per row
     constexpr int RPW = kWave / LPR;                  // rows per wave per group
-    static_assert(!LISTS || (APPEND && NQ == 1), "candidate lists: the one-query decode step");
+    static_assert(!LISTS || APPEND, "candidate lists: the decode step");
     static_assert(!LISTS || NW * kListLen <= kWave, "one merged entry per lane of wave 0");
     static_assert(NQ >= 1 && NQ <= NW, "one wave per query for the appended row");
     const int lane = threadIdx.x & (kWave - 1);
@@ -98,17 +103,21 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
                 mine = rank_key(sc, (uint32_t)ap.b_lo);
             }
         }
-        if (LISTS) {
-            // its list: the new block (if any), then empty slots
-            if (wave == 0 && lane < kListLen)
-                cl.list[lane] = lane == 0 ? mine : 0ull;
-            if (threadIdx.x == 0)
-                cl.rows[0] = (uint32_t)ap.n_blocks;
+        if (LISTS && wave < NQ && lane < kListLen) {
+            // query row `wave` (the token at n_before + wave) sees the new block
+            // once its token completes it: that row's list holds it, the others
+            // are empty
+            const bool sees = ap.n_blocks == 1 &&
+                              ap.n_before + wave >= kBlockTokens * ap.b_lo + (kBlockTokens - 1);
+            const int64_t li = (int64_t)wave * kListWgs;
+            cl.list[li * kListLen + lane] = (lane == 0 && sees) ? mine : 0ull;
+            if (lane == 0)
+                cl.rows[li] = sees ? 1u : 0u;
         }
         return;
     }
 
-    __shared__ uint64_t wtop[LISTS ? NW * kListLen : 1];
+    __shared__ uint64_t wtop[LISTS ? NQ : 1][LISTS ? NW * kListLen : 1];
     __shared__ uint32_t wrows[NW];
     __shared__ uint32_t wdone;
     if (LISTS) {
@@ -135,10 +144,9 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
         ((int64_t)(wave / kRun) * nwg + (blockIdx.x - (APPEND ? 1 : 0))) * kRun + wave % kRun;
     const int64_t tw = nwg * NW;
     const h16x8 *rows = (const h16x8 *)pool;
-    uint64_t top[kListLen];
-#pragma unroll
-    for (int i = 0; i < kListLen; i++)
-        top[i] = 0ull;
+    static_assert(!LISTS || NQ * kListLen <= kWave, "one list per 8 lanes");
+    const int lgrp = lane / kListLen, lslot = lane % kListLen;
+    uint64_t lst = 0ull;  // entry lslot of query lgrp's list
     uint32_t nrows = 0;
 
     for (int64_t g0 = gw; g0 < groups; g0 += tw * U) {
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
         }
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            float acc = 0.f;
+            float acc[NQ];
 #pragma unroll
             for (int qi = 0; qi < NQ; qi++) {
                 float a = 0.f;
@@ -168,17 +176,28 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
                 a = group_sum<LPR>(a);
                 if (sub == 0 && r[u] < nb)
                     scores[(int64_t)qi * ld + r[u]] = a;
-                acc = a;
+                acc[qi] = a;
             }
             if (LISTS) {
-                // the RPW rows of this group, one at a time, as wave-uniform values
+                // the RPW rows of this group, one at a time: lane group g inserts
+                // query g's key
 #pragma unroll
                 for (int rs = 0; rs < RPW; rs++) {
                     const int64_t rr = (g0 + (int64_t)u * tw) * RPW + rs;
                     if (rr < nb) {
-                        const float sc =
-                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), rs * LPR));
-                        list_insert(top, rank_key(sc, (uint32_t)rr));
+                        // one row per wave: the butterfly sum left every query's
+                        // score in every lane; otherwise read it from the row's lanes
+                        float sc = 0.f;
+#pragma unroll
+                        for (int qi = 0; qi < NQ; qi++) {
+                            const float s_q =
+                                RPW == 1 ? acc[qi]
+                                         : __int_as_float(__builtin_amdgcn_readlane(
+                                               __float_as_int(acc[qi]), rs * LPR));
+                            sc = lgrp == qi ? s_q : sc;
+                        }
+                        const uint64_t x = lgrp < NQ ? rank_key(sc, (uint32_t)rr) : 0ull;
+                        lst = lane_list_insert(lst, x, lslot);
                         nrows++;
                     }
                 }
@@ -189,58 +208,44 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
     if (LISTS) {
         // no barrier: each wave posts its list and counts itself done; the last
         // wave of the work group merges (earlier waves just end)
-        if (lane == 0) {
-#pragma unroll
-            for (int i = 0; i < kListLen; i++)
-                wtop[wave * kListLen + i] = top[i];
+        if (lgrp < NQ)
+            wtop[lgrp][wave * kListLen + lslot] = lst;
+        if (lane == 0)
             wrows[wave] = nrows;
-        }
         uint32_t prev = 0;
         if (lane == 0)
             prev = __hip_atomic_fetch_add(&wdone, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
         prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
         if (prev == NW - 1) {
-            // the kListLen largest of the NW * kListLen entries, one per lane,
-            // found in registers: a bitwise search with ballots for the
-            // kListLen-th largest score key, then (only if it is tied) for the
-            // low word among the entries with that key
+            // per query row, the kListLen largest of the NW * kListLen entries, one
+            // per lane: each lane counts the entries that outrank its own (LDS
+            // broadcast reads; keys are distinct, empty entries are 0), so the
+            // kListLen best have ranks 0 .. kListLen - 1 and take those slots
             constexpr int NE = NW * kListLen;
-            const uint64_t me = lane < NE ? wtop[lane] : 0ull;
-            const uint32_t hi = (uint32_t)(me >> 32), lo = (uint32_t)me;
-            uint32_t th = 0;
-            for (int bit = 31; bit >= 0; bit--) {
-                const uint32_t c = th | (1u << bit);
-                if (__popcll(__ballot(hi >= c)) >= kListLen)
-                    th = c;
-            }
-            uint32_t tl = 0;
-            const uint32_t n_above = (uint32_t)__popcll(__ballot(hi > th));
-            if (__popcll(__ballot(hi >= th)) > kListLen) {
-                const uint32_t want = kListLen - n_above;
-                for (int bit = 31; bit >= 0; bit--) {
-                    const uint32_t c = tl | (1u << bit);
-                    if ((uint32_t)__popcll(__ballot(hi == th && lo >= c)) >= want)
-                        tl = c;
-                }
-            }
-            // chosen: > (th, tl); empty entries (0) never; the list keeps them in
-            // lane order, the rest of its slots empty
-            const uint64_t thr = ((uint64_t)th << 32) | tl;
-            const bool pick = me != 0ull && me >= thr;
-            const uint64_t pm = __ballot(pick);
-            const uint32_t slot = (uint32_t)__popcll(pm & ((1ull << lane) - 1ull));
-            const uint32_t npick = (uint32_t)__popcll(pm);
-            uint64_t *dst = cl.list + (int64_t)blockIdx.x * kListLen;
-            if (pick && slot < (uint32_t)kListLen)
-                dst[slot] = me;
-            if ((uint32_t)lane >= npick && lane < kListLen)
-                dst[lane] = 0ull;
-            if (lane == 0) {
-                uint32_t n = 0;
+            static_assert(!LISTS || NE == kWave, "one entry per lane");
+            uint32_t n = 0;
 #pragma unroll
-                for (int w = 0; w < NW; w++)
-                    n += wrows[w];
-                cl.rows[blockIdx.x] = n;
+            for (int w = 0; w < NW; w++)
+                n += wrows[w];
+#pragma unroll
+            for (int qi = 0; qi < NQ; qi++) {
+                const uint64_t me = wtop[qi][lane];
+                uint32_t rank = 0;
+#pragma unroll 8
+                for (int j = 0; j < NE; j += 2) {
+                    const uint64_t a0 = wtop[qi][j], a1 = wtop[qi][j + 1];
+                    rank += (a0 > me ? 1u : 0u) + (a1 > me ? 1u : 0u);
+                }
+                const bool pick = me != 0ull && rank < (uint32_t)kListLen;
+                const uint32_t npick = (uint32_t)__popcll(__ballot(pick));
+                const int64_t li = (int64_t)qi * kListWgs + blockIdx.x;
+                uint64_t *dst = cl.list + li * kListLen;
+                if (pick)
+                    dst[rank] = me;
+                if ((uint32_t)lane >= npick && lane < kListLen)
+                    dst[lane] = 0ull;
+                if (lane == 0)
+                    cl.rows[li] = n;
             }
         }
     }
@@ -265,7 +270,7 @@ hipError_t launch_step(const h16 *q, const h16 *pool, int32_t nb, float *scores,
         grid = 1;
     const size_t lds = sizeof(f32x2) * (size_t)(ap.d / 2) + sizeof(h16) * (size_t)ROWC * 8;
     if (cl) {
-        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kStepThreads, 1, true, true>),
+        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kStepThreads, NQ, true, true>),
                            dim3((uint32_t)grid + 1), dim3(kStepThreads), lds, s, q, pool, nb,
                            scores, ld, ap, *cl);
         *n_lists = (int32_t)grid + 1;
@@ -303,9 +308,9 @@ hipError_t launch_rowc(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb, f
     }
     switch (n_q) {
     case 1: return launch_step<ROWC, 1>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
-    case 2: return launch_step<ROWC, 2>(q, pool, nb, scores, ld, *ap, nullptr, n_lists, s);
-    case 3: return launch_step<ROWC, 3>(q, pool, nb, scores, ld, *ap, nullptr, n_lists, s);
-    case 4: return launch_step<ROWC, 4>(q, pool, nb, scores, ld, *ap, nullptr, n_lists, s);
+    case 2: return launch_step<ROWC, 2>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
+    case 3: return launch_step<ROWC, 3>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
+    case 4: return launch_step<ROWC, 4>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -319,8 +324,8 @@ hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32
     if (nb <= 0 && !ap)
         return hipSuccess;
     // the fused append builds at most one pooled row, of the block right after the
-    // scanned ones, in the layout the scan reads; candidate lists for one query only
-    if (n_q < 1 || n_q > 4 || (!ap && n_q != 1) || (cl && (n_q != 1 || !n_lists)) ||
+    // scanned ones, in the layout the scan reads; candidate lists need the append
+    if (n_q < 1 || n_q > 4 || (!ap && n_q != 1) || (cl && (!ap || !n_lists)) ||
         (ap && (ap->n_blocks > 1 || (ap->n_blocks == 1 && ap->b_lo != nb) ||
                 (int64_t)ap->H * ap->d != row_elems)))
         return hipErrorInvalidValue;

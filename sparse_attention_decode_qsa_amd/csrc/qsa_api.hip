@@ -272,21 +272,14 @@ int decode_impl(const char *fn, const qsa_config *cfg, const qsa_layer_bufs *Lb,
     ap.base = cfg->rope_base;
 
     // 2. scores of every query row over the blocks complete before the call; the
-    // append runs in the same launch and scores the block it completes.  One row:
-    // every scan work group leaves its best kListLen candidates; several rows:
-    // the candidate lists are built from the score rows by a second launch
+    // append runs in the same launch and scores the block it completes.  Every
+    // scan work group leaves its best kListLen candidates per query row
     float *scores = scores_out ? scores_out : at<float>(ws, L.scores);
     const int32_t ld = scores_out ? (n_q > 1 ? ld_scores : 0) : (int32_t)L.ld;
     const CandLists cl = cand_lists(ws, L);
     int32_t n_lists = 0;
-    if (n_q == 1) {
-        HIP_CHECK(launch_score_decode(H(q_idx), 1, H(Lb->k_pool), ap.b_lo, (int32_t)row, scores,
-                                      ld, &ap, &cl, &n_lists, s));
-    } else {
-        HIP_CHECK(launch_score_decode(H(q_idx), n_q, H(Lb->k_pool), ap.b_lo, (int32_t)row, scores,
-                                      ld, &ap, nullptr, nullptr, s));
-        HIP_CHECK(launch_score_lists(scores, n_q, ld, n_before, cl, &n_lists, s));
-    }
+    HIP_CHECK(launch_score_decode(H(q_idx), n_q, H(Lb->k_pool), ap.b_lo, (int32_t)row, scores, ld,
+                                  &ap, &cl, &n_lists, s));
 
     if (flags == QSA_STEP_FUSED_GATHER) {
         // 3-5. top-k from the candidate lists and attention over the chosen
