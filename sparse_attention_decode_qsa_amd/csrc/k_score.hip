@@ -227,15 +227,26 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
 #pragma unroll
             for (int w = 0; w < NW; w++)
                 n += wrows[w];
+            uint64_t mine[NQ];
+            uint32_t rk[NQ];
 #pragma unroll
             for (int qi = 0; qi < NQ; qi++) {
-                const uint64_t me = wtop[qi][lane];
-                uint32_t rank = 0;
-#pragma unroll 8
-                for (int j = 0; j < NE; j += 2) {
+                mine[qi] = wtop[qi][lane];
+                rk[qi] = 0;
+            }
+            // the query rows' counts in one pass, so their LDS reads overlap
+#pragma unroll 4
+            for (int j = 0; j < NE; j += 2) {
+#pragma unroll
+                for (int qi = 0; qi < NQ; qi++) {
                     const uint64_t a0 = wtop[qi][j], a1 = wtop[qi][j + 1];
-                    rank += (a0 > me ? 1u : 0u) + (a1 > me ? 1u : 0u);
+                    rk[qi] += (a0 > mine[qi] ? 1u : 0u) + (a1 > mine[qi] ? 1u : 0u);
                 }
+            }
+#pragma unroll
+            for (int qi = 0; qi < NQ; qi++) {
+                const uint64_t me = mine[qi];
+                const uint32_t rank = rk[qi];
                 const bool pick = me != 0ull && rank < (uint32_t)kListLen;
                 const uint32_t npick = (uint32_t)__popcll(__ballot(pick));
                 const int64_t li = (int64_t)qi * kListWgs + blockIdx.x;
