@@ -68,6 +68,17 @@ __global__ __launch_bounds__(kUBThreads) void union_build_kernel(
 
     for (int32_t i = t; i < n_ent; i += kUBThreads)
         sm.msk[i] = 0u;
+    // this thread's chosen ids (entry e = t + j * kUBThreads is row e / k, slot
+    // e % k), loaded once; -1 where the entry is past the row's choices
+    constexpr int kPer = kUnionCap / kUBThreads;
+    int32_t myid[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+        const int32_t e = t + j * kUBThreads;
+        const int32_t i = e / k, sl = e - i * k;
+        const bool ok = e < n_ent && sl < min(k, (pos0 + r0 + i + 1) / kBlockTokens);
+        myid[j] = ok ? blk[(int64_t)(r0 + i) * ldb + sl] : -1;
+    }
     uint32_t base = 0;
     for (int32_t w0 = 0; w0 < nb_hi; w0 += kWinBlocks) {
         const int32_t nwb = min(kWinBlocks, nb_hi - w0);
@@ -75,14 +86,11 @@ __global__ __launch_bounds__(kUBThreads) void union_build_kernel(
         for (int32_t i = t; i < nw; i += kUBThreads)
             sm.bits[i] = 0u;
         __syncthreads();
-        for (int32_t e = t; e < n_ent; e += kUBThreads) {
-            const int32_t i = e / k, j = e - i * k;
-            const int32_t ns = min(k, (pos0 + r0 + i + 1) / kBlockTokens);
-            if (j < ns) {
-                const uint32_t id = (uint32_t)(blk[(int64_t)(r0 + i) * ldb + j] - w0);
-                if (id < (uint32_t)nwb)
-                    atomicOr(&sm.bits[id >> 5], 1u << (id & 31));
-            }
+#pragma unroll
+        for (int j = 0; j < kPer; j++) {
+            const uint32_t id = (uint32_t)(myid[j] - w0);
+            if (myid[j] >= 0 && id < (uint32_t)nwb)
+                atomicOr(&sm.bits[id >> 5], 1u << (id & 31));
         }
         __syncthreads();
         const int32_t per = (nw + kUBThreads - 1) / kUBThreads;
@@ -103,16 +111,14 @@ __global__ __launch_bounds__(kUBThreads) void union_build_kernel(
         if (t == kUBThreads - 1)
             sm.total = pos;
         __syncthreads();
-        for (int32_t e = t; e < n_ent; e += kUBThreads) {
-            const int32_t i = e / k, j = e - i * k;
-            const int32_t ns = min(k, (pos0 + r0 + i + 1) / kBlockTokens);
-            if (j < ns) {
-                const uint32_t id = (uint32_t)(blk[(int64_t)(r0 + i) * ldb + j] - w0);
-                if (id < (uint32_t)nwb) {
-                    const uint32_t w = id >> 5;
-                    const uint32_t p = sm.pre[w] + __popc(sm.bits[w] & ((1u << (id & 31)) - 1u));
-                    atomicOr(&sm.msk[p], 1u << i);
-                }
+#pragma unroll
+        for (int j = 0; j < kPer; j++) {
+            const uint32_t id = (uint32_t)(myid[j] - w0);
+            if (myid[j] >= 0 && id < (uint32_t)nwb) {
+                const int32_t row = (t + j * kUBThreads) / k;
+                const uint32_t w = id >> 5;
+                const uint32_t p = sm.pre[w] + __popc(sm.bits[w] & ((1u << (id & 31)) - 1u));
+                atomicOr(&sm.msk[p], 1u << row);
             }
         }
         base = sm.total;
