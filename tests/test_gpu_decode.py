@@ -412,6 +412,65 @@ def test_decode_step_clustered_scores(gpu, pattern):
     assert_attn_close(host(out), ref_out)
 
 
+@pytest.mark.parametrize("pattern", ["one_scan_group", "recent_window", "all_equal",
+                                     "few_values"])
+def test_decode_multi_clustered_scores(gpu, pattern):
+    # three rows with their own score orders over the same clustered blocks (query
+    # all ones, all minus ones, half the features): each row's candidate lists come
+    # from the same scan, and a row whose chosen blocks crowd one work group falls
+    # back alone; row 2 completes block nb0, which only it sees
+    nb0, H, d, n_q = 20000, 16, 128, 3
+    n_before = 4 * nb0 + 1
+    w = small(n_before + n_q)
+    cfg = cfg_of(w)
+    r = np.random.default_rng(100 + len(pattern))
+    v = clustered_values(pattern, nb0, r)
+    pooled = np.zeros((w.cap_tokens // 4, H, d), np.float16)
+    pooled[:nb0] = v[:, None, None]
+    raw = np.zeros((w.cap_tokens, H, d), np.float16)
+    raw[4 * nb0:n_before] = synth.normal_f16(70, (n_before - 4 * nb0, H, d))
+    K = synth.normal_f16(71, (w.cap_tokens, 4, 128))
+    V = synth.normal_f16(72, (w.cap_tokens, 4, 128))
+    K[n_before:] = 0
+    V[n_before:] = 0
+    half = np.ones((H, d), np.float16)
+    half[:, d // 2:] = 0
+    q_idx = np.stack([np.ones((H, d)), -np.ones((H, d)), half]).astype(np.float16)
+    mult = [2048.0, -2048.0, 1024.0]  # complete blocks score exactly mult * v
+    q = synth.normal_f16(73, (n_q, 32, 128))
+    k_idx_new = synth.normal_f16(74, (n_q, H, d))
+    k_new = synth.normal_f16(75, (n_q, 4, 128))
+    v_new = synth.normal_f16(76, (n_q, 4, 128))
+
+    g = qb.Layer(cfg)
+    g.k_pool.copy_(dev(pooled))
+    g.k_raw.copy_(dev(raw))
+    g.k_cache.copy_(dev(K))
+    g.v_cache.copy_(dev(V))
+    ld = nb0 + 8
+    out = torch.empty((n_q, 32, 128), device="cuda")
+    scores = torch.full((n_q, ld), 321.0, device="cuda")
+    blk = torch.full((n_q, 512), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, n_q, w.cap_tokens)
+    qb.qsa_decode_multi(cfg, g, n_before, dev(q_idx), dev(k_idx_new), dev(q), dev(k_new),
+                        dev(v_new), out, ws, scores_out=scores, ld_scores=ld, blk_out=blk)
+    s_all, b_all, o_all = host(scores), host(blk), host(out)
+    for row in range(n_q):
+        ref = O.decode_step(shape_of(w), raw, pooled, K, V, n_before + row, q_idx[row],
+                            k_idx_new[row], q[row], k_new[row], v_new[row])
+        nb = (n_before + row + 1) // 4
+        s_gpu = s_all[row][:nb]
+        assert np.array_equal(s_gpu[:nb0], mult[row] * v.astype(np.float32)), row
+        if nb > nb0:
+            assert abs(s_gpu[nb0] - ref["scores64"][nb0]) <= \
+                SCORE_REL * np.max(np.abs(ref["scores64"]))
+        b_gpu = b_all[row][:min(512, nb)]
+        assert np.array_equal(b_gpu, O.topk_sort(s_gpu, 512)), row
+        assert np.array_equal(b_gpu, ref["blk"]), row
+        ref_out = O.attn_cells(q[row], K, V, O.cells(b_gpu, n_before + row + 1), w.scale)
+        assert_attn_close(o_all[row], ref_out, f"row {row}")
+
+
 # ------------------------------------------------------------------ f3 multi-query decode
 @pytest.mark.parametrize("n_tokens,n_q", [(4 * 3000 + 1, 3), (4 * 3000 + 3, 3), (4 * 3000, 2),
                                           (4 * 3000 + 2, 4), (2049, 3), (6, 4)])
