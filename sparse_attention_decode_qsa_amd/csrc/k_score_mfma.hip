@@ -9,9 +9,11 @@
 // Tiling: a work group computes a 256 (queries) x 128 (blocks) tile; its 4
 // waves each own 128 x 64 (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).
 // Every 32-feature step stages A (16 KiB) and B (8 KiB) in LDS with rows padded
-// to 80 bytes (conflict-free 16-byte fragment reads); the next step's global
-// loads are issued before the current step's MFMAs.  Blocks at or past the
-// last row's causal bound are neither read nor written.
+// to 80 bytes (conflict-free 16-byte fragment reads).  Two LDS buffers and two
+// register sets: while step s is multiplied, step s + 1 waits in registers to be
+// stored into the other buffer and step s + 2's global loads are in flight, so a
+// load has two steps of MFMA work to arrive, and a step needs one barrier.
+// Blocks at or past the last row's causal bound are neither read nor written.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -23,14 +25,14 @@ constexpr int PITCH = TK + 8;  // halfs per LDS row (80 bytes)
 constexpr int WM = 128, WN = 64;
 constexpr int FI = WM / 16, FJ = WN / 16;
 
-__global__ __launch_bounds__(kThreads) void score_prefill_kernel(const h16 *__restrict__ Q,
+__global__ __launch_bounds__(kThreads, 2) void score_prefill_kernel(const h16 *__restrict__ Q,
                                                                  int32_t n_q, int32_t pos0,
                                                                  const h16 *__restrict__ P,
                                                                  int32_t K, float *__restrict__ S,
                                                                  int32_t ld)
 {
-    __shared__ __attribute__((aligned(16))) h16 As[TM * PITCH];
-    __shared__ __attribute__((aligned(16))) h16 Bs[TN * PITCH];
+    __shared__ __attribute__((aligned(16))) h16 As[2][TM * PITCH];
+    __shared__ __attribute__((aligned(16))) h16 Bs[2][TN * PITCH];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -40,8 +42,8 @@ __global__ __launch_bounds__(kThreads) void score_prefill_kernel(const h16 *__re
 
     // global -> register staging: A: 4 x 16B per thread, B: 2 x 16B per thread
     const int lr = t >> 2, lk = (t & 3) * 8;
-    h16x8 ga[4], gb[2];
-    auto gload = [&](int k0) {
+    h16x8 ga0[4], gb0[2], ga1[4], gb1[2];
+    auto gload = [&](h16x8 (&ga)[4], h16x8 (&gb)[2], int k0) {
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int32_t r = r0 + lr + 64 * j;
@@ -55,13 +57,13 @@ __global__ __launch_bounds__(kThreads) void score_prefill_kernel(const h16 *__re
                                  : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
     };
-    auto sstore = [&]() {
+    auto sstore = [&](const h16x8 (&ga)[4], const h16x8 (&gb)[2], h16 *as, h16 *bs) {
 #pragma unroll
         for (int j = 0; j < 4; j++)
-            *(h16x8 *)&As[(lr + 64 * j) * PITCH + lk] = ga[j];
+            *(h16x8 *)&as[(lr + 64 * j) * PITCH + lk] = ga[j];
 #pragma unroll
         for (int j = 0; j < 2; j++)
-            *(h16x8 *)&Bs[(lr + 64 * j) * PITCH + lk] = gb[j];
+            *(h16x8 *)&bs[(lr + 64 * j) * PITCH + lk] = gb[j];
     };
 
     f32x4 acc[FI][FJ];
@@ -72,25 +74,47 @@ __global__ __launch_bounds__(kThreads) void score_prefill_kernel(const h16 *__re
             acc[i][j] = f32x4{0, 0, 0, 0};
 
     const int fr = lane & 15, fk = (lane >> 4) * 8;
-    gload(0);
-    for (int k0 = 0; k0 < K; k0 += TK) {
-        __syncthreads();
-        sstore();
-        __syncthreads();
-        if (k0 + TK < K)
-            gload(k0 + TK);
+    auto mma = [&](const h16 *as, const h16 *bs) {
         h16x8 b[FJ];
 #pragma unroll
         for (int j = 0; j < FJ; j++)
-            b[j] = *(const h16x8 *)&Bs[(wn * WN + j * 16 + fr) * PITCH + fk];
+            b[j] = *(const h16x8 *)&bs[(wn * WN + j * 16 + fr) * PITCH + fk];
 #pragma unroll
         for (int i = 0; i < FI; i++) {
-            const h16x8 a = *(const h16x8 *)&As[(wm * WM + i * 16 + fr) * PITCH + fk];
+            const h16x8 a = *(const h16x8 *)&as[(wm * WM + i * 16 + fr) * PITCH + fk];
 #pragma unroll
             for (int j = 0; j < FJ; j++)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
         }
+    };
+
+    // step s is read from buffer s % 2; register set s % 2 carries step s (and
+    // later s + 2) from global memory to its buffer.  The loop runs over pairs of
+    // steps so that each register set has a fixed name.
+    const int nsteps = K / TK;
+    gload(ga0, gb0, 0);
+    if (nsteps > 1)
+        gload(ga1, gb1, TK);
+    sstore(ga0, gb0, As[0], Bs[0]);
+    __syncthreads();
+    if (nsteps > 2)
+        gload(ga0, gb0, 2 * TK);
+    int s0 = 0;
+    for (; s0 + 1 < nsteps; s0 += 2) {
+        mma(As[0], Bs[0]);
+        sstore(ga1, gb1, As[1], Bs[1]);
+        __syncthreads();
+        if (s0 + 3 < nsteps)
+            gload(ga1, gb1, (s0 + 3) * TK);
+        mma(As[1], Bs[1]);
+        if (s0 + 2 < nsteps)
+            sstore(ga0, gb0, As[0], Bs[0]);
+        __syncthreads();
+        if (s0 + 4 < nsteps)
+            gload(ga0, gb0, (s0 + 4) * TK);
     }
+    if (s0 < nsteps)  // an odd last step, already in buffer 0
+        mma(As[0], Bs[0]);
 
     // D layout: lane holds column (lane & 15), rows 4*(lane >> 4) + e
 #pragma unroll
