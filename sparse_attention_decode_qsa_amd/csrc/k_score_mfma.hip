@@ -6,9 +6,9 @@
 // exactly the per-lane operand layout of v_mfma_f32_16x16x32_f16: a lane holds
 // 8 consecutive features of one row of A and of one column of B.
 //
-// Tiling: a work group computes a 256 (queries) x 128 (blocks) tile; its 4
+// Tiling: a work group computes a 256 (queries) x 256 (blocks) tile; its 8
 // waves each own 128 x 64 (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).
-// Every 32-feature step stages A (16 KiB) and B (8 KiB) in LDS with rows padded
+// Every 32-feature step stages A (16 KiB) and B (16 KiB) in LDS with rows padded
 // to 80 bytes (conflict-free 16-byte fragment reads).  Two LDS buffers and two
 // register sets: while step s is multiplied, step s + 1 waits in registers to be
 // stored into the other buffer and step s + 2's global loads are in flight, so a
@@ -19,13 +19,13 @@
 namespace qsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int TM = 256, TN = 128, TK = 32;
+constexpr int kThreads = 512;
+constexpr int TM = 256, TN = 256, TK = 32;
 constexpr int PITCH = TK + 8;  // halfs per LDS row (80 bytes)
 constexpr int WM = 128, WN = 64;
 constexpr int FI = WM / 16, FJ = WN / 16;
 
-__global__ __launch_bounds__(kThreads, 2) void score_prefill_kernel(const h16 *__restrict__ Q,
+__global__ __launch_bounds__(kThreads, 1) void score_prefill_kernel(const h16 *__restrict__ Q,
                                                                  int32_t n_q, int32_t pos0,
                                                                  const h16 *__restrict__ P,
                                                                  int32_t K, float *__restrict__ S,
@@ -35,35 +35,35 @@ __global__ __launch_bounds__(kThreads, 2) void score_prefill_kernel(const h16 *_
     __shared__ __attribute__((aligned(16))) h16 Bs[2][TN * PITCH];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int32_t r0 = blockIdx.y * TM;
     const int32_t c0 = blockIdx.x * TN;
     const int32_t nb_max = (pos0 + n_q) / kBlockTokens;
 
-    // global -> register staging: A: 4 x 16B per thread, B: 2 x 16B per thread
+    // global -> register staging: A: 2 x 16B per thread, B: 2 x 16B per thread
     const int lr = t >> 2, lk = (t & 3) * 8;
-    h16x8 ga0[4], gb0[2], ga1[4], gb1[2];
-    auto gload = [&](h16x8 (&ga)[4], h16x8 (&gb)[2], int k0) {
+    h16x8 ga0[2], gb0[2], ga1[2], gb1[2];
+    auto gload = [&](h16x8 (&ga)[2], h16x8 (&gb)[2], int k0) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int32_t r = r0 + lr + 64 * j;
+        for (int j = 0; j < 2; j++) {
+            const int32_t r = r0 + lr + 128 * j;
             ga[j] = (r < n_q) ? *(const h16x8 *)(Q + (int64_t)r * K + k0 + lk)
                               : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const int32_t c = c0 + lr + 64 * j;
+            const int32_t c = c0 + lr + 128 * j;
             gb[j] = (c < nb_max) ? *(const h16x8 *)(P + (int64_t)c * K + k0 + lk)
                                  : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
     };
-    auto sstore = [&](const h16x8 (&ga)[4], const h16x8 (&gb)[2], h16 *as, h16 *bs) {
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            *(h16x8 *)&as[(lr + 64 * j) * PITCH + lk] = ga[j];
+    auto sstore = [&](const h16x8 (&ga)[2], const h16x8 (&gb)[2], h16 *as, h16 *bs) {
 #pragma unroll
         for (int j = 0; j < 2; j++)
-            *(h16x8 *)&bs[(lr + 64 * j) * PITCH + lk] = gb[j];
+            *(h16x8 *)&as[(lr + 128 * j) * PITCH + lk] = ga[j];
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+            *(h16x8 *)&bs[(lr + 128 * j) * PITCH + lk] = gb[j];
     };
 
     f32x4 acc[FI][FJ];
