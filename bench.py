@@ -446,7 +446,9 @@ def cpu_baseline_prefill(w, I, budget_s):
             break
     return dict(value=rows / el, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{rows} oracle prefill rows of the chunk (positions depth+r), single "
-                       f"thread, {el:.1f} s")
+                       f"thread, {el:.1f} s",
+                measured_rows=rows,
+                extrapolated_chunk_s=round(w.n_q * el / rows, 1))
 
 
 def bench_mla(args):
@@ -555,7 +557,23 @@ def main():
         res = bench_mla(args)
     else:
         res = bench_decode(args)
+    if "cpu_baseline" in res:
+        res["cpu_baseline"].update(host_cpu())
     print(json.dumps(res), flush=True)
+
+
+def host_cpu() -> dict:
+    """The host the oracle ran on: CPU model and logical core count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_logical_cores": os.cpu_count()}
 
 
 if __name__ == "__main__":

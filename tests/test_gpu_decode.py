@@ -332,10 +332,12 @@ def test_decode_step_small_contexts(gpu):
         check_step(w, L, cfg, g, o, L["n_prefix"], 0, qb.QSA_STEP_FUSED_GATHER)
 
 
-def test_decode_step_255181_planted(gpu):
-    # the 256k workload, one layer: planted blocks are chosen, full parity
+@pytest.mark.parametrize("layer", [0, 7])
+def test_decode_step_255181_planted(gpu, layer):
+    # the 256k workload, layer 0 and one other seeded layer: planted blocks are
+    # chosen, full parity
     w = synth.WORKLOADS["decode_255181"]
-    L, cfg, g, o = setup_decode(w)
+    L, cfg, g, o = setup_decode(w, layer)
     n0 = L["n_prefix"]
     # pooled cache built by the library vs the oracle, on 2000 sampled rows
     rows = np.sort(np.random.default_rng(1).choice(n0 // 4, 2000, replace=False))
