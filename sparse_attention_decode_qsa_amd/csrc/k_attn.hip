@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
             o[hh][j] = 0.f;
     }
     const float sl2 = a.scale * kLog2e;
-    const int64_t kg = (int64_t)g * D, vg = (int64_t)g * DV;
+    const int64_t kg = a.kv_shared ? 0 : (int64_t)g * D, vg = a.kv_shared ? 0 : (int64_t)g * DV;
     // QK: wave w takes cells 16w .. 16w+15 of the chunk; the 4 lanes of a quad
     // split one cell's head dim in quarters, so their partial dots meet in-quad
     const int cl = wave * 16 + (lane >> 2);

@@ -16,7 +16,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kPerWave = kListSeg / kWaves;  // 1024 positions: 16 ballots per wave
+constexpr int kPerWave = kListSeg / kWaves;  // 256 positions: 4 ballots per wave
 constexpr uint16_t kNegInf = 0xFC00u;
 
 __device__ __forceinline__ bool visible(const h16 *mask, int32_t n, int64_t j)

@@ -761,7 +761,7 @@ size_t qsa_mla_workspace_size(int32_t hq, int32_t dv, int32_t list_cap)
     if (hq < 1 || dv < 1 || list_cap < 1)
         return 0;
     const size_t splits = ((size_t)list_cap + kAttnChunk - 1) / kAttnChunk;
-    size_t off = round_up(sizeof(uint32_t) * 2048, 256);    // segment counts
+    size_t off = round_up(sizeof(uint32_t) * kListSegMax, 256);  // segment counts
     off += round_up(sizeof(int32_t) * (size_t)list_cap, 256);  // list
     off += round_up(sizeof(float) * (size_t)hq * splits * (size_t)(dv + 2), 256);
     return off;
@@ -782,7 +782,7 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
         return fail(QSA_ERR_UNSUPPORTED, "qsa_mla_sparse_attn: implemented for dkq=576, dv=512");
     if (!pow2(hq) || hq > 16)
         return fail(QSA_ERR_UNSUPPORTED, "qsa_mla_sparse_attn: hq must be 1, 2, 4, 8 or 16");
-    if ((int64_t)n > (int64_t)kListSeg * 2048)
+    if ((int64_t)n > (int64_t)kListSeg * kListSegMax)
         return fail(QSA_ERR_UNSUPPORTED, "qsa_mla_sparse_attn: n too large");
     if (!isfinite(scale))
         return fail(QSA_ERR_INVALID, "qsa_mla_sparse_attn: scale is not finite");
@@ -801,7 +801,7 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
     uint32_t *seg_cnt = (uint32_t *)w;
-    int32_t *list = (int32_t *)(w + round_up(sizeof(uint32_t) * 2048, 256));
+    int32_t *list = (int32_t *)(w + round_up(sizeof(uint32_t) * kListSegMax, 256));
     float *part = (float *)((char *)list + round_up(sizeof(int32_t) * (size_t)list_cap, 256));
     if (list_out)
         list = list_out;
@@ -813,8 +813,11 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
     a.vbase = v ? H(v) : H(kv);
     a.k_tok = dkq;
     a.v_tok = v ? dv : dkq;
+    // one latent KV head: its query heads go in groups of up to 4 to separate work
+    // groups, which read the same rows (more work groups for a latency-bound call)
     a.hq = hq;
-    a.hkv = 1;
+    a.hkv = hq > 4 ? hq / 4 : 1;
+    a.kv_shared = 1;
     a.mode = kCellsList;
     a.list = list;
     a.n_list = n_list;

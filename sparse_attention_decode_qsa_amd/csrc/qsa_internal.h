@@ -113,6 +113,8 @@ struct AttnArgs {
     float *out;             // [rows][hq][dv]
     int32_t rows;
     int32_t tok_bound;      // list: tokens must be < tok_bound (the mask length)
+    int32_t kv_shared;      // 1: every KV-head group reads the same K/V rows (one latent
+                            // head, its query heads split into hkv groups)
 };
 hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s);
 // Merge of split-K partials [rows][hq][splits][dv + 2] into out [rows][hq][dv].
@@ -171,7 +173,8 @@ int32_t union_splits(int32_t n_q, int32_t hq, int32_t hkv);
 hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s);
 
 // ---- MLA list (k_mla.hip) ---------------------------------------------------
-constexpr int kListSeg = 4096;  // positions per list-building work group
+constexpr int kListSeg = 1024;     // positions per list-building work group
+constexpr int kListSegMax = 8192;  // segments: masks of up to 8,388,608 positions
 hipError_t launch_mask_list(const h16 *mask, int32_t n, int32_t list_cap, uint32_t *seg_cnt,
                             int32_t *list, int32_t *n_list, hipStream_t s);
 

@@ -193,14 +193,14 @@ def correlated_rows(z: np.ndarray, rho: float) -> np.ndarray:
     return x.astype(np.float16)
 
 
-def mla_inputs(w: Workload, runs: bool = False) -> dict:
+def mla_inputs(w: Workload, runs: bool = False, layer: int = 0) -> dict:
     """Latent KV rows [n, dkq], queries [hq, dkq] and an additive binary16 mask
     (0 visible, -inf hidden) with list_len visible positions: uniform distinct
     positions, or (runs=True) list_len/4 distinct 4-aligned runs of 4."""
     assert w.kind == "mla"
-    kv = normal_f16(seed_for(w.cid, 0, T_K), (w.n_tokens, w.d))
-    q = normal_f16(seed_for(w.cid, 0, T_Q), (w.hq, w.d))
-    r = rng(seed_for(w.cid, 0, T_PLANT) + (1 if runs else 0))
+    kv = normal_f16(seed_for(w.cid, layer, T_K), (w.n_tokens, w.d))
+    q = normal_f16(seed_for(w.cid, layer, T_Q), (w.hq, w.d))
+    r = rng(seed_for(w.cid, layer, T_PLANT) + (1 if runs else 0))
     if runs:
         starts = r.choice(w.n_tokens // 4, size=w.list_len // 4, replace=False) * 4
         pos = (starts[:, None] + np.arange(4)[None]).ravel()
