@@ -69,15 +69,19 @@ __global__ __launch_bounds__(kUBThreads) void union_build_kernel(
     for (int32_t i = t; i < n_ent; i += kUBThreads)
         sm.msk[i] = 0u;
     // this thread's chosen ids (entry e = t + j * kUBThreads is row e / k, slot
-    // e % k), loaded once; -1 where the entry is past the row's choices
+    // e % k), loaded once; -1 where the entry is past the row's choices, and for an
+    // id outside the row's [0, nb_r) (only a broken selection has one: dropped, as
+    // the per-row attention drops it, so no row reaches past its own prefix)
     constexpr int kPer = kUnionCap / kUBThreads;
     int32_t myid[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
         const int32_t e = t + j * kUBThreads;
         const int32_t i = e / k, sl = e - i * k;
-        const bool ok = e < n_ent && sl < min(k, (pos0 + r0 + i + 1) / kBlockTokens);
-        myid[j] = ok ? blk[(int64_t)(r0 + i) * ldb + sl] : -1;
+        const int32_t nb_r = (pos0 + r0 + i + 1) / kBlockTokens;
+        const bool ok = e < n_ent && sl < min(k, nb_r);
+        const int32_t id = ok ? blk[(int64_t)(r0 + i) * ldb + sl] : -1;
+        myid[j] = (id >= 0 && id < nb_r) ? id : -1;
     }
     uint32_t base = 0;
     for (int32_t w0 = 0; w0 < nb_hi; w0 += kWinBlocks) {

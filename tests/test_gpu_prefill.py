@@ -261,6 +261,41 @@ def test_prefill_attn_union_past_one_bitmap_window(gpu):
     union_direct(8, 1, 512, 4 * ((1 << 18) + (1 << 16)) + 1001, 18, 90, shared=0.25)
 
 
+def test_prefill_attn_broken_ids_are_dropped(gpu):
+    # ids outside a row's [0, nb_r) (only a broken selection has them) are dropped by
+    # both forms, so no row reaches past its own prefix: both equal the oracle on
+    # the valid ids
+    hq, hkv, k, pos0, n_q, d = 32, 4, 64, 4001, 20, 128
+    n_all = pos0 + n_q
+    cap = (n_all + 64) // 4 * 4
+    cfg = qb.Config(topk_blocks=k, hq=hq, hkv=hkv, d=d, dv=d, cap_tokens=cap)
+    K = synth.normal_f16(95, (n_all, hkv, d))
+    V = synth.normal_f16(96, (n_all, hkv, d))
+    Q = synth.normal_f16(97, (n_q, hq, d))
+    r = np.random.default_rng(95)
+    B = np.zeros((n_q, k), np.int32)
+    valid = []
+    for i in range(n_q):
+        nb = (pos0 + i + 1) // 4
+        ids = np.sort(r.choice(nb, size=k, replace=False)).astype(np.int32)
+        ids[-1] = nb + 2 if i % 2 == 0 else -3   # past the prefix / negative
+        ids[-2] = nb                              # the first block the row cannot see
+        B[i] = ids
+        valid.append(ids[(ids >= 0) & (ids < nb)])
+    kc = torch.zeros((cap, hkv, d), dtype=torch.float16, device="cuda")
+    vc = torch.zeros((cap, hkv, d), dtype=torch.float16, device="cuda")
+    kc[:n_all], vc[:n_all] = dev(K), dev(V)
+    ws = qb.workspace(cfg, n_q, n_all)
+    scale = 1.0 / np.sqrt(d)
+    for flags in (qb.QSA_PREFILL_PER_ROW, UNION):
+        out = torch.full((n_q, hq, d), 5.0, device="cuda")
+        qb.qsa_prefill_attn(cfg, dev(Q), pos0, dev(B), k, kc, vc, out, ws, flags=flags)
+        got = host(out)
+        for i in range(n_q):
+            ref = O.attn_cells(Q[i], K, V, O.cells(np.sort(valid[i]), pos0 + i + 1), scale)
+            assert_attn_close(got[i], ref, f"flags {flags} row {i}")
+
+
 def test_prefill_attn_union_no_overlap(gpu):
     # rows with disjoint choices: the union holds rows x k blocks
     union_direct(32, 4, 64, 40000, 16, 91, shared=0.0)
