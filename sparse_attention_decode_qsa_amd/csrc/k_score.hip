@@ -31,6 +31,19 @@ namespace {
 constexpr int kThreads = 256;   // stand-alone scan
 constexpr int kStepThreads = 512;  // decode-step scan: 8 waves, so one list per 8 waves
 
+// Sum of a row's lane partials: a whole-wave row by DPP within the 16-lane rows
+// and the four row totals added in a fixed order (no LDS permutes); narrower rows
+// by a butterfly within their lane group.  Every lane of the row gets the same
+// value, and the scan and the appended row use this same order.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float a)
+{
+    if constexpr (LPR == kWave)
+        return wave_sum(a);
+    else
+        return group_sum<LPR>(a);
+}
+
 // Score of one row held in LDS, by one wave, in the scan's lane order; lane 0
 // returns it.
 template <int ROWC>
@@ -44,7 +57,7 @@ __device__ __forceinline__ float score_row_lds(const h16 *q, const h16 *row)
 #pragma unroll
     for (int j = 0; j < CPL; j++)
         acc = dot8(((const h16x8 *)q)[sub + LPR * j], ((const h16x8 *)row)[sub + LPR * j], acc);
-    return group_sum<LPR>(acc);
+    return row_sum<LPR>(acc);
 }
 
 // A wave's candidate lists live across its lanes: lane 8 g + i holds entry i of
@@ -173,7 +186,7 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
 #pragma unroll
                 for (int j = 0; j < CPL; j++)
                     a = dot8(qv[qi][j], kv[u][j], a);
-                a = group_sum<LPR>(a);
+                a = row_sum<LPR>(a);
                 if (sub == 0 && r[u] < nb)
                     scores[(int64_t)qi * ld + r[u]] = a;
                 acc[qi] = a;
@@ -185,8 +198,8 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
                 for (int rs = 0; rs < RPW; rs++) {
                     const int64_t rr = (g0 + (int64_t)u * tw) * RPW + rs;
                     if (rr < nb) {
-                        // one row per wave: the butterfly sum left every query's
-                        // score in every lane; otherwise read it from the row's lanes
+                        // one row per wave: the row sum left every query's score in
+                        // every lane; otherwise read it from the row's lanes
                         float sc = 0.f;
 #pragma unroll
                         for (int qi = 0; qi < NQ; qi++) {
