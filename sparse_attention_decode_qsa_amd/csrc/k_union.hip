@@ -365,8 +365,7 @@ __global__ __launch_bounds__(kSetThreads * SETS, 3 - SETS) void union_attn_kerne
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     tmax = fmaxf(tmax, s[mb][e]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            tmax = max_across_rows(tmax);
             // scores are scaled inside the exponent: p = 2^(s * sl2 - m)
             const float mnew = fmaxf(m_run[nb], tmax * sl2);
             const float mref = (mnew == -INFINITY) ? 0.f : mnew;

@@ -117,6 +117,18 @@ __device__ __forceinline__ float wave_sum(float x)
     return (a + b) + (c + d);
 }
 
+// Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the matching lanes of the four
+// 16-lane rows), every such lane gets it: the gfx950 row swaps leave a lane's own
+// value and its partner's (16, then 32 lanes away) in the two results, so the
+// maximum of the pair is the same whichever result holds which.
+__device__ __forceinline__ float max_across_rows(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Minimum / maximum of a uint32 over the 64 lanes (every lane gets it).
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x)
 {
