@@ -128,17 +128,11 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
             mine += ((uint32_t)(4 * ((j / 4) * NT + tt) + j % 4) < nb && bin_of(j) >= L) ? 1u : 0u;
     }
     {
-        uint32_t incl = mine;  // inclusive scan over the wave
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const uint32_t u = __shfl_up(incl, o, kWave);
-            if ((t & (kWave - 1)) >= o)
-                incl += u;
-        }
+        const uint32_t incl = wave_incl_scan(mine);  // inclusive scan over the wave (DPP)
         uint32_t base = 0;
         if ((t & (kWave - 1)) == kWave - 1 && incl)
             base = atomicAdd(&S.cnt, incl);
-        base = __shfl(base, kWave - 1, kWave) + incl - mine;
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, kWave - 1) + incl - mine;
         if (mine) {
 #pragma unroll
             for (int j = 0; j < KPT / 2; j++)
