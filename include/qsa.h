@@ -210,9 +210,13 @@ int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint16_t *k_
  * stream the union of their chosen blocks and their tails once, on the matrix
  * cores, with a per-row mask so that every row attends to exactly its own cells;
  * the output equals the per-row form up to fp32 summation order and binary16
- * rounding of the softmax weights).  The union form needs hq/hkv in {4, 8, 16},
- * d = dv = 128 and (128 / (hq/hkv)) * topk_blocks <= 16384 (else
- * QSA_ERR_UNSUPPORTED) and a workspace of qsa_workspace_size(cfg, n_q, pos0 + n_q).
+ * rounding of the softmax weights; on an MI355X, for 1,024 rows at depth 126,253,
+ * it takes 0.15 ms when neighbouring rows share most of their blocks and 0.78 ms
+ * when they share almost none, against 0.92-0.94 ms per row).  The union form
+ * needs hq/hkv in {4, 8, 16}, d = dv = 128 and (128 / (hq/hkv)) * topk_blocks <=
+ * 16384 (else QSA_ERR_UNSUPPORTED) and a workspace of
+ * qsa_workspace_size(cfg, n_q, pos0 + n_q).  Both forms drop a chosen id outside
+ * the row's [0, nb_r).
  */
 int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int32_t pos0,
                      const int32_t *blk, int32_t ldb, const uint16_t *k_cache,
