@@ -57,6 +57,26 @@ def test_incremental_append_is_bitwise_chunk_append(gpu):
     assert np.array_equal(pa, host(c.k_pool).view(np.uint16))
 
 
+@pytest.mark.parametrize("hkv,d,dv,n_before,n_new", [(4, 128, 128, 0, 1), (4, 128, 128, 1003, 37),
+                                                     (1, 64, 64, 4000, 96), (2, 64, 64, 17, 1)])
+def test_kv_append_is_an_exact_copy(gpu, hkv, d, dv, n_before, n_new):
+    # byte work: the new rows land bit for bit at [n_before, n_before + n_new); every
+    # other row keeps its contents
+    cap = 4160
+    cfg = qb.Config(hq=hkv * 8, hkv=hkv, d=d, dv=dv, cap_tokens=cap)
+    k_new = synth.normal_f16(120 + n_new, (n_new, hkv, d))
+    v_new = synth.normal_f16(121 + n_new, (n_new, hkv, dv))
+    kc0 = synth.normal_f16(122, (cap, hkv, d))
+    vc0 = synth.normal_f16(123, (cap, hkv, dv))
+    kc, vc = dev(kc0), dev(vc0)
+    qb.qsa_kv_append(cfg, dev(k_new), dev(v_new), n_before, kc, vc)
+    ek, ev = kc0.copy(), vc0.copy()
+    ek[n_before:n_before + n_new] = k_new
+    ev[n_before:n_before + n_new] = v_new
+    assert np.array_equal(host(kc).view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(host(vc).view(np.uint16), ev.view(np.uint16))
+
+
 # ------------------------------------------------------------------ cache lifecycle
 def test_pool_rebuild_after_state_load_and_edit(gpu):
     # a state load (only the raw keys restored) and a sequence edit from token t on:
