@@ -401,7 +401,8 @@ def bench_prefill(args):
          "attention_form": "per-row" if args.per_row else "grouped union"},
         {"bound": "mfma", "kernel": "score_prefill_kernel", "achieved": round(tflops, 2),
          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-         "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+         "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+         "traffic": traffic_for("score_prefill_kernel", "k_score_mfma.hip"),
          "algorithmic_flop_per_launch": flop, "avg_launch_us": round(score_us, 2)})
     res["stages_us"] = {"step": round(step_us, 2), "score": round(score_us, 2),
                         "topk": round(topk_us, 2), "attn": round(attn_us, 2),
