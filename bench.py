@@ -240,7 +240,8 @@ def bench_decode(args):
     step_gbps = step_bytes / step_s / 1e9
 
     res = {
-        "metric": METRIC,
+        "metric": METRIC if w.n_tokens == 255181 else
+        METRIC.replace("at 256k ctx", f"at {w.n_tokens:,}-token ctx"),
         "value": round(layer_steps_s, 2),
         "unit": "layer-steps/s",
         "n_gpus": 1,
@@ -277,7 +278,8 @@ def bench_decode(args):
         },
     }
     if rows > 1:
-        res["metric"] = f"QSA layer verification steps/s ({rows} query rows) at 256k ctx"
+        res["metric"] = (f"QSA layer verification steps/s ({rows} query rows) at "
+                         + ("256k ctx" if w.n_tokens == 255181 else f"{w.n_tokens:,}-token ctx"))
         res["unit"] = "layer-verify-steps/s"
         res["config"]["rows"] = rows
         res["config"]["step"] = (f"one verification step = all layers, serially, each appending "
@@ -534,7 +536,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_255181",
-                    choices=["decode_255181", "decode_61789", "tiny_decode_4k",
+                    choices=["decode_255181", "decode_126253", "decode_61789", "tiny_decode_4k",
                              "prefill_1024_at_126253", "prefill_1024_at_126253_corr",
                              "mla_list_262144"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")

@@ -330,10 +330,13 @@ def test_decode_step_tiny_workload(gpu, flags):
     assert_pool_close(host(g.k_pool[1023]), o.pooled[1023])
 
 
-@pytest.mark.parametrize("flags", [qb.QSA_STEP_FUSED_GATHER, qb.QSA_STEP_COMPACT_GATHER])
-def test_decode_step_cycle_61789(gpu, flags):
-    # the 64k workload, 4 consecutive steps: tails 1, 2, 3, then a completed block
-    w = synth.WORKLOADS["decode_61789"]
+@pytest.mark.parametrize("name,flags", [("decode_61789", qb.QSA_STEP_FUSED_GATHER),
+                                        ("decode_61789", qb.QSA_STEP_COMPACT_GATHER),
+                                        ("decode_126253", qb.QSA_STEP_FUSED_GATHER)])
+def test_decode_step_cycle(gpu, name, flags):
+    # the 64k and 128k workloads, 4 consecutive steps: the tail lengths of the cycle
+    # and a completed block
+    w = synth.WORKLOADS[name]
     L, cfg, g, o = setup_decode(w)
     n0 = L["n_prefix"]
     for step in range(4):
