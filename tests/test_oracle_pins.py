@@ -51,7 +51,8 @@ def test_f16_encode_matches_numpy_rne():
                      np.inf, -np.inf])
     x = np.concatenate([x, mids, -mids, edge])
     ours = O.d2h(x).view(np.uint16)
-    ref = x.astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):  # the overflow edges are the point
+        ref = x.astype(np.float16).view(np.uint16)
     assert np.array_equal(ours, ref)
     assert np.isnan(O.d2h(np.array([np.nan])).astype(np.float64)[0])
 
