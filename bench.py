@@ -536,7 +536,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_255181",
-                    choices=["decode_255181", "decode_126253", "decode_61789", "tiny_decode_4k",
+                    choices=["decode_255181", "decode_126253", "decode_61789", "decode_31898",
+                             "tiny_decode_4k",
                              "prefill_1024_at_126253", "prefill_1024_at_126253_corr",
                              "mla_list_262144"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")

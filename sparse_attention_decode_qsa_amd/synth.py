@@ -113,6 +113,8 @@ WORKLOADS = {
                                hq=8, hkv=1, d=128, dv=128),
     "decode_61789": Workload("decode_61789", 2, "decode", 61789, n_layers=12),
     "decode_126253": Workload("decode_126253", 8, "decode", 126253, n_layers=12),
+    # one rank's share of the 255,181 context split over 8 GPUs
+    "decode_31898": Workload("decode_31898", 9, "decode", 31898, n_layers=12),
     "decode_255181": Workload("decode_255181", 3, "decode", 255181, n_layers=12, planted=8),
     "prefill_1024_at_126253": Workload("prefill_1024_at_126253", 4, "prefill", 126253, n_q=1024),
     # the same caches, with indexer queries that drift slowly from row to row
