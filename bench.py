@@ -57,10 +57,11 @@ def src_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, source: str):
-    """Counter-measured HBM bytes per launch, only if taken on the current source."""
+def traffic_for(kernel: str, source: str, workload: str):
+    """Counter-measured HBM bytes per launch, only if taken on this workload and on
+    the current source."""
     try:
-        t = json.load(open(TRAFFIC_FILE))[kernel]
+        t = json.load(open(TRAFFIC_FILE))[kernel][workload]
     except (OSError, KeyError, ValueError):
         return None
     if t.get("source_hash") != src_hash(source):
@@ -222,7 +223,7 @@ def bench_decode(args):
     row = w.h_idx * w.d_idx * 2
     scan_bytes = nb * row
     achieved = scan_bytes / (kern_us * 1e-6) / 1e9
-    traffic = traffic_for("score_decode_kernel", "k_score.hip")
+    traffic = traffic_for("score_decode_kernel", "k_score.hip", w.name)
 
     # whole-step algorithmic bandwidth, averaged over the 4-step position cycle
     per = []
@@ -404,7 +405,7 @@ def bench_prefill(args):
         {"bound": "mfma", "kernel": "score_prefill_kernel", "achieved": round(tflops, 2),
          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
          "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-         "traffic": traffic_for("score_prefill_kernel", "k_score_mfma.hip"),
+         "traffic": traffic_for("score_prefill_kernel", "k_score_mfma.hip", w.name),
          "algorithmic_flop_per_launch": flop, "avg_launch_us": round(score_us, 2)})
     res["stages_us"] = {"step": round(step_us, 2), "score": round(score_us, 2),
                         "topk": round(topk_us, 2), "attn": round(attn_us, 2),

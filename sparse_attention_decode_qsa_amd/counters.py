@@ -4,13 +4,15 @@
         --fetch K_FETCH.csv --write K_WRITE.csv \
         --calib-fetch C_FETCH.csv --calib-write C_WRITE.csv --calib-mib 256 \
         --kernel <substring of the mangled name> --key score_decode_kernel \
-        [--json profiles/traffic.json]
+        --workload decode_255181 [--json profiles/traffic.json]
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch; each counter in a run of its own)
 are averaged over the dispatches whose kernel name contains --kernel.  The
 calibration runs (bench.py --calib-copy-mib N: a device-to-device copy of N MiB,
 nothing else) give the scale factor per counter: the bytes the copy must read
-(or write) / what the counter reports for the copy dispatches.
+(or write) / what the counter reports for the copy dispatches.  The JSON file
+holds one entry per (key, workload): a figure is valid only for the workload it
+was taken on.
 """
 from __future__ import annotations
 
@@ -56,11 +58,12 @@ def main():
     ap.add_argument("--calib-mib", type=int, default=256)
     ap.add_argument("--kernel", required=True)
     ap.add_argument("--key", required=True)
+    ap.add_argument("--workload", required=True, help="the bench.py workload the runs used")
     ap.add_argument("--source", default="k_score.hip")
     ap.add_argument("--json", default=None)
     a = ap.parse_args()
     cb = float(a.calib_mib << 20)
-    out = {"source_hash": src_hash(a.source), "kernel_match": a.kernel}
+    out = {"workload": a.workload, "source_hash": src_hash(a.source), "kernel_match": a.kernel}
     total = 0.0
     for name, kpath, cpath, counter in (("fetch", a.fetch, a.calib_fetch, "FETCH_SIZE"),
                                         ("write", a.write, a.calib_write, "WRITE_SIZE")):
@@ -75,7 +78,7 @@ def main():
     print(json.dumps(out, indent=1))
     if a.json:
         d = json.load(open(a.json)) if os.path.exists(a.json) else {}
-        d[a.key] = out
+        d.setdefault(a.key, {})[a.workload] = out
         with open(a.json, "w") as f:
             json.dump(d, f, indent=1)
 
