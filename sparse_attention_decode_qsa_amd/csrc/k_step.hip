@@ -66,7 +66,7 @@ struct alignas(16) TailLds {
     alignas(16) h16 qs[G * D];
     alignas(16) int32_t ids[kMaxTopk];
     alignas(16) int32_t toks[kMaxChunks * kAttnChunk];
-    uint32_t wsum[kNT / kWave];
+    alignas(16) uint32_t wsum[kNT / kWave];
 };
 
 // Sum over aligned groups of W lanes (W = 8 or 16) by DPP within 16-lane rows.
@@ -115,7 +115,14 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
     cl.rows += (int64_t)row * kListWgs;
     const int32_t b_lo = c_lo / kBlockTokens;  // its chosen-block positions
     const int32_t b_hi = b_lo + chunks * kAttnChunk / kBlockTokens;
+    const bool from_lists = nb > a.k;  // else every complete block is chosen
 
+    // candidate list t, issued before the query loads so that the two round
+    // trips overlap
+    uint64_t R[kListLen];
+    uint32_t nrows = 0;
+    if (from_lists)
+        load_list(cl, a.n_lists, R, &nrows);
     // the query rows of this KV head (independent of the selection)
     const h16 *qrow = a.q + ((int64_t)row * a.hq + (int64_t)g * G) * D;
     for (int i = t; i < G * D / 8; i += kNT)
@@ -127,6 +134,9 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
                          ? kBlockTokens * nb + (c - kBlockTokens * nsel)
                          : -1;
     }
+    // the selection's first stage shares this barrier
+    if (from_lists)
+        lists_prepare(R, nrows, t < a.n_lists, sm.L);
     __syncthreads();
     // the chosen blocks; position i goes to cells 4i .. 4i + 3
     auto place = [&](int32_t pos, int32_t id) {
@@ -140,18 +150,15 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
     // ---- 1. selection
     const bool want_blk = a.blk_out && blockIdx.x == 0 && blockIdx.y == 0;
     int32_t *blk_out = a.blk_out ? a.blk_out + (int64_t)row * a.k : nullptr;
-    if (nb <= a.k) {
+    if (!from_lists) {
         for (int32_t i = t; i < nb; i += kNT) {
             place(i, i);
             if (want_blk)
                 sm.ids[i] = i;
         }
     } else {
-        uint64_t R[kListLen];
-        uint32_t nrows;
-        load_list(cl, a.n_lists, R, &nrows);
         uint64_t rs = 0;
-        if (lists_select(R, nrows, t < a.n_lists, (uint32_t)a.k, sm.L, &rs)) {
+        if (lists_select_rest(R, (uint32_t)a.k, sm.L, &rs)) {
             uint32_t c = 0;
 #pragma unroll
             for (int j = 0; j < kListLen; j++)
@@ -163,8 +170,12 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
                 sm.wsum[wave] = incl;
             __syncthreads();
             uint32_t pos = incl - c;
-            for (int i = 0; i < wave; i++)
-                pos += sm.wsum[i];
+#pragma unroll
+            for (int i = 0; i < kNT / kWave; i += 4) {
+                const uint4 v = *(const uint4 *)&sm.wsum[i];
+                pos += (i < wave ? v.x : 0u) + (i + 1 < wave ? v.y : 0u) +
+                       (i + 2 < wave ? v.z : 0u) + (i + 3 < wave ? v.w : 0u);
+            }
 #pragma unroll
             for (int j = 0; j < kListLen; j++)
                 if (R[j] >= rs) {

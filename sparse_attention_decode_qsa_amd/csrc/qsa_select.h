@@ -371,18 +371,19 @@ struct alignas(16) ListSelLds {
     Scratch<kSelThreads> S;
     uint32_t wtot[kSelThreads / kWave];
     uint64_t wlast[kSelThreads / kWave];
-    uint32_t wkey[2][kSelThreads / kWave];
+    alignas(16) uint32_t wkey[2][kSelThreads / kWave];
     uint64_t rstar;
     uint32_t hidden;
 };
 
-// All kSelThreads threads call it; on true, *rs = R*.  Leaves L.hist cleared.
-__device__ bool lists_select(const uint64_t (&R)[kListLen], uint32_t nrows, bool has_list,
-                             uint32_t k, ListSelLds &L, uint64_t *rs)
+// The part of the selection before its first barrier: clears the histograms and
+// writes each wave's key range and largest full-list minimum.  All kSelThreads
+// threads call it; a barrier must follow before lists_select_rest.
+__device__ void lists_prepare(const uint64_t (&R)[kListLen], uint32_t nrows, bool has_list,
+                              ListSelLds &L)
 {
-    constexpr int NT = kSelThreads;
     const int t = threadIdx.x;
-    Scratch<NT> &S = L.S;
+    Scratch<kSelThreads> &S = L.S;
     ((uint4 *)L.hist[0])[t] = uint4{0, 0, 0, 0};
     ((uint4 *)L.hist[1])[t] = uint4{0, 0, 0, 0};
     if (t == 0)
@@ -412,7 +413,16 @@ __device__ bool lists_select(const uint64_t (&R)[kListLen], uint32_t nrows, bool
             L.wkey[1][t / kWave] = kmax;
         }
     }
-    __syncthreads();
+}
+
+// The rest of the selection, after lists_prepare and a barrier.  All kSelThreads
+// threads call it with the same R; on true, *rs = R*.  Leaves L.hist cleared.
+__device__ bool lists_select_rest(const uint64_t (&R)[kListLen], uint32_t k, ListSelLds &L,
+                                  uint64_t *rs)
+{
+    constexpr int NT = kSelThreads;
+    const int t = threadIdx.x;
+    Scratch<NT> &S = L.S;
 
     // 1. key passes over [lo, lo + span] in 4096 buckets ((key - lo) >> s), then
     // id digits (bits 18..0 of the id; bits 31..19 of ~id are 1 for every id
@@ -421,9 +431,10 @@ __device__ bool lists_select(const uint64_t (&R)[kListLen], uint32_t nrows, bool
     static_assert(kMaxBlocks == 1 << 19, "id digits cover 19 bits");
     uint32_t lo = 0xffffffffu, hi_key = 0u;
 #pragma unroll
-    for (int i = 0; i < NT / kWave; i++) {
-        lo = min(lo, L.wkey[0][i]);
-        hi_key = max(hi_key, L.wkey[1][i]);
+    for (int i = 0; i < NT / kWave; i += 4) {
+        const uint4 a = *(const uint4 *)&L.wkey[0][i], b = *(const uint4 *)&L.wkey[1][i];
+        lo = min(min(lo, min(a.x, a.y)), min(a.z, a.w));
+        hi_key = max(max(hi_key, max(b.x, b.y)), max(b.z, b.w));
     }
     uint32_t span = hi_key - lo;
     uint32_t imask = 0u, ival = 0u;
@@ -512,6 +523,15 @@ __device__ bool lists_select(const uint64_t (&R)[kListLen], uint32_t nrows, bool
     __syncthreads();
     *rs = L.rstar;
     return L.hidden == 0u;
+}
+
+// The whole selection: lists_prepare, a barrier, lists_select_rest.
+__device__ bool lists_select(const uint64_t (&R)[kListLen], uint32_t nrows, bool has_list,
+                             uint32_t k, ListSelLds &L, uint64_t *rs)
+{
+    lists_prepare(R, nrows, has_list, L);
+    __syncthreads();
+    return lists_select_rest(R, k, L, rs);
 }
 
 // Loads list t (thread t < W) and its row count; empty otherwise.
