@@ -18,7 +18,8 @@ Reported:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Other workloads (one JSON line each, same keys): prefill_1024_at_126253 (prefill
-chunk tokens/s; roofline = MFMA scoring against the f16 dense peak, plus the
+chunk tokens/s; roofline = MFMA scoring against the f16 dense peak, timed alone
+over three pooled-cache copies in turn so that none is left in cache, plus the
 attention's K/V GB/s for the per-row form and the bytes / MFMA rate of the
 grouped-union form; --per-row makes the step use the per-row form),
 prefill_1024_at_126253_corr (the same caches with indexer queries correlated from
@@ -362,9 +363,18 @@ def bench_prefill(args):
             step()
     stream.synchronize()
     step_us = _timed(stream, step, args.steps)
-    # the stages alone, on the caches the step leaves behind
-    score_us = _timed(stream, lambda: qb.qsa_index_score(cfg, q_idx, depth, g.k_pool, scores,
-                                                         ld=ld), args.steps)
+    # the stages alone, on the caches the step leaves behind.  The scoring kernel
+    # rotates over three copies of the pooled cache (3 x 130 MB, more than the
+    # 256 MB last-level cache), so no launch finds its operand left in cache by the
+    # previous one, as inside a step
+    pools = [g.k_pool] + [g.k_pool.clone() for _ in range(2)]
+    turn = [0]
+
+    def score_once():
+        qb.qsa_index_score(cfg, q_idx, depth, pools[turn[0] % len(pools)], scores, ld=ld)
+        turn[0] += 1
+
+    score_us = _timed(stream, score_once, args.steps)
     topk_us = _timed(stream, lambda: qb.qsa_topk_blocks(cfg, scores, n_q, ld, depth, blk, nsel,
                                                         ws), args.steps)
     attn_row_us = _timed(stream, lambda: qb.qsa_prefill_attn(
