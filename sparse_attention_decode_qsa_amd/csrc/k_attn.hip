@@ -11,6 +11,11 @@
 //     query heads held in LDS, and reduce across the quarters;
 //   * PV: each wave owns G/4 query heads; a lane owns DV/64 value dims and walks
 //     the chunk's cells, reading each V row once per wave, coalesced.
+// Every K piece of a chunk is loaded before its QK (one memory round trip, the
+// next chunk's loads in flight during this chunk's softmax and PV).  With VK (V
+// rows are the first DV elements of the K rows, as in the MLA latent view) the V
+// rows go to LDS from those K registers, so V is not loaded at all; otherwise up
+// to 4 V pieces per thread ride along with the K loads and the rest follow.
 // With several splits, each writes (m, l, o) partials and attn_combine_kernel (a
 // second launch; the kernel boundary makes the partials visible) merges them.
 #include "qsa_internal.h"
@@ -68,7 +73,7 @@ struct CellMap {
     }
 };
 
-template <int G, int D, int DV>
+template <int G, int D, int DV, bool VK>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
 {
     constexpr int HPW = G >= 4 ? G / 4 : 1;          // query heads per wave (softmax, PV)
@@ -76,13 +81,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     constexpr int QV = D / 32;                       // 16-byte K pieces per lane (a quarter row)
     constexpr int VPR = DV / 8;                      // 16-byte pieces per V row
     constexpr int VV = kAttnChunk * VPR / kThreads;  // V pieces per thread per chunk
-    constexpr int KP = QV < 4 ? QV : 4;              // K pieces loaded a chunk ahead
-    constexpr int VP = VV < 4 ? VV : 4;              // V pieces loaded a chunk ahead
+    constexpr int KP = QV;                           // K pieces loaded a chunk ahead (all)
+    constexpr int VP = VK ? 0 : (VV < 4 ? VV : 4);   // V pieces loaded a chunk ahead
+    // LDS row pitch of V: padded when the rows are written from K registers
+    // (16 cells of a wave write the same column; a 1 KB pitch would put them all
+    // in one bank group)
+    constexpr int VPITCH = VK ? DV + 8 : DV;
     static_assert(D % 32 == 0 && DV % kWave == 0 && VV >= 1, "shape");
+    static_assert(!VK || DV <= D, "V is a prefix of the K row");
     typedef typename VecH<DPL>::T vtype;
 
     __shared__ __attribute__((aligned(16))) h16 qs[G * D];
-    __shared__ __attribute__((aligned(16))) h16 vs[kAttnChunk * DV];
+    __shared__ __attribute__((aligned(16))) h16 vs[kAttnChunk * VPITCH];
     __shared__ __attribute__((aligned(16))) float ps[G][kAttnChunk];
     __shared__ int32_t toks[2][kAttnChunk];
 
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     const int pt = lane & 3;
     const int32_t cbase = split * a.chunks * kAttnChunk;
 
-    h16x8 kreg[KP], vreg[VP];
+    h16x8 kreg[KP], vreg[VP > 0 ? VP : 1];
     auto kaddr = [&](int32_t tok) {
         return a.kbase + (int64_t)max(tok, 0) * a.k_tok + kg + pt * (D / 4);
     };
@@ -173,15 +183,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
 #pragma unroll
             for (int h = 0; h < G; h++)
                 acc[h] = 0.f;
-            const h16 *kr = kaddr(tok);
-#pragma unroll 4
+            // fully unrolled, so that kreg stays in registers; with long rows the
+            // scheduler is kept from hoisting every piece's query reads at once
+#pragma unroll
             for (int v = 0; v < QV; v++) {
-                const h16x8 kv = (v < KP) ? kreg[v < KP ? v : 0]
-                                 : ((tok >= 0) ? *(const h16x8 *)(kr + 8 * v)
-                                               : h16x8{0, 0, 0, 0, 0, 0, 0, 0});
 #pragma unroll
                 for (int h = 0; h < G; h++)
-                    acc[h] = dot8(*(const h16x8 *)&qs[h * D + pt * (D / 4) + 8 * v], kv, acc[h]);
+                    acc[h] = dot8(*(const h16x8 *)&qs[h * D + pt * (D / 4) + 8 * v], kreg[v], acc[h]);
+                if constexpr (QV > 4)
+                    __builtin_amdgcn_sched_barrier(0);
             }
             float bias = 0.f;
             if (a.bias && tok >= 0)
@@ -195,19 +205,30 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
                     ps[h][cl] = (tok >= 0) ? acc[h] * sl2 + bias : -INFINITY;
             }
         }
+        if constexpr (VK) {
+            // the cell's V row = the first DV elements of the K row this lane holds a
+            // quarter of (zeros for a dropped cell)
 #pragma unroll
-        for (int i = 0; i < VP; i++)
-            *(h16x8 *)&vs[(t + kThreads * i) * 8] = vreg[i];
-        for (int i0 = VP; i0 < VV; i0 += 4) {  // large value dims: the rest, 4 at a time
-            h16x8 tmp[4];
+            for (int v = 0; v < QV; v++) {
+                const int d0 = pt * (D / 4) + 8 * v;
+                if (d0 < DV)
+                    *(h16x8 *)&vs[cl * VPITCH + d0] = kreg[v];
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (i0 + i < VV)
-                    tmp[i] = vload(toks[cur], i0 + i);
+            for (int i = 0; i < VP; i++)
+                *(h16x8 *)&vs[(t + kThreads * i) * 8] = vreg[i];
+            for (int i0 = VP; i0 < VV; i0 += 4) {  // large value dims: the rest, 4 at a time
+                h16x8 tmp[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (i0 + i < VV)
-                    *(h16x8 *)&vs[(t + kThreads * (i0 + i)) * 8] = tmp[i];
+                for (int i = 0; i < 4; i++)
+                    if (i0 + i < VV)
+                        tmp[i] = vload(toks[cur], i0 + i);
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    if (i0 + i < VV)
+                        *(h16x8 *)&vs[(t + kThreads * (i0 + i)) * 8] = tmp[i];
+            }
         }
         if (has_next && t < kAttnChunk)
             toks[cur ^ 1][t] = next_tok;
@@ -245,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
                     p4[hh] = *(const f32x4 *)&ps[min(wave * HPW + hh, G - 1)][c4];
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
-                    const vtype vv = *(const vtype *)&vs[(c4 + u) * DV + lane * DPL];
+                    const vtype vv = *(const vtype *)&vs[(c4 + u) * VPITCH + lane * DPL];
 #pragma unroll
                     for (int hh = 0; hh < HPW; hh++) {
                         const float p = p4[hh][u];
@@ -403,16 +424,26 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restr
         vs[dst0 * vrow16 + i] = vc[tok0 * vrow16 + i];
 }
 
-template <int D, int DV>
+template <int D, int DV, bool VK>
 hipError_t launch_g(const AttnArgs &a, int G, hipStream_t s)
 {
     const dim3 grid((uint32_t)a.splits, (uint32_t)a.hkv, (uint32_t)a.rows);
+    // the 576-wide latent rows are attended in head groups of at most 4
+    constexpr int kMaxG = D > 128 ? 4 : 16;
+    if (G > kMaxG)
+        return hipErrorInvalidValue;
     switch (G) {
-    case 1: hipLaunchKernelGGL((attn_kernel<1, D, DV>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<2, D, DV>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<4, D, DV>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_kernel<8, D, DV>), grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((attn_kernel<16, D, DV>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((attn_kernel<1, D, DV, VK>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<2, D, DV, VK>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_kernel<4, D, DV, VK>), grid, dim3(kThreads), 0, s, a); break;
+    case 8:
+        if constexpr (kMaxG >= 8)
+            hipLaunchKernelGGL((attn_kernel<8, D, DV, VK>), grid, dim3(kThreads), 0, s, a);
+        break;
+    case 16:
+        if constexpr (kMaxG >= 16)
+            hipLaunchKernelGGL((attn_kernel<16, D, DV, VK>), grid, dim3(kThreads), 0, s, a);
+        break;
     default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
@@ -431,12 +462,14 @@ hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s)
     const int G = a.hq / a.hkv;
     if (a.splits > kAttnMaxSplits)
         return hipErrorInvalidValue;
-    if (D == 128 && DV == 128)
-        return launch_g<128, 128>(a, G, s);
-    if (D == 64 && DV == 64)
-        return launch_g<64, 64>(a, G, s);
+    if (a.v_in_k && (a.vbase != a.kbase || a.v_tok != a.k_tok))
+        return hipErrorInvalidValue;
+    if (D == 128 && DV == 128 && !a.v_in_k)
+        return launch_g<128, 128, false>(a, G, s);
+    if (D == 64 && DV == 64 && !a.v_in_k)
+        return launch_g<64, 64, false>(a, G, s);
     if (D == 576 && DV == 512)
-        return launch_g<576, 512>(a, G, s);
+        return a.v_in_k ? launch_g<576, 512, true>(a, G, s) : launch_g<576, 512, false>(a, G, s);
     return hipErrorInvalidValue;
 }
 

@@ -818,6 +818,7 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
     a.hq = hq;
     a.hkv = hq > 4 ? hq / 4 : 1;
     a.kv_shared = 1;
+    a.v_in_k = v ? 0 : 1;  // the latent view: V rows are KV[:, :dv]
     a.mode = kCellsList;
     a.list = list;
     a.n_list = n_list;

@@ -115,6 +115,8 @@ struct AttnArgs {
     int32_t tok_bound;      // list: tokens must be < tok_bound (the mask length)
     int32_t kv_shared;      // 1: every KV-head group reads the same K/V rows (one latent
                             // head, its query heads split into hkv groups)
+    int32_t v_in_k;         // 1: each V row is the first DV elements of its K row
+                            // (vbase == kbase, v_tok == k_tok; the MLA latent view)
 };
 hipError_t launch_attn(const AttnArgs &a, int32_t D, int32_t DV, hipStream_t s);
 // Merge of split-K partials [rows][hq][splits][dv + 2] into out [rows][hq][dv].
