@@ -49,12 +49,18 @@ __device__ __forceinline__ float h2f(h16 x) { return (float)x; }
 
 // Cell c of row `row` -> token, or -1 (past the row's cells, or a dropped id).
 struct CellMap {
-    int32_t mode, count, nsel, nbr, tok_bound;
+    int32_t mode, count, nsel, nbr, tok_bound, cap;
     const int32_t *blkr;
     const int32_t *list;
 
     __device__ __forceinline__ int32_t operator()(int32_t c) const
     {
+        if (mode == kCellsList) {
+            // the entry is read whether or not c is below the device count (c < cap
+            // keeps the read inside the list), so its load overlaps the count's
+            const int32_t j = c < cap ? list[c] : -1;
+            return (c < count && (uint32_t)j < (uint32_t)tok_bound) ? j : -1;
+        }
         if (c >= count)
             return -1;
         if (mode == kCellsCompact)
@@ -68,8 +74,7 @@ struct CellMap {
             }
             return kBlockTokens * nbr + (c - kBlockTokens * nsel);
         }
-        const int32_t j = list[c];
-        return ((uint32_t)j < (uint32_t)tok_bound) ? j : -1;
+        return -1;
     }
 };
 
@@ -104,6 +109,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     cm.nsel = 0;
     cm.nbr = 0;
     cm.tok_bound = a.tok_bound;
+    cm.cap = a.list_cap;
     cm.list = a.list;
     cm.blkr = a.blk ? a.blk + (int64_t)row * a.ldb : nullptr;
     bool overflow = false;

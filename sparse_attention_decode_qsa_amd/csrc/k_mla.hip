@@ -62,27 +62,27 @@ __global__ __launch_bounds__(kThreads) void mask_write_kernel(const h16 *__restr
                                                               int32_t *__restrict__ list,
                                                               int32_t *__restrict__ n_list)
 {
-    __shared__ uint32_t red[kThreads];
+    __shared__ uint32_t pre[kWaves];
     __shared__ uint32_t wc[kWaves];
     const int t = threadIdx.x, wave = t / kWave;
     const uint32_t seg = blockIdx.x;
+    // the counts of the segments before this one, summed per wave, and this
+    // wave's own count: one barrier publishes both
     uint32_t s = 0;
     for (uint32_t i = t; i < seg; i += kThreads)
         s += seg_cnt[i];
-    red[t] = s;
-    __syncthreads();
-    for (int o = kThreads / 2; o > 0; o >>= 1) {
-        if (t < o)
-            red[t] += red[t + o];
-        __syncthreads();
-    }
-    const uint32_t seg_off = red[0];
-
+    const uint32_t ws = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(s), kWave - 1);
     const int64_t base = (int64_t)seg * kListSeg + (int64_t)wave * kPerWave;
     const uint32_t c = wave_count(mask, n, base);
-    if (lane_id() == 0)
+    if (lane_id() == 0) {
+        pre[wave] = ws;
         wc[wave] = c;
+    }
     __syncthreads();
+    uint32_t seg_off = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++)
+        seg_off += pre[w];
     uint32_t off = seg_off;
     for (int w = 0; w < wave; w++)
         off += wc[w];
