@@ -126,9 +126,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         cm.count = overflow ? 0 : nl;
     }
 
-    const h16 *qrow = a.q + ((int64_t)row * a.hq + (int64_t)g * G) * D;
-    for (int i = t; i < G * D / 8; i += kThreads)
-        ((h16x8 *)qs)[i] = ((const h16x8 *)qrow)[i];
+    // the query rows of this head group: all loads issued at once (indexes clamped;
+    // a loop of load-then-store would wait for each), stored to LDS with the cell map
+    constexpr int QN = G * D / 8, QPT = (QN + kThreads - 1) / kThreads;
+    const h16x8 *qrow8 = (const h16x8 *)(a.q + ((int64_t)row * a.hq + (int64_t)g * G) * D);
+    h16x8 qv[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; i++)
+        qv[i] = qrow8[min(t + i * kThreads, QN - 1)];
+    auto store_q = [&]() {
+#pragma unroll
+        for (int i = 0; i < QPT; i++)
+            if (t + i * kThreads < QN)
+                ((h16x8 *)qs)[t + i * kThreads] = qv[i];
+    };
 
     float m_run[HPW], l_run[HPW], o[HPW][DPL];
 #pragma unroll
@@ -170,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
 
     if (t < kAttnChunk)
         toks[0][t] = cm(cbase + t);
+    store_q();
     __syncthreads();
     issue_loads(toks[0]);
 

@@ -17,22 +17,29 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kPerWave = kListSeg / kWaves;  // 256 positions: 4 ballots per wave
-constexpr uint16_t kNegInf = 0xFC00u;
 
+// The load is unconditional (index clamped into the mask), so a wave's loads for
+// several ballots are all in flight before the first ballot.
 __device__ __forceinline__ bool visible(const h16 *mask, int32_t n, int64_t j)
 {
-    if (j >= n)
-        return false;
-    const uint16_t bits = *(const uint16_t *)(mask + j);
-    return bits != kNegInf;
+    const uint16_t bits = *(const uint16_t *)(mask + (j < n ? j : (int64_t)n - 1));
+    return j < n && bits != kF16NegInf;
 }
 
-__device__ uint32_t wave_count(const h16 *mask, int32_t n, int64_t base)
+// This wave's kPerWave positions from base: one ballot per 64 (all loads issued
+// first); returns the visible count.
+__device__ uint32_t wave_masks(const h16 *mask, int32_t n, int64_t base,
+                               uint64_t (&mk)[kPerWave / kWave])
 {
+    bool v[kPerWave / kWave];
+#pragma unroll
+    for (int it = 0; it < kPerWave / kWave; it++)
+        v[it] = visible(mask, n, base + it * kWave + lane_id());
     uint32_t c = 0;
+#pragma unroll
     for (int it = 0; it < kPerWave / kWave; it++) {
-        const uint64_t m = __ballot(visible(mask, n, base + it * kWave + lane_id()));
-        c += (uint32_t)__popcll(m);
+        mk[it] = __ballot(v[it]);
+        c += (uint32_t)__popcll(mk[it]);
     }
     return c;
 }
@@ -44,7 +51,8 @@ __global__ __launch_bounds__(kThreads) void mask_count_kernel(const h16 *__restr
     __shared__ uint32_t wc[kWaves];
     const int wave = threadIdx.x / kWave;
     const int64_t base = (int64_t)blockIdx.x * kListSeg + (int64_t)wave * kPerWave;
-    const uint32_t c = wave_count(mask, n, base);
+    uint64_t mk[kPerWave / kWave];
+    const uint32_t c = wave_masks(mask, n, base, mk);
     if (lane_id() == 0)
         wc[wave] = c;
     __syncthreads();
@@ -67,13 +75,16 @@ __global__ __launch_bounds__(kThreads) void mask_write_kernel(const h16 *__restr
     const int t = threadIdx.x, wave = t / kWave;
     const uint32_t seg = blockIdx.x;
     // the counts of the segments before this one, summed per wave, and this
-    // wave's own count: one barrier publishes both
-    uint32_t s = 0;
-    for (uint32_t i = t; i < seg; i += kThreads)
+    // wave's ballots: one barrier publishes both.  The first count is loaded
+    // unconditionally (index clamped) so that it is in flight with the mask loads
+    const uint32_t first = seg_cnt[min((uint32_t)t, gridDim.x - 1)];
+    const int64_t base = (int64_t)seg * kListSeg + (int64_t)wave * kPerWave;
+    uint64_t mk[kPerWave / kWave];
+    const uint32_t c = wave_masks(mask, n, base, mk);
+    uint32_t s = (uint32_t)t < seg ? first : 0u;
+    for (uint32_t i = t + kThreads; i < seg; i += kThreads)
         s += seg_cnt[i];
     const uint32_t ws = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(s), kWave - 1);
-    const int64_t base = (int64_t)seg * kListSeg + (int64_t)wave * kPerWave;
-    const uint32_t c = wave_count(mask, n, base);
     if (lane_id() == 0) {
         pre[wave] = ws;
         wc[wave] = c;
@@ -86,14 +97,13 @@ __global__ __launch_bounds__(kThreads) void mask_write_kernel(const h16 *__restr
     uint32_t off = seg_off;
     for (int w = 0; w < wave; w++)
         off += wc[w];
+#pragma unroll
     for (int it = 0; it < kPerWave / kWave; it++) {
-        const int64_t j = base + it * kWave + lane_id();
-        const bool v = visible(mask, n, j);
-        const uint64_t m = __ballot(v);
-        if (v) {
+        const uint64_t m = mk[it];  // the ballots of the count: the mask is read once
+        if ((m >> lane_id()) & 1ull) {
             const uint32_t slot = off + rank_in_mask(m);
             if (slot < (uint32_t)list_cap)
-                list[slot] = (int32_t)j;
+                list[slot] = (int32_t)(base + it * kWave + lane_id());
         }
         off += (uint32_t)__popcll(m);
     }

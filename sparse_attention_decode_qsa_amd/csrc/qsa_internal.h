@@ -177,6 +177,8 @@ hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s);
 // ---- MLA list (k_mla.hip) ---------------------------------------------------
 constexpr int kListSeg = 1024;     // positions per list-building work group
 constexpr int kListSegMax = 8192;  // segments: masks of up to 8,388,608 positions
+constexpr uint16_t kF16NegInf = 0xFC00u;  // binary16 -inf: a hidden position
+// Counts per segment, then the whole ascending list and its count.
 hipError_t launch_mask_list(const h16 *mask, int32_t n, int32_t list_cap, uint32_t *seg_cnt,
                             int32_t *list, int32_t *n_list, hipStream_t s);
 

@@ -99,3 +99,35 @@ def test_mla_nothing_visible(gpu):
     # softmax over an empty set: the oracle's 0/0 is NaN, and so is the kernel's
     ref = O.mla_attn(q, kv, None, mask, np.zeros(0, np.int32), 512, 0.05)
     assert np.isnan(ref).all() and np.isnan(out).all()
+
+
+@pytest.mark.parametrize("list_cap", [64, 4096, 4160, 8192])
+def test_mla_list_forms(gpu, list_cap):
+    # list capacities of one and of several 64-slot chunks per attention work group,
+    # with the caller's list or without it: the same list, count and attention
+    n = 2 * list_cap if list_cap >= 4096 else 8192
+    r = np.random.default_rng(list_cap)
+    kv = synth.normal_f16(200 + list_cap % 97, (n, 576))
+    q = synth.normal_f16(300 + list_cap % 89, (16, 576))
+    mask = np.full(n, -np.inf, np.float16)
+    # clustered and scattered positions: runs over several 1,024-position segments,
+    # whole empty segments, single positions
+    vis = min(list_cap, 3000)
+    pos = np.sort(np.unique(np.concatenate([
+        np.arange(100, 100 + vis // 2),
+        r.choice(np.arange(5000, n), vis - vis // 2, replace=False)])))[:vis]
+    mask[pos] = 0.0
+    scale = 1.0 / np.sqrt(576)
+    out, lst, nl, _ = run_mla(q, kv, mask, list_cap, scale)
+    assert nl == pos.size and np.array_equal(lst[:nl], pos)
+    ref = O.mla_attn(q, kv, None, mask, pos, 512, scale)
+    assert_attn_close(out, ref)
+    # no list output requested: the same count and attention
+    ws = torch.zeros(qb.qsa_mla_workspace_size(16, 512, list_cap), dtype=torch.uint8,
+                     device="cuda")
+    qb.qsa_workspace_init(ws)
+    out2 = torch.empty((16, 512), device="cuda")
+    n_list = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qb.qsa_mla_sparse_attn(dev(q), dev(kv), None, dev(mask), list_cap, scale, n_list, out2, ws)
+    assert int(host(n_list)[0]) == pos.size
+    assert np.array_equal(host(out2), out)
