@@ -117,16 +117,19 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
     const int32_t b_hi = b_lo + chunks * kAttnChunk / kBlockTokens;
     const bool from_lists = nb > a.k;  // else every complete block is chosen
 
-    // candidate list t, issued before the query loads so that the two round
-    // trips overlap
+    // the query rows of this KV head (independent of the selection) and candidate
+    // list t: every load issued (indexes clamped, no branch) before any result is
+    // used, so that the two round trips overlap
+    constexpr int QN = G * D / 8;  // 16-byte pieces of the query rows
+    static_assert(QN <= kNT, "one query piece per thread");
+    const h16x8 *qrow8 = (const h16x8 *)(a.q + ((int64_t)row * a.hq + (int64_t)g * G) * D);
+    const h16x8 qv = qrow8[t < QN ? t : QN - 1];
     uint64_t R[kListLen];
     uint32_t nrows = 0;
     if (from_lists)
-        load_list(cl, a.n_lists, R, &nrows);
-    // the query rows of this KV head (independent of the selection)
-    const h16 *qrow = a.q + ((int64_t)row * a.hq + (int64_t)g * G) * D;
-    for (int i = t; i < G * D / 8; i += kNT)
-        ((h16x8 *)sm.qs)[i] = ((const h16x8 *)qrow)[i];
+        load_list_raw(cl, a.n_lists, R, &nrows);
+    if (t < QN)
+        ((h16x8 *)sm.qs)[t] = qv;
     // the split's tail cells (the incomplete block, after the chosen ones)
     for (int i = t; i < chunks * kAttnChunk; i += kNT) {
         const int32_t c = c_lo + i;
@@ -135,8 +138,10 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
                          : -1;
     }
     // the selection's first stage shares this barrier
-    if (from_lists)
+    if (from_lists) {
+        drop_absent_list(a.n_lists, R, &nrows);
         lists_prepare(R, nrows, t < a.n_lists, sm.L);
+    }
     __syncthreads();
     // the chosen blocks; position i goes to cells 4i .. 4i + 3
     auto place = [&](int32_t pos, int32_t id) {

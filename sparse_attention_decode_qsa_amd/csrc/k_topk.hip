@@ -65,26 +65,52 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
     };
 
     // top 16 key bits, two per register (the histogram and the bin test need 12)
+    // Every load is issued unconditionally from an address inside the row, so the
+    // loads of a group overlap (a load under a branch makes the compiler wait for
+    // it where the branches merge).  Groups of 4 wholly below nb are 16-byte loads;
+    // the row's last partial group is read once per thread with clamped scalar
+    // loads; groups at or past nb give key 0.  A misaligned or very short row
+    // takes clamped scalar loads throughout.
     uint32_t kp[KPT / 2];
-    const bool vec_ok = (((uintptr_t)row) & 15) == 0;
+    if ((((uintptr_t)row) & 15) == 0 && nb >= 4) {
+        const uint32_t ip = nb & ~3u;  // first id of the partial group (if nb % 4)
+        float pv[3];
 #pragma unroll
-    for (int j = 0; j < V4; j++) {
-        const uint32_t i0 = id_of(j, 0);
-        uint32_t kk[4];
-        if (vec_ok && i0 + 3 < nb) {
-            const f32x4 v = *(const f32x4 *)(row + i0);
+        for (int e = 0; e < 3; e++)
+            pv[e] = row[min(ip + e, nb - 1)];
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                kk[e] = score_key(v[e]);
-        } else {
+        for (int j = 0; j < V4; j++) {
+            const uint32_t i0 = id_of(j, 0);
+            const bool full = i0 + 3 < nb;
+            const f32x4 v = *(const f32x4 *)(row + (full ? i0 : 0u));
+            const bool part = i0 == ip;
+            uint32_t kk[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                kk[e] = (i0 + e < nb) ? score_key(row[i0 + e]) : 0u;
+            for (int e = 0; e < 4; e++) {
+                const float x = part ? pv[e < 3 ? e : 0] : v[e];
+                const bool on = full || (part && i0 + e < nb);
+                kk[e] = score_key(x) & (0u - (uint32_t)on);  // no branch: 0 when off
+            }
+            kp[2 * j] = (kk[0] >> 16) | (kk[1] & 0xffff0000u);
+            kp[2 * j + 1] = (kk[2] >> 16) | (kk[3] & 0xffff0000u);
+            if ((j & 7) == 7)
+                __builtin_amdgcn_sched_barrier(0);  // at most 8 row loads in flight per lane
         }
-        kp[2 * j] = (kk[0] >> 16) | (kk[1] & 0xffff0000u);
-        kp[2 * j + 1] = (kk[2] >> 16) | (kk[3] & 0xffff0000u);
-        if ((j & 7) == 7)
-            __builtin_amdgcn_sched_barrier(0);  // at most 8 row loads in flight per lane
+    } else {
+#pragma unroll
+        for (int j = 0; j < V4; j++) {
+            const uint32_t i0 = id_of(j, 0);
+            uint32_t kk[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float x = row[min(i0 + e, nb - 1)];
+                kk[e] = score_key(x) & (0u - (uint32_t)(i0 + e < nb));
+            }
+            kp[2 * j] = (kk[0] >> 16) | (kk[1] & 0xffff0000u);
+            kp[2 * j + 1] = (kk[2] >> 16) | (kk[3] & 0xffff0000u);
+            if ((j & 7) == 7)
+                __builtin_amdgcn_sched_barrier(0);
+        }
     }
     auto bin_of = [&](int j) -> uint32_t {  // j-th key of this thread, top 12 bits
         const uint32_t w = kp[j >> 1];

@@ -134,6 +134,26 @@ __device__ void find_from_top_wg(const uint32_t *hist, uint32_t need, Scratch<NT
     __syncthreads();
 }
 
+// Calls f(score_key(row[i]), i) for every i < nb, thread by thread in strides of
+// NT.  The loads of kRowBatch strides are all issued (indexes clamped into the
+// row) before the first key is used, so a pass over a row costs one memory round
+// trip per batch rather than one per stride.
+constexpr int kRowBatch = 8;
+template <int NT, class F>
+__device__ __forceinline__ void each_row_key(const float *row, uint32_t nb, F f)
+{
+    for (uint32_t i0 = threadIdx.x; i0 < nb; i0 += NT * kRowBatch) {
+        float x[kRowBatch];
+#pragma unroll
+        for (int u = 0; u < kRowBatch; u++)
+            x[u] = row[min(i0 + (uint32_t)(u * NT), nb - 1)];
+#pragma unroll
+        for (int u = 0; u < kRowBatch; u++)
+            if (i0 + (uint32_t)(u * NT) < nb)
+                f(score_key(x[u]), i0 + (uint32_t)(u * NT));
+    }
+}
+
 // Candidate sources: each calls f(key, id) for every block of bin B.
 template <int NT>
 struct LdsCands {
@@ -169,11 +189,10 @@ struct RowCands {
     template <class F>
     __device__ void each(F f) const
     {
-        for (uint32_t i = threadIdx.x; i < nb; i += NT) {
-            const uint32_t key = score_key(row[i]);
+        each_row_key<NT>(row, nb, [&](uint32_t key, uint32_t i) {
             if ((key >> (32 - kHistBits)) == bin)
                 f(key, i);
-        }
+        });
     }
 };
 
@@ -304,16 +323,15 @@ __device__ void select_row_global(const float *row, uint32_t nb, int32_t k, int3
     if (threadIdx.x == 0)
         S.cnt = 0;
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nb; i += NT)
-        atomicAdd(&hist[score_key(row[i]) >> (32 - kHistBits)], 1u);
+    each_row_key<NT>(row, nb,
+                     [&](uint32_t key, uint32_t) { atomicAdd(&hist[key >> (32 - kHistBits)], 1u); });
     __syncthreads();
     find_from_top<NT, kHistBins>(hist, (uint32_t)k, S);
     const uint32_t B = S.res[0];
     const uint32_t need = (uint32_t)k - S.res[1];
     zero_words<NT>(bitmap, (nb + 31) / 32);
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nb; i += NT) {
-        const uint32_t key = score_key(row[i]);
+    each_row_key<NT>(row, nb, [&](uint32_t key, uint32_t i) {
         const uint32_t bin = key >> (32 - kHistBits);
         if (bin > B) {
             set_bit(bitmap, i);
@@ -322,7 +340,7 @@ __device__ void select_row_global(const float *row, uint32_t nb, int32_t k, int3
             if (slot < kCandCap)
                 cand[slot] = ((uint64_t)key << 32) | i;
         }
-    }
+    });
     __syncthreads();
     const uint32_t c = S.cnt;
     uint32_t *h256 = hist;  // the 12-bit histogram is no longer needed
@@ -534,25 +552,38 @@ __device__ bool lists_select(const uint64_t (&R)[kListLen], uint32_t nrows, bool
     return lists_select_rest(R, k, L, rs);
 }
 
+// Issues the loads of list min(t, W - 1) and its row count (W >= 1): no branch,
+// so the loads stay in flight while the caller issues others.  Threads t >= W
+// must call drop_absent_list before using R.
+__device__ void load_list_raw(const CandLists &cl, int32_t W, uint64_t (&R)[kListLen],
+                              uint32_t *nrows)
+{
+    const int t = threadIdx.x < W ? (int)threadIdx.x : W - 1;
+    const uint4 *src = (const uint4 *)(cl.list + (int64_t)t * kListLen);
+#pragma unroll
+    for (int j = 0; j < kListLen / 2; j++) {
+        const uint4 v = src[j];
+        R[2 * j] = ((uint64_t)v.y << 32) | v.x;
+        R[2 * j + 1] = ((uint64_t)v.w << 32) | v.z;
+    }
+    *nrows = cl.rows[t];
+}
+
+// Empties the list of a thread that holds none (t >= W).
+__device__ void drop_absent_list(int32_t W, uint64_t (&R)[kListLen], uint32_t *nrows)
+{
+    const bool on = (int)threadIdx.x < W;
+#pragma unroll
+    for (int j = 0; j < kListLen; j++)
+        R[j] = on ? R[j] : 0ull;
+    *nrows = on ? *nrows : 0u;
+}
+
 // Loads list t (thread t < W) and its row count; empty otherwise.
 __device__ void load_list(const CandLists &cl, int32_t W, uint64_t (&R)[kListLen], uint32_t *nrows)
 {
-    const int t = threadIdx.x;
-    if (t < W) {
-        const uint4 *src = (const uint4 *)(cl.list + (int64_t)t * kListLen);
-#pragma unroll
-        for (int j = 0; j < kListLen / 2; j++) {
-            const uint4 v = src[j];
-            R[2 * j] = ((uint64_t)v.y << 32) | v.x;
-            R[2 * j + 1] = ((uint64_t)v.w << 32) | v.z;
-        }
-        *nrows = cl.rows[t];
-    } else {
-#pragma unroll
-        for (int j = 0; j < kListLen; j++)
-            R[j] = 0ull;
-        *nrows = 0;
-    }
+    load_list_raw(cl, W, R, nrows);
+    drop_absent_list(W, R, nrows);
 }
 
 }  // namespace
