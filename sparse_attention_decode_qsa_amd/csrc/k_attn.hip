@@ -446,14 +446,17 @@ template <int D, int DV, bool VK>
 hipError_t launch_g(const AttnArgs &a, int G, hipStream_t s)
 {
     const dim3 grid((uint32_t)a.splits, (uint32_t)a.hkv, (uint32_t)a.rows);
-    // the 576-wide latent rows are attended in head groups of at most 4
-    constexpr int kMaxG = D > 128 ? 4 : 16;
+    // the 576-wide latent rows are attended in head groups of at most 2
+    constexpr int kMaxG = D > 128 ? 2 : 16;
     if (G > kMaxG)
         return hipErrorInvalidValue;
     switch (G) {
     case 1: hipLaunchKernelGGL((attn_kernel<1, D, DV, VK>), grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((attn_kernel<2, D, DV, VK>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<4, D, DV, VK>), grid, dim3(kThreads), 0, s, a); break;
+    case 4:
+        if constexpr (kMaxG >= 4)
+            hipLaunchKernelGGL((attn_kernel<4, D, DV, VK>), grid, dim3(kThreads), 0, s, a);
+        break;
     case 8:
         if constexpr (kMaxG >= 8)
             hipLaunchKernelGGL((attn_kernel<8, D, DV, VK>), grid, dim3(kThreads), 0, s, a);
