@@ -345,7 +345,10 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const float 
 {
     constexpr int DPT = DV > kCombThreads ? DV / kCombThreads : 1;  // dims per thread
     constexpr int G = DV < kCombThreads ? kCombThreads / DV : 1;    // split groups
-    constexpr int CH = 32 / DPT;                                     // splits per thread per round
+    // splits per thread per round: G * 32 splits (32 at 512 value dims, 64 at 128)
+    // are merged in one round, i.e. one memory round trip
+    constexpr int CH = 32;
+    static_assert(DPT * CH <= 64, "partials held per thread");
     __shared__ float w_sh[kAttnMaxSplits];
     __shared__ float l_sh;
     __shared__ float red[G][DV];
@@ -364,6 +367,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const float 
 #pragma unroll
     for (int p = 0; p < DPT; p++)
         acc[p] = 0.f;
+    int32_t nl = 0;
     for (int s0 = 0; s0 < S; s0 += G * CH) {
         float o[CH][DPT];
 #pragma unroll
@@ -375,6 +379,8 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const float 
                 o[i][p] = pb[sc * stride + 2 + jt + p * (DV / DPT)];
         }
         if (s0 == 0) {
+            // the list count (a scalar load) goes out with this round's partials
+            nl = n_list ? *n_list : 0;
             if (t < kWave) {
                 const float M = wave_max(m);
                 const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const float 
                 acc[p] = sl < S ? fmaf(w, o[i][p], acc[p]) : acc[p];
         }
     }
-    const bool overflow = n_list && *n_list > list_cap;
+    const bool overflow = n_list && nl > list_cap;
     if (G > 1) {
         red[grp][jt] = acc[0];
         __syncthreads();
