@@ -82,7 +82,12 @@ template <int G, int D, int DV, bool VK>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
 {
     constexpr int HPW = G >= 4 ? G / 4 : 1;          // query heads per wave (softmax, PV)
-    constexpr int DPL = DV / kWave;                  // value dims per lane in PV
+    // with fewer than 4 heads, WPH waves share a head in PV, each on DV / WPH of
+    // its value dims (at least 64), so that no wave idles; the head's first wave
+    // runs its softmax and passes the rescale and the final sum through LDS
+    constexpr int WPH0 = G >= 4 ? 1 : 4 / G;
+    constexpr int WPH = WPH0 < DV / kWave ? WPH0 : DV / kWave;
+    constexpr int DPL = DV / WPH / kWave;            // value dims per lane in PV
     constexpr int QV = D / 32;                       // 16-byte K pieces per lane (a quarter row)
     constexpr int VPR = DV / 8;                      // 16-byte pieces per V row
     constexpr int VV = kAttnChunk * VPR / kThreads;  // V pieces per thread per chunk
@@ -100,9 +105,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) h16 vs[kAttnChunk * VPITCH];
     __shared__ __attribute__((aligned(16))) float ps[G][kAttnChunk];
     __shared__ int32_t toks[2][kAttnChunk];
+    __shared__ float alpha_sh[G], lsum_sh[G];  // WPH > 1: the head's rescale, final sum
 
     const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    // head hh of this wave, the first value dim of its PV slice, and whether it
+    // runs the head's softmax
+    auto head = [&](int hh) { return WPH > 1 ? wave / WPH : wave * HPW + hh; };
+    const int d0 = (wave % WPH) * (DV / WPH);
+    const bool lead = wave % WPH == 0;
 
     CellMap cm;
     cm.mode = a.mode;
@@ -257,8 +268,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         // ---- online softmax update for this wave's heads (lane = cell)
 #pragma unroll
         for (int hh = 0; hh < HPW; hh++) {
-            const int h = wave * HPW + hh;
-            if (h < G) {
+            const int h = head(hh);
+            if (h < G && lead) {
                 const float s = ps[h][lane];
                 const float mnew = fmaxf(m_run[hh], wave_max(s));
                 const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run[hh] - mnew);
@@ -266,25 +277,38 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
                 ps[h][lane] = p;
                 l_run[hh] = l_run[hh] * alpha + wave_sum(p);
                 m_run[hh] = mnew;
+                if constexpr (WPH > 1) {
+                    if (lane == 0)
+                        alpha_sh[h] = alpha;
+                } else {
 #pragma unroll
-                for (int j = 0; j < DPL; j++)
-                    o[hh][j] *= alpha;
+                    for (int j = 0; j < DPL; j++)
+                        o[hh][j] *= alpha;
+                }
             }
         }
         __syncthreads();
+        if constexpr (WPH > 1) {
+            if (head(0) < G) {
+                const float alpha = alpha_sh[head(0)];
+#pragma unroll
+                for (int j = 0; j < DPL; j++)
+                    o[0][j] *= alpha;
+            }
+        }
 
         // ---- PV from the LDS copy of the chunk's V rows.  Cells past the end or
         // dropped have p = 0 and zeroed V rows, so all 64 are walked unguarded.
-        if (wave * HPW < G) {
+        if (head(0) < G) {
 #pragma unroll 4
             for (int c4 = 0; c4 < kAttnChunk; c4 += 4) {
                 f32x4 p4[HPW];
 #pragma unroll
                 for (int hh = 0; hh < HPW; hh++)
-                    p4[hh] = *(const f32x4 *)&ps[min(wave * HPW + hh, G - 1)][c4];
+                    p4[hh] = *(const f32x4 *)&ps[min(head(hh), G - 1)][c4];
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
-                    const vtype vv = *(const vtype *)&vs[(c4 + u) * VPITCH + lane * DPL];
+                    const vtype vv = *(const vtype *)&vs[(c4 + u) * VPITCH + d0 + lane * DPL];
 #pragma unroll
                     for (int hh = 0; hh < HPW; hh++) {
                         const float p = p4[hh][u];
@@ -303,25 +327,30 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     }
 
     const int64_t hq0 = (int64_t)row * a.hq + (int64_t)g * G;
+    if constexpr (WPH > 1) {
+        if (lead && lane == 0 && head(0) < G)
+            lsum_sh[head(0)] = l_run[0];
+        __syncthreads();
+    }
 #pragma unroll
     for (int hh = 0; hh < HPW; hh++) {
-        const int h = wave * HPW + hh;
+        const int h = head(hh);
         if (h < G) {
             if (a.splits == 1) {
-                const float inv = 1.f / l_run[hh];
+                const float inv = 1.f / (WPH > 1 ? lsum_sh[h] : l_run[hh]);
 #pragma unroll
                 for (int j = 0; j < DPL; j++)
-                    a.out[(hq0 + h) * DV + lane * DPL + j] = overflow ? NAN : o[hh][j] * inv;
+                    a.out[(hq0 + h) * DV + d0 + lane * DPL + j] = overflow ? NAN : o[hh][j] * inv;
             } else {
                 // split-K partial (m, l, o); attn_combine_kernel merges them
                 float *pb = a.part + ((hq0 + h) * a.splits + split) * (DV + 2);
-                if (lane == 0) {
+                if (lead && lane == 0) {
                     pb[0] = m_run[hh];
                     pb[1] = l_run[hh];
                 }
 #pragma unroll
                 for (int j = 0; j < DPL; j++)
-                    pb[2 + lane * DPL + j] = o[hh][j];
+                    pb[2 + d0 + lane * DPL + j] = o[hh][j];
             }
         }
     }
