@@ -115,7 +115,7 @@ def run_cpu_baseline(w, L, budget_s):
 def bench_decode(args):
     import torch
     from sparse_attention_decode_qsa_amd import binding as qb
-    from sparse_attention_decode_qsa_amd import synth
+    import synth
 
     w = synth.WORKLOADS[args.workload]
     n_layers = args.layers or w.n_layers
@@ -324,7 +324,7 @@ def bench_prefill(args):
     causal prefix (append, MFMA scores, per-row top-k, per-row sparse attention)."""
     import torch
     from sparse_attention_decode_qsa_amd import binding as qb
-    from sparse_attention_decode_qsa_amd import synth
+    import synth
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -470,7 +470,7 @@ def bench_mla(args):
     layer state (its own latent rows, mask and queries), the states taken in turn."""
     import torch
     from sparse_attention_decode_qsa_amd import binding as qb
-    from sparse_attention_decode_qsa_amd import synth
+    import synth
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

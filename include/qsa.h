@@ -289,14 +289,26 @@ int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_b
  * length.  Preconditions (else QSA_ERR_UNSUPPORTED): mask != NULL, n >= 4096,
  * n >= 2*list_cap, dkq == 576, dv == 512, hq in {1, 2, 4, 8, 16}.  If more
  * than list_cap positions are visible, n_list receives the true count, nothing
- * past list_cap is read and out is filled with NaN; the host learns of it by
- * reading n_list.
+ * past list_cap is read and out is filled with NaN.  The list length is known only
+ * on the device when the call returns, so the capacity error reaches the host
+ * through qsa_mla_list_status() below (the call itself stays asynchronous).
  */
 size_t qsa_mla_workspace_size(int32_t hq, int32_t dv, int32_t list_cap);
 int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const uint16_t *v,
                         int32_t dkq, int32_t dv, const uint16_t *mask, int32_t n,
                         int32_t list_cap, float scale, int32_t *list_out, int32_t *n_list,
                         float *out, void *ws, size_t ws_bytes, qsa_stream_t stream);
+
+/*
+ * Capacity status of a qsa_mla_sparse_attn call (devotd.net news, section 3: the
+ * list holds at most list_cap positions).  Waits for `stream`, reads the device
+ * count n_list [1] that the call wrote and returns QSA_ERR_CAPACITY if it exceeds
+ * list_cap (that call's out is NaN), else QSA_OK.  n_list_host (optional, host
+ * memory) receives the count.  Blocks the calling thread; not for graph capture.
+ * Errors: INVALID (n_list NULL, list_cap < 1), HIP (copy or wait failed).
+ */
+int qsa_mla_list_status(const int32_t *n_list, int32_t list_cap, int32_t *n_list_host,
+                        qsa_stream_t stream);
 
 #ifdef __cplusplus
 }

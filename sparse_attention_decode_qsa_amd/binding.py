@@ -33,7 +33,7 @@ EXPORTS = [
     "qsa_workspace_init", "qsa_pool_append", "qsa_pool_rebuild", "qsa_kv_append",
     "qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_attn",
     "qsa_prefill_attn", "qsa_decode_step", "qsa_decode_multi", "qsa_prefill_step",
-    "qsa_mla_workspace_size", "qsa_mla_sparse_attn",
+    "qsa_mla_workspace_size", "qsa_mla_sparse_attn", "qsa_mla_list_status",
 ]
 
 
@@ -91,6 +91,7 @@ def load():
         "qsa_mla_workspace_size": (sz, [i32, i32, i32]),
         "qsa_mla_sparse_attn": (C.c_int, [p, i32, p, p, i32, i32, p, i32, i32, C.c_float, p, p,
                                           p, p, sz, p]),
+        "qsa_mla_list_status": (C.c_int, [p, i32, C.POINTER(i32), p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -317,3 +318,12 @@ def qsa_mla_sparse_attn(q, kv, v, mask, list_cap: int, scale: float, n_list, out
                                       _ptr(n_list, torch.int32, name="n_list"),
                                       _ptr(out, torch.float32, name="out"), _ptr(ws),
                                       ws.numel(), _stream()))
+
+
+def qsa_mla_list_status(n_list, list_cap: int) -> int:
+    """Waits for the current stream and returns the visible-position count of the
+    last list call; raises QsaError(QSA_ERR_CAPACITY) if it exceeds list_cap."""
+    n = C.c_int32(0)
+    _check(load().qsa_mla_list_status(_ptr(n_list, torch.int32, name="n_list"), list_cap,
+                                      C.byref(n), _stream()))
+    return int(n.value)

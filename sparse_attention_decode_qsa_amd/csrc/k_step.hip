@@ -361,6 +361,9 @@ hipError_t launch_step_tail(const StepTail &st, hipStream_t s)
     const int64_t wgs = (int64_t)n_chunks * st.hkv * st.rows;
     a.chunks = (int32_t)((wgs + 255) / 256);
     a.chunks = a.chunks < 1 ? 1 : (a.chunks > kMaxChunks ? kMaxChunks : a.chunks);
+    // never more splits than the partial buffer holds (k = 1024 has up to 65 chunks)
+    const int32_t c_min = (n_chunks + kAttnMaxSplits - 1) / kAttnMaxSplits;
+    a.chunks = a.chunks < c_min ? c_min : a.chunks;
     a.splits = (n_chunks + a.chunks - 1) / a.chunks;
     if (a.splits > kAttnMaxSplits)
         return hipErrorInvalidValue;

@@ -835,4 +835,23 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
     return QSA_OK;
 }
 
+int qsa_mla_list_status(const int32_t *n_list, int32_t list_cap, int32_t *n_list_host,
+                        qsa_stream_t stream)
+{
+    if (!n_list)
+        return fail(QSA_ERR_INVALID, "qsa_mla_list_status: n_list is NULL");
+    if (list_cap < 1)
+        return fail(QSA_ERR_INVALID, "qsa_mla_list_status: list_cap=%d", list_cap);
+    int32_t n = 0;
+    HIP_CHECK(hipMemcpyAsync(&n, n_list, sizeof(n), hipMemcpyDeviceToHost, (hipStream_t)stream));
+    HIP_CHECK(hipStreamSynchronize((hipStream_t)stream));
+    if (n_list_host)
+        *n_list_host = n;
+    if (n > list_cap)
+        return fail(QSA_ERR_CAPACITY,
+                    "qsa_mla_sparse_attn: %d positions visible, list_cap is %d (out is NaN)", n,
+                    list_cap);
+    return QSA_OK;
+}
+
 }  // extern "C"

@@ -4,7 +4,7 @@ import torch
 
 import oracle as O
 from sparse_attention_decode_qsa_amd import binding as qb
-from sparse_attention_decode_qsa_amd import synth
+import synth
 
 # Scores against the oracle run on the oracle's own pooled rows: max |delta| per row
 # <= SCORE_REL * max |score| (fp32 accumulation plus <= 1 binary16 ulp per pooled value).

@@ -179,3 +179,6 @@ def test_mla_preconditions(lib):
     assert lib.qsa_mla_sparse_attn(*args(6000, 3001)) == qb.QSA_ERR_UNSUPPORTED     # n < 2 cap
     assert lib.qsa_mla_sparse_attn(*args(8192, 1024, dkq=512)) == qb.QSA_ERR_UNSUPPORTED
     assert lib.qsa_mla_sparse_attn(*args(8192, 1024, hq=12)) == qb.QSA_ERR_UNSUPPORTED
+    # the capacity check after a list call rejects bad arguments on the host
+    assert lib.qsa_mla_list_status(None, 2048, None, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_mla_list_status(FAKE, 0, None, None) == qb.QSA_ERR_INVALID

@@ -3,7 +3,7 @@ only for the workload and kernel source it was taken on."""
 import json
 
 import bench
-from sparse_attention_decode_qsa_amd import synth
+import synth
 
 
 def test_stored_traffic_names_its_workload():

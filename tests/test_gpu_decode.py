@@ -5,7 +5,7 @@ import torch
 
 import oracle as O
 from sparse_attention_decode_qsa_amd import binding as qb
-from sparse_attention_decode_qsa_amd import synth
+import synth
 from _helpers import (SCORE_ABS_REL, SCORE_REL, assert_attn_close, assert_pool_close, cfg_of,
                       dev, host, setup_decode, shape_of)
 
@@ -355,18 +355,62 @@ def test_decode_step_small_contexts(gpu):
         check_step(w, L, cfg, g, o, L["n_prefix"], 0, qb.QSA_STEP_FUSED_GATHER)
 
 
+def test_decode_step_k1024_one_kv_head_cycle(gpu):
+    # k = 1024 with one KV head: up to 4 * 1024 + 3 = 4099 cells, 65 chunks of 64,
+    # more than the 64 splits one work group per chunk would need; every position
+    # of the 4-step cycle (tails 1, 2, 3 and a completed block)
+    w = small(4 * 3000 + 1, topk=1024, hq=8, hkv=1)
+    L, cfg, g, o = setup_decode(w)
+    n0 = L["n_prefix"]
+    for step in range(4):
+        check_step(w, L, cfg, g, o, n0 + step, step, qb.QSA_STEP_FUSED_GATHER)
+
+
+@pytest.mark.parametrize("n_tokens", [4 * 3000 + 2, 4 * 3000 + 3])
+def test_decode_multi_k1024_two_kv_heads(gpu, n_tokens):
+    # two verification rows with k = 1024 and two KV heads: rows of 4097 .. 4099 cells
+    w = small(n_tokens, topk=1024, hq=8, hkv=2)
+    L, cfg, g, o = setup_decode(w)
+    n0, n_q = L["n_prefix"], 2
+    q_idx = synth.normal_f16(85, (n_q, 16, 128))
+    q = synth.normal_f16(86, (n_q, 8, 128))
+    out = torch.empty((n_q, 8, 128), device="cuda")
+    ld = (n0 + n_q) // 4 + 3
+    scores = torch.empty((n_q, ld), device="cuda")
+    blk = torch.full((n_q, 1024), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, n_q, w.cap_tokens)
+    qb.qsa_decode_multi(cfg, g, n0, dev(q_idx), dev(L["k_idx_new"][:n_q]), dev(q),
+                        dev(L["k_new"][:n_q]), dev(L["v_new"][:n_q]), out, ws,
+                        scores_out=scores, ld_scores=ld, blk_out=blk)
+    for row in range(n_q):
+        ref = O.decode_step(shape_of(w), o.raw, o.pooled, o.k, o.v, n0 + row, q_idx[row],
+                            L["k_idx_new"][row], q[row], L["k_new"][row], L["v_new"][row])
+        nb = (n0 + row + 1) // 4
+        s_gpu = host(scores[row])[:nb]
+        assert np.max(np.abs(s_gpu - ref["scores64"])) <= SCORE_REL * np.max(np.abs(ref["scores64"]))
+        b_gpu = host(blk[row])[:min(1024, nb)]
+        assert np.array_equal(b_gpu, O.topk_sort(s_gpu, 1024)), row
+        ref_out = O.attn_cells(q[row], o.k, o.v, O.cells(b_gpu, n0 + row + 1), w.scale)
+        assert_attn_close(host(out[row]), ref_out, f"row {row}")
+
+
 @pytest.mark.parametrize("layer", [0, 7])
 def test_decode_step_255181_planted(gpu, layer):
     # the 256k workload, layer 0 and one other seeded layer: planted blocks are
-    # chosen, full parity
+    # chosen, full parity.  Layer 0 runs the whole cycle the benchmark times
+    # (positions N-1 .. N+2: tails 1, 2, 3, then the step that completes a block)
     w = synth.WORKLOADS["decode_255181"]
     L, cfg, g, o = setup_decode(w, layer)
     n0 = L["n_prefix"]
     # pooled cache built by the library vs the oracle, on 2000 sampled rows
     rows = np.sort(np.random.default_rng(1).choice(n0 // 4, 2000, replace=False))
     assert_pool_close(host(g.k_pool[torch.from_numpy(rows).cuda()]), o.pooled[rows])
-    b = check_step(w, L, cfg, g, o, n0, 0, qb.QSA_STEP_FUSED_GATHER)
-    assert set(L["planted"].tolist()) <= set(b.tolist())
+    for step in range(4 if layer == 0 else 1):
+        b = check_step(w, L, cfg, g, o, n0 + step, step, qb.QSA_STEP_FUSED_GATHER)
+        assert set(L["planted"].tolist()) <= set(b.tolist())
+    if layer == 0:
+        nb = (n0 + 4) // 4  # the block completed by the last step, pooled on the GPU
+        assert_pool_close(host(g.k_pool[nb - 1]), o.pooled[nb - 1])
 
 
 # ------------------------------------------------------------------ decode top-k on clustered scores

@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 from sparse_attention_decode_qsa_amd import binding as qb
-from sparse_attention_decode_qsa_amd import synth
+import synth
 from _helpers import assert_attn_close, dev, host
 
 pytestmark = pytest.mark.gpu
@@ -32,6 +32,8 @@ def test_mla_full_workload(gpu, runs):
     scale = 1.0 / np.sqrt(576)
     out, lst, nl, ws = run_mla(I["q"], I["kv"], I["mask"], w.list_len, scale)
     ref_list = np.flatnonzero(I["mask"] != -np.inf)
+    n_list = torch.tensor([nl], dtype=torch.int32, device="cuda")
+    assert qb.qsa_mla_list_status(n_list, w.list_len) == w.list_len
     assert nl == ref_list.size == w.list_len
     assert np.array_equal(lst[:nl], ref_list)
     assert np.array_equal(lst[:nl], O.mask_list(I["mask"]))
@@ -87,6 +89,12 @@ def test_mla_list_overflow_reports_count_and_nan(gpu):
     assert np.isnan(out).all()
     # the first list_cap entries are still the first visible positions
     assert np.array_equal(lst, np.flatnonzero(mask != -np.inf)[:1024])
+    # the host-side status call reports the overflow as a capacity error
+    n_list = torch.tensor([nl], dtype=torch.int32, device="cuda")
+    with pytest.raises(qb.QsaError) as e:
+        qb.qsa_mla_list_status(n_list, 1024)
+    assert e.value.status == qb.QSA_ERR_CAPACITY
+    assert qb.qsa_mla_list_status(n_list, visible) == visible
 
 
 def test_mla_nothing_visible(gpu):

@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 from sparse_attention_decode_qsa_amd import binding as qb
-from sparse_attention_decode_qsa_amd import synth
+import synth
 from _helpers import (SCORE_ABS_REL, SCORE_REL, OracleLayer, assert_attn_close, cfg_of, dev, host,
                       shape_of)
 

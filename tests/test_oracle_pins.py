@@ -12,7 +12,7 @@ import pytest
 from scipy.special import softmax
 
 import oracle as O
-from sparse_attention_decode_qsa_amd import synth
+import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")
 
