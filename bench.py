@@ -83,8 +83,20 @@ def decode_bytes(w, nb, cells):
     return scan, kv, small
 
 
+def host_threads() -> int:
+    """Host cores this process may use (its affinity mask), at most 16: the CPU share
+    of one GPU on the boxes this runs on."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def run_cpu_baseline(w, L, budget_s):
-    """The oracle's decode step on layer 0 of the same workload, single thread."""
+    """The oracle's decode step on layer 0 of the same workload, timed two ways:
+    (i) the parity oracle on one thread; (ii) the same step with its block scan split
+    over every usable host core (oracle/qsa_oracle_mt.c; identical results)."""
     import oracle as O
     n0 = L["n_prefix"]
     cap = w.cap_tokens
@@ -97,19 +109,32 @@ def run_cpu_baseline(w, L, budget_s):
     kc[:n0], vc[:n0] = L["k"], L["v"]
     log(f"[cpu] oracle cache build {time.time() - t0:.1f}s")
     sh = O.Shape(w.h_idx, w.d_idx, w.topk, w.hq, w.hkv, w.d, w.dv)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        j = steps % 4
-        O.decode_step(sh, raw, pooled, kc, vc, n0 + j, L["q_idx"], L["k_idx_new"][j], L["q"],
-                      L["k_new"][j], L["v_new"][j])
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 64:
-            break
-    return dict(value=steps / el, unit="layer-steps/s", cores=1, kind="oracle",
-                sample=f"{steps} oracle decode steps on layer 0 at N={w.n_tokens} "
-                       f"(positions cycling N-1..N+2), single thread, {el:.1f} s")
+
+    def timed(step, budget):
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            j = steps % 4
+            step(n0 + j, L["k_idx_new"][j], L["k_new"][j], L["v_new"][j])
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or steps >= 64:
+                return steps, el
+
+    one = lambda n, ki, kn, vn: O.decode_step(sh, raw, pooled, kc, vc, n, L["q_idx"], ki,
+                                               L["q"], kn, vn)
+    s1, e1 = timed(one, budget_s * 2 / 3)
+    threads = host_threads()
+    many = lambda n, ki, kn, vn: O.decode_step_mt(sh, raw, pooled, kc, vc, n, L["q_idx"], ki,
+                                                   L["q"], kn, vn, threads=threads)
+    s2, e2 = timed(many, budget_s / 3)
+    log(f"[cpu] oracle: 1 thread {s1 / e1:.2f}, {threads} threads {s2 / e2:.2f} layer-steps/s")
+    return dict(value=s1 / e1, unit="layer-steps/s", cores=1, kind="oracle",
+                sample=f"{s1} oracle decode steps on layer 0 at N={w.n_tokens} "
+                       f"(positions cycling N-1..N+2), single thread, {e1:.1f} s",
+                all_cores=dict(value=s2 / e2, unit="layer-steps/s", cores=threads,
+                               sample=f"{s2} oracle decode steps, same positions, block scan "
+                                      f"split over {threads} threads, {e2:.1f} s"))
 
 
 def bench_decode(args):
@@ -441,28 +466,46 @@ def bench_prefill(args):
 
 
 def cpu_baseline_prefill(w, I, budget_s):
-    """Oracle prefill rows (each a decode-equivalent row), single thread."""
+    """Oracle prefill rows (each a decode-equivalent row): (i) one thread, (ii) rows
+    spread over every usable host core (the oracle releases the interpreter lock)."""
     import oracle as O
+    from concurrent.futures import ThreadPoolExecutor
     depth = I["depth"]
     n_all = depth + w.n_q
     t0 = time.time()
     pooled = O.pool_rebuild(I["raw"], n_all)
     log(f"[cpu] oracle pooled rebuild {time.time() - t0:.1f}s")
     sh = O.Shape(w.h_idx, w.d_idx, w.topk, w.hq, w.hkv, w.d, w.dv)
+
+    def row(i):
+        r = (i * 97) % w.n_q
+        O.prefill_row(sh, pooled, I["k"], I["v"], depth + r, I["q_idx"][r], I["q"][r])
+
     rows = 0
     t0 = time.perf_counter()
     while True:
-        r = (rows * 97) % w.n_q
-        O.prefill_row(sh, pooled, I["k"], I["v"], depth + r, I["q_idx"][r], I["q"][r])
+        row(rows)
         rows += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or rows >= 64:
+        if el >= budget_s * 2 / 3 or rows >= 64:
             break
+    threads = host_threads()
+    n_mt = min(64, 4 * threads)
+    t1 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(row, range(n_mt)))
+    el_mt = time.perf_counter() - t1
+    log(f"[cpu] oracle prefill rows: 1 thread {rows / el:.2f}/s, {threads} threads "
+        f"{n_mt / el_mt:.2f}/s")
     return dict(value=rows / el, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{rows} oracle prefill rows of the chunk (positions depth+r), single "
                        f"thread, {el:.1f} s",
                 measured_rows=rows,
-                extrapolated_chunk_s=round(w.n_q * el / rows, 1))
+                extrapolated_chunk_s=round(w.n_q * el / rows, 1),
+                all_cores=dict(value=n_mt / el_mt, unit="tokens/s", cores=threads,
+                               sample=f"{n_mt} oracle prefill rows on {threads} threads, "
+                                      f"{el_mt:.1f} s",
+                               extrapolated_chunk_s=round(w.n_q * el_mt / n_mt, 1)))
 
 
 def bench_mla(args):
@@ -602,7 +645,8 @@ def host_cpu() -> dict:
                     break
     except OSError:
         pass
-    return {"cpu_model": model, "host_logical_cores": os.cpu_count()}
+    return {"cpu_model": model, "host_logical_cores": os.cpu_count(),
+            "usable_cores": host_threads()}
 
 
 if __name__ == "__main__":

@@ -24,12 +24,21 @@ _LIB = os.path.join(_HERE, "libqsa_oracle.so")
 BLOCK = 4
 
 
+_SRC_MT = os.path.join(_HERE, "qsa_oracle_mt.c")
+_LIB_MT = os.path.join(_HERE, "libqsa_oracle_mt.so")
+CFLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fPIC"]
+
+
 def build() -> str:
-    """Compile qsa_oracle.c with gcc (strict IEEE: no fast-math, no contraction)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fPIC",
-           "-shared", "-o", _LIB + ".tmp", _SRC, "-lm"]
+    """Compile qsa_oracle.c with gcc (strict IEEE: no fast-math, no contraction) into
+    the parity library, and, as a second library, the same source together with
+    qsa_oracle_mt.c (the all-core timing form of the decode step)."""
+    cmd = ["gcc", *CFLAGS, "-shared", "-o", _LIB + ".tmp", _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
+    cmd = ["gcc", *CFLAGS, "-pthread", "-shared", "-o", _LIB_MT + ".tmp", _SRC, _SRC_MT, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_MT + ".tmp", _LIB_MT)
     return _LIB
 
 
@@ -71,6 +80,25 @@ def lib():
             f.argtypes = args
         _lib = L
     return _lib
+
+
+_lib_mt = None
+
+
+def lib_mt():
+    """The timing library (qsa_oracle.c + qsa_oracle_mt.c); used only to time the
+    oracle over all host cores."""
+    global _lib_mt
+    if _lib_mt is None:
+        if not os.path.exists(_LIB_MT):
+            build()
+        L = C.CDLL(_LIB_MT)
+        p, i64 = C.c_void_p, C.c_int64
+        L.orc_decode_step_mt.restype = i64
+        L.orc_decode_step_mt.argtypes = [p, p, p, p, p, i64, p, p, p, p, p, p, p, p, p, p,
+                                         C.c_int]
+        _lib_mt = L
+    return _lib_mt
 
 
 class _Cfg(C.Structure):
@@ -243,6 +271,30 @@ def decode_step(shape: Shape, raw, pooled, k_cache, v_cache, n_before, q_idx, k_
                                _ptr(_f16(q)), _ptr(_f16(k_new)), _ptr(_f16(v_new)), _ptr(wv),
                                _ptr(s64), _ptr(s32), _ptr(blk), _ptr(out))
     return dict(scores64=s64, scores32=s32, blk=blk[:ns], out=out)
+
+
+def decode_step_mt(shape: Shape, raw, pooled, k_cache, v_cache, n_before, q_idx, k_idx_new,
+                   q, k_new, v_new, threads: int, rms_w=None):
+    """decode_step with the block scan split over `threads` POSIX threads (timing form:
+    each thread runs the same per-block fp64 sum on its own block range, so the
+    results equal decode_step's)."""
+    n = n_before + 1
+    nb = n // BLOCK
+    s64 = np.empty(max(nb, 1), np.float64)
+    s32 = np.empty(max(nb, 1), np.float32)
+    blk = np.empty(max(min(shape.topk, nb), 1), np.int32)
+    out = np.empty((shape.hq, shape.dv), np.float64)
+    wv = None if rms_w is None else np.ascontiguousarray(rms_w, np.float32)
+    cfg = shape.c()
+    for a in (raw, pooled, k_cache, v_cache):
+        assert a.flags.c_contiguous and a.dtype == np.float16
+    assert n <= raw.shape[0] and n <= k_cache.shape[0] and nb <= pooled.shape[0]
+    ns = lib_mt().orc_decode_step_mt(C.byref(cfg), _ptr(raw), _ptr(pooled), _ptr(k_cache),
+                                     _ptr(v_cache), n_before, _ptr(_f16(q_idx)),
+                                     _ptr(_f16(k_idx_new)), _ptr(_f16(q)), _ptr(_f16(k_new)),
+                                     _ptr(_f16(v_new)), _ptr(wv), _ptr(s64), _ptr(s32), _ptr(blk),
+                                     _ptr(out), int(threads))
+    return dict(scores64=s64[:nb], scores32=s32[:nb], blk=blk[:ns], out=out)
 
 
 def prefill_row(shape: Shape, pooled, k_cache, v_cache, pos, q_idx_row, q_row):

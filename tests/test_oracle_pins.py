@@ -360,6 +360,34 @@ def test_decode_step_selects_planted_blocks():
     assert s[L["planted"]].min() > 0.9 * 4 * 64
 
 
+def test_all_core_timing_form_equals_decode_step():
+    # the benchmark's all-core oracle timing splits only the block scan over threads;
+    # every result is the single-threaded decode step's, bit for bit
+    w = synth.Workload("mt_small", 9, "decode", 4 * 3000 + 2, h_idx=4, d_idx=64, topk=32,
+                       hq=4, hkv=1, d=32, dv=32)
+    L = synth.decode_layer(w, 0)
+    n0 = L["n_prefix"]
+    sh = O.Shape(4, 64, 32, 4, 1, 32, 32)
+    cap = n0 + 8
+
+    def caches():
+        raw = np.zeros((cap, 4, 64), np.float16)
+        pooled = np.zeros((cap // 4, 4, 64), np.float16)
+        Kc = np.zeros((cap, 1, 32), np.float16)
+        Vc = np.zeros((cap, 1, 32), np.float16)
+        O.pool_append(L["raw"], 0, raw, pooled)
+        Kc[:n0], Vc[:n0] = L["k"], L["v"]
+        return raw, pooled, Kc, Vc
+
+    args = (n0, L["q_idx"], L["k_idx_new"][0], L["q"], L["k_new"][0], L["v_new"][0])
+    ref = O.decode_step(sh, *caches(), *args)
+    for threads in (1, 3, 8, 64):
+        got = O.decode_step_mt(sh, *caches(), *args, threads=threads)
+        assert np.array_equal(got["scores64"], ref["scores64"])
+        assert np.array_equal(got["blk"], ref["blk"])
+        assert np.array_equal(got["out"], ref["out"])
+
+
 def test_prefill_row_equals_decode_at_that_length():
     sh = O.Shape(2, 32, 8, 4, 2, 32, 32)
     n_all = 4 * 40 + 3
