@@ -531,10 +531,10 @@ int32_t union_group_rows(int32_t hq, int32_t hkv) { return 128 / (hq / hkv); }
 
 int32_t union_splits(int32_t n_q, int32_t hq, int32_t hkv)
 {
-    const int32_t groups = (n_q + union_group_rows(hq, hkv) - 1) / union_group_rows(hq, hkv);
-    const int32_t wgs = groups * hkv;
-    int32_t s = (kUnionTargetWgs + wgs - 1) / wgs;
-    return s < 1 ? 1 : (s > kUnionMaxSplits ? kUnionMaxSplits : s);
+    const int64_t G = union_group_rows(hq, hkv);
+    const int64_t wgs = (((int64_t)n_q + G - 1) / G) * hkv;
+    const int64_t s = (kUnionTargetWgs + wgs - 1) / wgs;
+    return s < 1 ? 1 : (s > kUnionMaxSplits ? kUnionMaxSplits : (int32_t)s);
 }
 
 hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s)

@@ -123,7 +123,7 @@ Layout layout(const qsa_config *c, int32_t n_q, int32_t n_ctx)
     size_t groups = 0, cap_u = 0, usplits = 0;
     if (union_supported(c->hq, c->hkv, c->d, c->dv, c->topk_blocks)) {
         const int32_t G = union_group_rows(c->hq, c->hkv);
-        groups = (size_t)((n_q + G - 1) / G);
+        groups = (size_t)(((int64_t)n_q + G - 1) / G);
         cap_u = (size_t)G * c->topk_blocks;
         const int32_t sp = union_splits(n_q, c->hq, c->hkv);
         usplits = sp > 1 ? (size_t)sp : 0;
