@@ -45,6 +45,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every entry point below is exported from the shared library; nothing else is. */
+#if defined(__GNUC__) || defined(__clang__)
+#define QSA_API __attribute__((visibility("default")))
+#else
+#define QSA_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -98,23 +105,23 @@ typedef struct qsa_layer_bufs {
 } qsa_layer_bufs;
 
 /* Text for a status code. */
-const char *qsa_status_string(int status);
+QSA_API const char *qsa_status_string(int status);
 
 /* Message for the calling thread's last failed call ("" if none). */
-const char *qsa_last_error(void);
+QSA_API const char *qsa_last_error(void);
 
 /* QSA_OK if cfg describes a shape the kernels implement. */
-int qsa_config_check(const qsa_config *cfg);
+QSA_API int qsa_config_check(const qsa_config *cfg);
 
 /*
  * Workspace bytes for calls with up to n_q query rows over contexts of up to
  * n_ctx tokens (n_ctx <= cap_tokens).  Returns 0 for an invalid cfg.
  */
-size_t qsa_workspace_size(const qsa_config *cfg, int32_t n_q, int32_t n_ctx);
+QSA_API size_t qsa_workspace_size(const qsa_config *cfg, int32_t n_q, int32_t n_ctx);
 
 /* Clears a workspace (a fill kernel on `stream`).  Optional: no call reads a
  * workspace byte it has not written in the same call. */
-int qsa_workspace_init(void *ws, size_t ws_bytes, qsa_stream_t stream);
+QSA_API int qsa_workspace_init(void *ws, size_t ws_bytes, qsa_stream_t stream);
 
 /*
  * Pooled-key cache append (Qiita part 10, "QSAとQSA indexerについて" and
@@ -127,7 +134,7 @@ int qsa_workspace_init(void *ws, size_t ws_bytes, qsa_stream_t stream);
  * token-by-token calls give the same bits.
  * Errors: INVALID (null, n_new < 0, n_before < 0), CAPACITY (n_before + n_new > cap_tokens).
  */
-int qsa_pool_append(const qsa_config *cfg, const uint16_t *k_new, int32_t n_new,
+QSA_API int qsa_pool_append(const qsa_config *cfg, const uint16_t *k_new, int32_t n_new,
                     int32_t n_before, uint16_t *k_raw, uint16_t *k_pool, const float *rms_w,
                     qsa_stream_t stream);
 
@@ -145,11 +152,11 @@ int qsa_pool_append(const qsa_config *cfg, const uint16_t *k_new, int32_t n_new,
  * Errors: INVALID (null k_raw/k_pool, n_tokens outside [0, cap_tokens], b_from
  * outside [0, floor(n_tokens/4)]).
  */
-int qsa_pool_rebuild(const qsa_config *cfg, const uint16_t *k_raw, uint16_t *k_pool,
+QSA_API int qsa_pool_rebuild(const qsa_config *cfg, const uint16_t *k_raw, uint16_t *k_pool,
                      const float *rms_w, int32_t b_from, int32_t n_tokens, qsa_stream_t stream);
 
 /* Copies k_new/v_new [n_new][hkv][d|dv] to cache rows [n_before, n_before+n_new). */
-int qsa_kv_append(const qsa_config *cfg, const uint16_t *k_new, const uint16_t *v_new,
+QSA_API int qsa_kv_append(const qsa_config *cfg, const uint16_t *k_new, const uint16_t *v_new,
                   int32_t n_new, int32_t n_before, uint16_t *k_cache, uint16_t *v_cache,
                   qsa_stream_t stream);
 
@@ -162,7 +169,7 @@ int qsa_kv_append(const qsa_config *cfg, const uint16_t *k_new, const uint16_t *
  * n_q == 1 streams the pooled cache once (decode); n_q > 1 runs an MFMA
  * contraction (prefill chunk).
  */
-int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, int32_t pos0,
+QSA_API int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, int32_t pos0,
                     const uint16_t *k_pool, float *scores, int32_t ld, qsa_stream_t stream);
 
 /*
@@ -172,7 +179,7 @@ int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, i
  * lower block id, -0 equal to +0, NaN lowest.  blk[r*k ..] receives the chosen
  * ids in ascending order.  Deterministic: the result depends only on the scores.
  */
-int qsa_topk_blocks(const qsa_config *cfg, const float *scores, int32_t n_q, int32_t ld,
+QSA_API int qsa_topk_blocks(const qsa_config *cfg, const float *scores, int32_t n_q, int32_t ld,
                     int32_t pos0, int32_t *blk, int32_t *n_sel, void *ws, size_t ws_bytes,
                     qsa_stream_t stream);
 
@@ -183,7 +190,7 @@ int qsa_topk_blocks(const qsa_config *cfg, const float *scores, int32_t n_q, int
  * then the tail tokens [4*floor(n_tokens/4), n_tokens).  Rows written:
  * 4*n_blk + n_tokens mod 4.  n_blk must equal min(k, floor(n_tokens/4)).
  */
-int qsa_gather_kv(const qsa_config *cfg, const int32_t *blk, int32_t n_blk, int32_t n_tokens,
+QSA_API int qsa_gather_kv(const qsa_config *cfg, const int32_t *blk, int32_t n_blk, int32_t n_tokens,
                   const uint16_t *k_cache, const uint16_t *v_cache, uint16_t *k_sel,
                   uint16_t *v_sel, qsa_stream_t stream);
 
@@ -193,7 +200,7 @@ int qsa_gather_kv(const qsa_config *cfg, const int32_t *blk, int32_t n_blk, int3
  * sum_c softmax_c(attn_scale * <q[h], k_sel[c][g]>) v_sel[c][g][j] with
  * g = h / (hq/hkv).  Split over cells, fp32 partials, one combining pass.
  */
-int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint16_t *k_sel,
+QSA_API int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint16_t *k_sel,
                     const uint16_t *v_sel, int32_t n_cells, float *out, void *ws,
                     size_t ws_bytes, qsa_stream_t stream);
 
@@ -218,7 +225,7 @@ int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint16_t *k_
  * qsa_workspace_size(cfg, n_q, pos0 + n_q).  Both forms drop a chosen id outside
  * the row's [0, nb_r).
  */
-int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int32_t pos0,
+QSA_API int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int32_t pos0,
                      const int32_t *blk, int32_t ldb, const uint16_t *k_cache,
                      const uint16_t *v_cache, float *out, uint32_t flags, void *ws,
                      size_t ws_bytes, qsa_stream_t stream);
@@ -235,7 +242,7 @@ int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int3
  * QSA_STEP_COMPACT_GATHER (separate top-k and gather launches, then attention
  * over the compact rows).
  */
-int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
+QSA_API int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
                     const uint16_t *q_idx, const uint16_t *k_idx_new, const uint16_t *q,
                     const uint16_t *k_new, const uint16_t *v_new, float *out, float *scores_out,
                     int32_t *blk_out, uint32_t flags, void *ws, size_t ws_bytes,
@@ -257,7 +264,7 @@ int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_be
  * Errors: INVALID (n_q outside [1, 4], ld_scores too small, null or misaligned
  * pointers), CAPACITY (n_before + n_q > cap_tokens, workspace too small).
  */
-int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
+QSA_API int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
                      int32_t n_q, const uint16_t *q_idx, const uint16_t *k_idx_new,
                      const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, float *out,
                      float *scores_out, int32_t ld_scores, int32_t *blk_out, void *ws,
@@ -271,7 +278,7 @@ int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_b
  * Optional outputs: scores_out [n_new][ld_scores], blk_out [n_new][k].
  * flags: QSA_PREFILL_PER_ROW or QSA_PREFILL_GROUPED_UNION, as for qsa_prefill_attn.
  */
-int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
+QSA_API int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
                      int32_t n_new, const uint16_t *q_idx, const uint16_t *k_idx_new,
                      const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, float *out,
                      float *scores_out, int32_t ld_scores, int32_t *blk_out, uint32_t flags,
@@ -293,8 +300,8 @@ int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_b
  * on the device when the call returns, so the capacity error reaches the host
  * through qsa_mla_list_status() below (the call itself stays asynchronous).
  */
-size_t qsa_mla_workspace_size(int32_t hq, int32_t dv, int32_t list_cap);
-int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const uint16_t *v,
+QSA_API size_t qsa_mla_workspace_size(int32_t hq, int32_t dv, int32_t list_cap);
+QSA_API int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const uint16_t *v,
                         int32_t dkq, int32_t dv, const uint16_t *mask, int32_t n,
                         int32_t list_cap, float scale, int32_t *list_out, int32_t *n_list,
                         float *out, void *ws, size_t ws_bytes, qsa_stream_t stream);
@@ -307,7 +314,7 @@ int qsa_mla_sparse_attn(const uint16_t *q, int32_t hq, const uint16_t *kv, const
  * memory) receives the count.  Blocks the calling thread; not for graph capture.
  * Errors: INVALID (n_list NULL, list_cap < 1), HIP (copy or wait failed).
  */
-int qsa_mla_list_status(const int32_t *n_list, int32_t list_cap, int32_t *n_list_host,
+QSA_API int qsa_mla_list_status(const int32_t *n_list, int32_t list_cap, int32_t *n_list_host,
                         qsa_stream_t stream);
 
 #ifdef __cplusplus

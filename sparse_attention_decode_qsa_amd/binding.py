@@ -327,3 +327,4 @@ def qsa_mla_list_status(n_list, list_cap: int) -> int:
     _check(load().qsa_mla_list_status(_ptr(n_list, torch.int32, name="n_list"), list_cap,
                                       C.byref(n), _stream()))
     return int(n.value)
+

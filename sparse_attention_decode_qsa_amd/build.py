@@ -22,6 +22,8 @@ FLAGS = [
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    # host symbols hidden unless qsa.h exports them (QSA_API)
+    "-Xarch_host", "-fvisibility=hidden",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

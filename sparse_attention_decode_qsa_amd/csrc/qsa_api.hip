@@ -581,7 +581,7 @@ int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint16_t *k_
 
 // Attention of a prefill chunk over each row's chosen blocks and tail: per row, or
 // (QSA_PREFILL_GROUPED_UNION) per group of rows over the union of their blocks.
-hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32_t n_q, int32_t pos0,
+static hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32_t n_q, int32_t pos0,
                                const int32_t *blk, int32_t ldb, const h16 *kc, const h16 *vc,
                                float *out, uint32_t flags, void *ws, const Layout &L,
                                hipStream_t s)
@@ -622,7 +622,7 @@ hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32_t n_q,
     return launch_attn(a, cfg->d, cfg->dv, s);
 }
 
-int check_prefill_flags(const qsa_config *cfg, uint32_t flags, const char *fn)
+static int check_prefill_flags(const qsa_config *cfg, uint32_t flags, const char *fn)
 {
     if (flags & ~QSA_PREFILL_GROUPED_UNION)
         return fail(QSA_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
