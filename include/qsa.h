@@ -249,6 +249,29 @@ QSA_API int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *L, int3
                     qsa_stream_t stream);
 
 /*
+ * qsa_decode_step for callers that cannot allocate or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid device allocation.
+ * Same arguments, results and kernels as qsa_decode_step, without ws/ws_bytes: the
+ * scratch is a static array of QSA_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU, which each GPU keeps until the process ends (its address is looked up
+ * once per device, on that device's first call).  The call allocates nothing.
+ * The device current on the calling thread must be the stream's device.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and give undefined results; serialise
+ * them.  The array keeps the last call's contents; no call reads a byte of it that
+ * the same call did not write, so nothing needs clearing.
+ * Errors: as qsa_decode_step; CAPACITY also when the shape's scratch
+ * (qsa_workspace_size(cfg, 1, n_before + 1)) exceeds QSA_NOALLOC_SCRATCH_BYTES;
+ * INVALID when the stream belongs to another device.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+QSA_API int qsa_decode_step_noalloc(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
+                            const uint16_t *q_idx, const uint16_t *k_idx_new, const uint16_t *q,
+                            const uint16_t *k_new, const uint16_t *v_new, float *out,
+                            float *scores_out, int32_t *blk_out, uint32_t flags,
+                            qsa_stream_t stream);
+
+/*
  * Multi-query decode step for checking speculative draft tokens (Qiita part 12,
  * 「MTPを入れたらPPが遅くなるのは仕方がないのか？」: the target model checks the
  * draft's tokens together; its setup table runs DraftMax = 2, so a step carries

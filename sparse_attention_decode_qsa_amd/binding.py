@@ -34,7 +34,9 @@ EXPORTS = [
     "qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_attn",
     "qsa_prefill_attn", "qsa_decode_step", "qsa_decode_multi", "qsa_prefill_step",
     "qsa_mla_workspace_size", "qsa_mla_sparse_attn", "qsa_mla_list_status",
+    "qsa_decode_step_noalloc",
 ]
+QSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class QsaError(RuntimeError):
@@ -92,6 +94,8 @@ def load():
         "qsa_mla_sparse_attn": (C.c_int, [p, i32, p, p, i32, i32, p, i32, i32, C.c_float, p, p,
                                           p, p, sz, p]),
         "qsa_mla_list_status": (C.c_int, [p, i32, C.POINTER(i32), p]),
+        "qsa_decode_step_noalloc": (C.c_int, [cfg, C.POINTER(qsa_layer_bufs), i32, p, p, p, p,
+                                              p, p, p, p, u32, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -328,3 +332,16 @@ def qsa_mla_list_status(n_list, list_cap: int) -> int:
                                       C.byref(n), _stream()))
     return int(n.value)
 
+
+def qsa_decode_step_noalloc(cfg, layer, n_before: int, q_idx, k_idx_new, q, k_new, v_new, out,
+                            scores_out=None, blk_out=None,
+                            flags: int = QSA_STEP_FUSED_GATHER) -> None:
+    """qsa_decode_step with the library's static scratch instead of a workspace."""
+    c = cfg.c()
+    b = layer.bufs()
+    _check(load().qsa_decode_step_noalloc(
+        C.byref(c), C.byref(b), n_before, _ptr(q_idx, H16, name="q_idx"),
+        _ptr(k_idx_new, H16, name="k_idx_new"), _ptr(q, H16, name="q"),
+        _ptr(k_new, H16, name="k_new"), _ptr(v_new, H16, name="v_new"),
+        _ptr(out, torch.float32, name="out"), _ptr(scores_out, torch.float32, name="scores_out"),
+        _ptr(blk_out, torch.int32, name="blk_out"), flags, _stream()))

@@ -327,6 +327,43 @@ int decode_impl(const char *fn, const qsa_config *cfg, const qsa_layer_bufs *Lb,
     return attn_decode_launch(cfg, a, cells, ws, L, s);
 }
 
+// Scratch of qsa_decode_step_noalloc: one array per GPU, in the library's code
+// object, kept until the process ends.  Host code never uses the array's name as
+// an address (on the host it stands in for the symbol only); the device address
+// comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = QSA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`; the stream must belong to that device.
+int static_scratch(hipStream_t stream, void **out, const char *fn)
+{
+    int dev = -1;
+    HIP_CHECK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn,
+                    dev, kMaxDevices);
+    if (stream) {
+        hipDevice_t sd = -1;
+        HIP_CHECK(hipStreamGetDevice(stream, &sd));
+        if (sd != dev)
+            return fail(QSA_ERR_INVALID, "%s: the stream belongs to device %d, device %d is current",
+                        fn, (int)sd, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p || !aligned16(p))
+            return fail(QSA_ERR_HIP, "%s: no usable address for the scratch array", fn);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -671,6 +708,32 @@ int qsa_decode_step(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_b
 {
     return decode_impl(__func__, cfg, Lb, n_before, 1, q_idx, k_idx_new, q, k_new, v_new, out,
                        scores_out, 0, blk_out, flags, ws, ws_bytes, stream);
+}
+
+int qsa_decode_step_noalloc(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_before,
+                            const uint16_t *q_idx, const uint16_t *k_idx_new, const uint16_t *q,
+                            const uint16_t *k_new, const uint16_t *v_new, float *out,
+                            float *scores_out, int32_t *blk_out, uint32_t flags,
+                            qsa_stream_t stream)
+{
+    int r = check_cfg(cfg);
+    if (r)
+        return r;
+    if (n_before < 0 || n_before >= cfg->cap_tokens)
+        return fail(n_before < 0 ? QSA_ERR_INVALID : QSA_ERR_CAPACITY,
+                    "qsa_decode_step_noalloc: n_before=%d outside [0, %d)", n_before,
+                    cfg->cap_tokens);
+    const size_t need = layout(cfg, 1, n_before + 1).total;
+    if (need > kStaticScratchBytes)
+        return fail(QSA_ERR_CAPACITY,
+                    "qsa_decode_step_noalloc: this shape needs %zu bytes of scratch, the "
+                    "library's static scratch holds %zu (use qsa_decode_step)",
+                    need, kStaticScratchBytes);
+    void *ws = nullptr;
+    if ((r = static_scratch((hipStream_t)stream, &ws, __func__)))
+        return r;
+    return decode_impl(__func__, cfg, Lb, n_before, 1, q_idx, k_idx_new, q, k_new, v_new, out,
+                       scores_out, 0, blk_out, flags, ws, kStaticScratchBytes, stream);
 }
 
 int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *Lb, int32_t n_before,
