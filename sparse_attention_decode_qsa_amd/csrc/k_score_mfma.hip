@@ -9,11 +9,19 @@
 // Tiling: a work group computes a 256 (queries) x 256 (blocks) tile; its 8
 // waves each own 128 x 64 (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).
 // Every 32-feature step stages A (16 KiB) and B (16 KiB) in LDS with rows padded
-// to 80 bytes (conflict-free 16-byte fragment reads).  Two LDS buffers and two
+// to 80 bytes (conflict-free 16-byte fragment reads).  Two LDS buffers and four
 // register sets: while step s is multiplied, step s + 1 waits in registers to be
-// stored into the other buffer and step s + 2's global loads are in flight, so a
-// load has two steps of MFMA work to arrive, and a step needs one barrier.
-// Blocks at or past the last row's causal bound are neither read nor written.
+// stored into the other buffer and the global loads of steps s + 2 .. s + 4 are
+// in flight, and a step needs one barrier.  Every load is issued unconditionally
+// (indexes clamped into the operands), so the compiler waits only for the oldest
+// register set: a load under a branch made it wait for all of them, which left one
+// step of work to cover a load.  Blocks at or past the last row's causal bound are
+// never written.
+//
+// On this shape (1,024 queries x 31,819 blocks x 2,048 features) the kernel is
+// bound by LDS traffic, not by the matrix cores: a step moves 32 KiB into LDS and
+// 96 KiB out of it per CU, which at 128 bytes per clock takes as long as the
+// step's MFMA work; the score tile's fp32 stores (130 MB per chunk) add the rest.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -25,108 +33,117 @@ constexpr int PITCH = TK + 8;  // halfs per LDS row (80 bytes)
 constexpr int WM = 128, WN = 64;
 constexpr int FI = WM / 16, FJ = WN / 16;
 
+// Tile order: the 1-D grid is dealt to the 8 XCDs round-robin (work group i runs
+// on XCD i mod 8), and each XCD takes its work groups in order.  Work group i is
+// mapped so that an XCD's consecutive work groups are the row tiles of one
+// block-column tile, c = 8 * (j / nrow) + (i mod 8) with j = i / 8: those tiles run
+// side by side on one L2, which then fetches the column's pooled rows once.
+constexpr int kXcds = 8;
+constexpr int NS = 4;  // register sets: a step's loads are issued NS steps ahead
+
 __global__ __launch_bounds__(kThreads, 1) void score_prefill_kernel(const h16 *__restrict__ Q,
                                                                  int32_t n_q, int32_t pos0,
                                                                  const h16 *__restrict__ P,
                                                                  int32_t K, float *__restrict__ S,
-                                                                 int32_t ld)
+                                                                 int32_t ld, int32_t ncol,
+                                                                 int32_t nrow)
 {
     __shared__ __attribute__((aligned(16))) h16 As[2][TM * PITCH];
     __shared__ __attribute__((aligned(16))) h16 Bs[2][TN * PITCH];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 2, wn = wave & 3;
-    const int32_t r0 = blockIdx.y * TM;
-    const int32_t c0 = blockIdx.x * TN;
+    const int32_t j = (int32_t)blockIdx.x / kXcds;
+    const int32_t col = kXcds * (j / nrow) + (int32_t)blockIdx.x % kXcds;
+    if (col >= ncol)
+        return;
+    const int32_t r0 = (j % nrow) * TM;
+    const int32_t c0 = col * TN;
     const int32_t nb_max = (pos0 + n_q) / kBlockTokens;
 
-    // global -> register staging: A: 2 x 16B per thread, B: 2 x 16B per thread
+    // global -> register staging: A: 2 x 16B per thread, B: 2 x 16B per thread.
+    // Rows past the last query / last block are clamped to it (their products are
+    // never stored) and feature offsets past the end to the last step (the loads
+    // issued ahead of the last steps are never used).
     const int lr = t >> 2, lk = (t & 3) * 8;
-    h16x8 ga0[2], gb0[2], ga1[2], gb1[2];
-    auto gload = [&](h16x8 (&ga)[2], h16x8 (&gb)[2], int k0) {
+    const h16 *qa[2], *pb[2];
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int32_t r = r0 + lr + 128 * j;
-            ga[j] = (r < n_q) ? *(const h16x8 *)(Q + (int64_t)r * K + k0 + lk)
-                              : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+    for (int i = 0; i < 2; i++) {
+        qa[i] = Q + (int64_t)min(r0 + lr + 128 * i, n_q - 1) * K + lk;
+        pb[i] = P + (int64_t)min(c0 + lr + 128 * i, nb_max - 1) * K + lk;
+    }
+    h16x8 ga[NS][2], gb[NS][2];
+    auto gload = [&](int u, int k0) {
+        k0 = min(k0, K - TK);
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int32_t c = c0 + lr + 128 * j;
-            gb[j] = (c < nb_max) ? *(const h16x8 *)(P + (int64_t)c * K + k0 + lk)
-                                 : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        for (int i = 0; i < 2; i++)
+            ga[u][i] = *(const h16x8 *)(qa[i] + k0);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            gb[u][i] = *(const h16x8 *)(pb[i] + k0);
     };
-    auto sstore = [&](const h16x8 (&ga)[2], const h16x8 (&gb)[2], h16 *as, h16 *bs) {
+    auto sstore = [&](int u, h16 *as, h16 *bs) {
 #pragma unroll
-        for (int j = 0; j < 2; j++)
-            *(h16x8 *)&as[(lr + 128 * j) * PITCH + lk] = ga[j];
+        for (int i = 0; i < 2; i++)
+            *(h16x8 *)&as[(lr + 128 * i) * PITCH + lk] = ga[u][i];
 #pragma unroll
-        for (int j = 0; j < 2; j++)
-            *(h16x8 *)&bs[(lr + 128 * j) * PITCH + lk] = gb[j];
+        for (int i = 0; i < 2; i++)
+            *(h16x8 *)&bs[(lr + 128 * i) * PITCH + lk] = gb[u][i];
     };
 
     f32x4 acc[FI][FJ];
 #pragma unroll
     for (int i = 0; i < FI; i++)
 #pragma unroll
-        for (int j = 0; j < FJ; j++)
-            acc[i][j] = f32x4{0, 0, 0, 0};
+        for (int jj = 0; jj < FJ; jj++)
+            acc[i][jj] = f32x4{0, 0, 0, 0};
 
     const int fr = lane & 15, fk = (lane >> 4) * 8;
     auto mma = [&](const h16 *as, const h16 *bs) {
         h16x8 b[FJ];
 #pragma unroll
-        for (int j = 0; j < FJ; j++)
-            b[j] = *(const h16x8 *)&bs[(wn * WN + j * 16 + fr) * PITCH + fk];
+        for (int jj = 0; jj < FJ; jj++)
+            b[jj] = *(const h16x8 *)&bs[(wn * WN + jj * 16 + fr) * PITCH + fk];
 #pragma unroll
         for (int i = 0; i < FI; i++) {
             const h16x8 a = *(const h16x8 *)&as[(wm * WM + i * 16 + fr) * PITCH + fk];
 #pragma unroll
-            for (int j = 0; j < FJ; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
+            for (int jj = 0; jj < FJ; jj++)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[jj], acc[i][jj], 0, 0, 0);
         }
     };
 
-    // step s is read from buffer s % 2; register set s % 2 carries step s (and
-    // later s + 2) from global memory to its buffer.  The loop runs over pairs of
-    // steps so that each register set has a fixed name.
+    // step s is read from buffer s % 2 and travels in register set s % NS.  K is a
+    // multiple of NS * TK (host check), so the loop runs over whole groups of NS
+    // steps (every register index a constant) with no branch around a load.
     const int nsteps = K / TK;
-    gload(ga0, gb0, 0);
-    if (nsteps > 1)
-        gload(ga1, gb1, TK);
-    sstore(ga0, gb0, As[0], Bs[0]);
+#pragma unroll
+    for (int u = 0; u < NS; u++)
+        gload(u, u * TK);
+    sstore(0, As[0], Bs[0]);
     __syncthreads();
-    if (nsteps > 2)
-        gload(ga0, gb0, 2 * TK);
-    int s0 = 0;
-    for (; s0 + 1 < nsteps; s0 += 2) {
-        mma(As[0], Bs[0]);
-        sstore(ga1, gb1, As[1], Bs[1]);
-        __syncthreads();
-        if (s0 + 3 < nsteps)
-            gload(ga1, gb1, (s0 + 3) * TK);
-        mma(As[1], Bs[1]);
-        if (s0 + 2 < nsteps)
-            sstore(ga0, gb0, As[0], Bs[0]);
-        __syncthreads();
-        if (s0 + 4 < nsteps)
-            gload(ga0, gb0, (s0 + 4) * TK);
+    gload(0, NS * TK);
+    for (int s0 = 0; s0 < nsteps; s0 += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; u++) {
+            mma(As[u % 2], Bs[u % 2]);                          // step s0 + u
+            sstore((u + 1) % NS, As[(u + 1) % 2], Bs[(u + 1) % 2]);  // step s0 + u + 1
+            __syncthreads();
+            gload((u + 1) % NS, (s0 + u + 1 + NS) * TK);        // step s0 + u + 1 + NS
+        }
     }
-    if (s0 < nsteps)  // an odd last step, already in buffer 0
-        mma(As[0], Bs[0]);
 
     // D layout: lane holds column (lane & 15), rows 4*(lane >> 4) + e
 #pragma unroll
     for (int i = 0; i < FI; i++) {
 #pragma unroll
-        for (int j = 0; j < FJ; j++) {
-            const int32_t c = c0 + wn * WN + j * 16 + (lane & 15);
+        for (int jj = 0; jj < FJ; jj++) {
+            const int32_t c = c0 + wn * WN + jj * 16 + (lane & 15);
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int32_t r = r0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
                 if (r < n_q && c < nb_max)
-                    S[(int64_t)r * ld + c] = acc[i][j][e];
+                    S[(int64_t)r * ld + c] = acc[i][jj][e];
             }
         }
     }
@@ -140,11 +157,13 @@ hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h
     const int32_t nb_max = (pos0 + n_q) / kBlockTokens;
     if (nb_max <= 0)
         return hipSuccess;
-    if (row_elems % TK)
+    if (row_elems % (NS * TK))
         return hipErrorInvalidValue;
-    const dim3 grid((uint32_t)((nb_max + TN - 1) / TN), (uint32_t)((n_q + TM - 1) / TM));
-    hipLaunchKernelGGL(score_prefill_kernel, grid, dim3(kThreads), 0, s, q, n_q, pos0, pool,
-                       row_elems, scores, ld);
+    const int32_t ncol = (nb_max + TN - 1) / TN, nrow = (n_q + TM - 1) / TM;
+    // every XCD gets whole columns (all their row tiles); columns past ncol exit
+    const int64_t wgs = (int64_t)((ncol + kXcds - 1) / kXcds) * kXcds * nrow;
+    hipLaunchKernelGGL(score_prefill_kernel, dim3((uint32_t)wgs), dim3(kThreads), 0, s, q, n_q,
+                       pos0, pool, row_elems, scores, ld, ncol, nrow);
     return hipGetLastError();
 }
 
