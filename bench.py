@@ -8,10 +8,12 @@ N-1, N, N+1, N+2 (tails 1, 2, 3 and a completed block), then rewinds.
 
 Reported:
   value        layer decode steps/s (= 12 * tokens / s)
-  roofline     the decode scoring kernel (the pooled-key scan): algorithmic bytes
-               per launch / its average duration, timed live with HIP events on the
-               stream it runs on, against 8 TB/s; plus HBM traffic per launch from
-               rocprofv3 counters when they were taken on the current kernel source
+  roofline     the decode step's scoring kernel (appends + pooled-key scan +
+               candidate lists): algorithmic bytes per launch / its average
+               duration, from the kernel's own start/end events (qsa_trace_scan) on
+               the stream it runs on, against 8 TB/s; plus HBM traffic per launch
+               from rocprofv3 counters when they were taken on the current kernel
+               source; "standalone" gives the same for qsa_index_score's scan
   step_hbm     algorithmic bytes of a whole layer step / measured step time
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
 
@@ -68,6 +70,19 @@ def traffic_for(kernel: str, source: str, workload: str):
     if t.get("source_hash") != src_hash(source):
         return None
     return t.get("bytes_per_launch")
+
+
+def hold_cycles(stream, ms: float) -> int:
+    """Spin cycles of torch.cuda._sleep that hold `stream` for about `ms`."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 1 << 20
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        torch.cuda._sleep(n)
+        b.record(stream)
+    b.synchronize()
+    return int(n * ms / max(a.elapsed_time(b), 1e-3))
 
 
 def decode_bytes(w, nb, cells):
@@ -179,17 +194,20 @@ def bench_decode(args):
             st["q_r"] = st["q"].unsqueeze(0).repeat(rows, 1, 1).contiguous()
             st["out_r"] = torch.empty((rows, w.hq, w.dv), dtype=torch.float32, device=dev)
 
+    def layer_step(st, j):
+        if rows == 1:
+            qb.qsa_decode_step(cfg, st["layer"], n0 + j, st["q_idx"], st["k_idx_new"][j],
+                               st["q"], st["k_new"][j], st["v_new"][j], st["out"], ws,
+                               flags=flags)
+        else:
+            qb.qsa_decode_multi(cfg, st["layer"], n0 + j, st["q_idx_r"],
+                                st["k_idx_new"][j:j + rows], st["q_r"],
+                                st["k_new"][j:j + rows], st["v_new"][j:j + rows],
+                                st["out_r"], ws)
+
     def token(j):
         for st in layers:
-            if rows == 1:
-                qb.qsa_decode_step(cfg, st["layer"], n0 + j, st["q_idx"], st["k_idx_new"][j],
-                                   st["q"], st["k_new"][j], st["v_new"][j], st["out"], ws,
-                                   flags=flags)
-            else:
-                qb.qsa_decode_multi(cfg, st["layer"], n0 + j, st["q_idx_r"],
-                                    st["k_idx_new"][j:j + rows], st["q_r"],
-                                    st["k_new"][j:j + rows], st["v_new"][j:j + rows],
-                                    st["out_r"], ws)
+            layer_step(st, j)
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -229,10 +247,36 @@ def bench_decode(args):
     layer_steps_s = tok_s * n_layers
     log(f"[time] {args.steps} tokens x {n_layers} layers in {ms:.2f} ms")
 
-    # dominant kernel: the pooled-key scan, timed alone on the same stream
+    # dominant kernel: the decode step's scan (appends, block scores, candidate
+    # lists), the kernel's own start and end times taken through qsa_trace_scan on
+    # eager steps in the timed region's order (layers, then positions), on its stream
+    per_cycle = n_layers * n_pos
+    reps = per_cycle * max(1, args.kernel_reps // per_cycle)
+    tev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    with torch.cuda.stream(stream):
+        for e in tev:
+            e.record(stream)  # creates the events
+        # hold the stream until the host has queued every step, so that the steps run
+        # back to back as in the graphs, not one by one behind the host
+        torch.cuda._sleep(hold_cycles(stream, args.trace_hold_ms))
+        for r in range(reps):
+            qb.qsa_trace_scan(tev[2 * r], tev[2 * r + 1])
+            layer_step(layers[r % n_layers], (r // n_layers) % n_pos)
+    stream.synchronize()
+    scan_us = sum(tev[2 * r].elapsed_time(tev[2 * r + 1]) for r in range(reps)) * 1e3 / reps
+    # scan bytes of the step: the rows complete before the call (the position cycle's
+    # mean), the appended block's row read back from LDS, not from HBM
+    row = w.h_idx * w.d_idx * 2
+    scan_bytes = float(np.mean([((w.n_tokens - 1 + j) // 4) * row for j in range(n_pos)]))
+    achieved = scan_bytes / (scan_us * 1e-6) / 1e9
+    rowc = w.h_idx * w.d_idx // 8
+    step_kernel = f"score_decode_kernel<{rowc},{2 if rowc >= 128 else 4},512,{rows},true,true>"
+
+    # the stand-alone scan (qsa_index_score), back-to-back launches between two
+    # events (dispatch gaps included)
     nb = w.n_tokens // 4
     scores = torch.empty(nb + 64, dtype=torch.float32, device=dev)
-    reps = 12 * max(1, args.kernel_reps // 12)
+    sreps = 12 * max(1, args.kernel_reps // 12)
     with torch.cuda.stream(stream):
         for r in range(12):
             st = layers[r % n_layers]
@@ -240,16 +284,14 @@ def bench_decode(args):
         k0 = torch.cuda.Event(enable_timing=True)
         k1 = torch.cuda.Event(enable_timing=True)
         k0.record(stream)
-        for r in range(reps):
+        for r in range(sreps):
             st = layers[r % n_layers]
             qb.qsa_index_score(cfg, st["q_idx"], w.n_tokens - 1, st["layer"].k_pool, scores)
         k1.record(stream)
     k1.synchronize()
-    kern_us = k0.elapsed_time(k1) * 1e3 / reps
-    row = w.h_idx * w.d_idx * 2
-    scan_bytes = nb * row
-    achieved = scan_bytes / (kern_us * 1e-6) / 1e9
-    traffic = traffic_for("score_decode_kernel", "k_score.hip", w.name)
+    alone_us = k0.elapsed_time(k1) * 1e3 / sreps
+    alone_bytes = nb * row
+    alone_gbps = alone_bytes / (alone_us * 1e-6) / 1e9
 
     # whole-step algorithmic bandwidth, averaged over the 4-step position cycle
     per = []
@@ -290,12 +332,21 @@ def bench_decode(args):
             "token_steps_per_s": round(tok_s, 2),
         },
         "roofline": {
-            "bound": "hbm", "kernel": "score_decode_kernel",
+            "bound": "hbm", "kernel": step_kernel,
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": scan_bytes,
-            "avg_launch_us": round(kern_us, 3),
+            "traffic": traffic_for("score_decode_step_kernel", "k_score.hip", w.name),
+            "algorithmic_bytes_per_launch": int(scan_bytes),
+            "avg_launch_us": round(scan_us, 3),
+            "timing": f"kernel start/end events of {reps} eager decode steps (qsa_trace_scan)",
+            "standalone": {
+                "kernel": f"score_decode_kernel<{rowc},{2 if rowc >= 128 else 4},256,1,false,false>",
+                "achieved": round(alone_gbps, 1), "frac": round(alone_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for("score_decode_kernel", "k_score.hip", w.name),
+                "algorithmic_bytes_per_launch": alone_bytes,
+                "avg_launch_us": round(alone_us, 3),
+                "timing": f"{sreps} back-to-back qsa_index_score launches between two events",
+            },
         },
         "step_hbm": {
             "algorithmic_bytes_per_layer_step": int(step_bytes),
@@ -603,6 +654,8 @@ def main():
     ap.add_argument("--per-row", action="store_true",
                     help="prefill: per-row attention instead of the grouped-union form")
     ap.add_argument("--kernel-reps", type=int, default=240)
+    ap.add_argument("--trace-hold-ms", type=float, default=40.0,
+                    help="stream hold before the traced decode steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,

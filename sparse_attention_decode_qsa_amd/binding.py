@@ -34,7 +34,7 @@ EXPORTS = [
     "qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_attn",
     "qsa_prefill_attn", "qsa_decode_step", "qsa_decode_multi", "qsa_prefill_step",
     "qsa_mla_workspace_size", "qsa_mla_sparse_attn", "qsa_mla_list_status",
-    "qsa_decode_step_noalloc",
+    "qsa_decode_step_noalloc", "qsa_trace_scan",
 ]
 QSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -96,6 +96,7 @@ def load():
         "qsa_mla_list_status": (C.c_int, [p, i32, C.POINTER(i32), p]),
         "qsa_decode_step_noalloc": (C.c_int, [cfg, C.POINTER(qsa_layer_bufs), i32, p, p, p, p,
                                               p, p, p, p, u32, p]),
+        "qsa_trace_scan": (C.c_int, [p, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -345,3 +346,16 @@ def qsa_decode_step_noalloc(cfg, layer, n_before: int, q_idx, k_idx_new, q, k_ne
         _ptr(k_new, H16, name="k_new"), _ptr(v_new, H16, name="v_new"),
         _ptr(out, torch.float32, name="out"), _ptr(scores_out, torch.float32, name="scores_out"),
         _ptr(blk_out, torch.int32, name="blk_out"), flags, _stream()))
+
+
+def qsa_trace_scan(start=None, stop=None) -> None:
+    """The calling thread's next decode step records `start` and `stop`
+    (torch.cuda.Event, timing enabled, each recorded once so that it exists) with
+    the start and end times of its scoring kernel; None for both clears."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:
+            raise ValueError("qsa_trace_scan: record the event once before passing it")
+        return C.c_void_p(ev.cuda_event)
+    _check(load().qsa_trace_scan(handle(start), handle(stop)))

@@ -23,6 +23,8 @@
 // query row, the kListLen best of their union (in any order) and writes them, so
 // the top-k reads a few thousand candidates per query row instead of the whole
 // score row.
+#include <hip/hip_ext.h>
+
 #include "qsa_append.h"
 
 namespace qsa {
@@ -275,9 +277,28 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
     }
 }
 
+// A launch of kern with the events of ev (kernel start and end times), else plain.
+template <typename F, typename... Args>
+void launch_ev(F kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, KernelEvents ev,
+               Args... args)
+{
+    if (ev.start || ev.stop)
+        hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kern, grid, block, lds, s, args...);
+}
+
+// Work groups of the decode-step scan, besides the append's.  Two of them are
+// resident per CU (8 waves each; the append's fp64 RoPE angles set the register
+// count), so 767 is one and a half rounds over 256 CUs; measured at 256k tokens it
+// beat a full two rounds (1,023) by 1% per step and one round (511) by 4%.
+constexpr int64_t kStepScanWgs = 767;
+static_assert(kStepScanWgs < kListWgs, "one list per thread of the top-k selection");
+
 template <int ROWC, int NQ>
 hipError_t launch_step(const h16 *q, const h16 *pool, int32_t nb, float *scores, int32_t ld,
-                       const AppendArgs &ap, const CandLists *cl, int32_t *n_lists, hipStream_t s)
+                       const AppendArgs &ap, const CandLists *cl, int32_t *n_lists, hipStream_t s,
+                       KernelEvents ev)
 {
     constexpr int U = ROWC >= 128 ? 2 : 4;
     constexpr int LPR = ROWC < kWave ? ROWC : kWave;
@@ -285,24 +306,23 @@ hipError_t launch_step(const h16 *q, const h16 *pool, int32_t nb, float *scores,
     constexpr int NW = kStepThreads / kWave;
     const int64_t groups = ((int64_t)nb + RPW - 1) / RPW;
     // one scan work group per 8 row groups (so every wave starts with a group), at
-    // most kListWgs - 1 of them: the lists, the append work group's included, fit
-    // one per thread of the top-k selection
+    // most kStepScanWgs of them
     int64_t grid = (groups + NW - 1) / NW;
-    if (grid > kListWgs - 1)
-        grid = kListWgs - 1;
+    if (grid > kStepScanWgs)
+        grid = kStepScanWgs;
     if (grid < 1)
         grid = 1;
     const size_t lds = sizeof(f32x2) * (size_t)(ap.d / 2) + sizeof(h16) * (size_t)ROWC * 8;
     if (cl) {
-        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kStepThreads, NQ, true, true>),
-                           dim3((uint32_t)grid + 1), dim3(kStepThreads), lds, s, q, pool, nb,
-                           scores, ld, ap, *cl);
+        launch_ev(score_decode_kernel<ROWC, U, kStepThreads, NQ, true, true>,
+                  dim3((uint32_t)grid + 1), dim3(kStepThreads), lds, s, ev, q, pool, nb, scores,
+                  ld, ap, *cl);
         *n_lists = (int32_t)grid + 1;
     } else {
         const CandLists nol{};
-        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kStepThreads, NQ, true, false>),
-                           dim3((uint32_t)grid + 1), dim3(kStepThreads), lds, s, q, pool, nb,
-                           scores, ld, ap, nol);
+        launch_ev(score_decode_kernel<ROWC, U, kStepThreads, NQ, true, false>,
+                  dim3((uint32_t)grid + 1), dim3(kStepThreads), lds, s, ev, q, pool, nb, scores,
+                  ld, ap, nol);
     }
     return hipGetLastError();
 }
@@ -310,7 +330,7 @@ hipError_t launch_step(const h16 *q, const h16 *pool, int32_t nb, float *scores,
 template <int ROWC>
 hipError_t launch_rowc(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb, float *scores,
                        int32_t ld, const AppendArgs *ap, const CandLists *cl, int32_t *n_lists,
-                       hipStream_t s)
+                       hipStream_t s, KernelEvents ev)
 {
     if (!ap) {
         constexpr int U = ROWC >= 128 ? 2 : 4;
@@ -331,10 +351,10 @@ hipError_t launch_rowc(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb, f
         return hipGetLastError();
     }
     switch (n_q) {
-    case 1: return launch_step<ROWC, 1>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
-    case 2: return launch_step<ROWC, 2>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
-    case 3: return launch_step<ROWC, 3>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
-    case 4: return launch_step<ROWC, 4>(q, pool, nb, scores, ld, *ap, cl, n_lists, s);
+    case 1: return launch_step<ROWC, 1>(q, pool, nb, scores, ld, *ap, cl, n_lists, s, ev);
+    case 2: return launch_step<ROWC, 2>(q, pool, nb, scores, ld, *ap, cl, n_lists, s, ev);
+    case 3: return launch_step<ROWC, 3>(q, pool, nb, scores, ld, *ap, cl, n_lists, s, ev);
+    case 4: return launch_step<ROWC, 4>(q, pool, nb, scores, ld, *ap, cl, n_lists, s, ev);
     default: return hipErrorInvalidValue;
     }
 }
@@ -343,7 +363,8 @@ hipError_t launch_rowc(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb, f
 
 hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb,
                                int32_t row_elems, float *scores, int32_t ld, const AppendArgs *ap,
-                               const CandLists *cl, int32_t *n_lists, hipStream_t s)
+                               const CandLists *cl, int32_t *n_lists, hipStream_t s,
+                               KernelEvents ev)
 {
     if (nb <= 0 && !ap)
         return hipSuccess;
@@ -354,12 +375,12 @@ hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32
                 (int64_t)ap->H * ap->d != row_elems)))
         return hipErrorInvalidValue;
     switch (row_elems / 8) {
-    case 16: return launch_rowc<16>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
-    case 32: return launch_rowc<32>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
-    case 64: return launch_rowc<64>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
-    case 128: return launch_rowc<128>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
-    case 256: return launch_rowc<256>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
-    case 512: return launch_rowc<512>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s);
+    case 16: return launch_rowc<16>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s, ev);
+    case 32: return launch_rowc<32>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s, ev);
+    case 64: return launch_rowc<64>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s, ev);
+    case 128: return launch_rowc<128>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s, ev);
+    case 256: return launch_rowc<256>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s, ev);
+    case 512: return launch_rowc<512>(q, n_q, pool, nb, scores, ld, ap, cl, n_lists, s, ev);
     default: return hipErrorInvalidValue;
     }
 }

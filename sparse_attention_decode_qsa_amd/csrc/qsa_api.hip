@@ -15,6 +15,8 @@ using namespace qsa;
 namespace {
 
 thread_local char g_err[512] = "";
+// Events for the calling thread's next decode-step scoring launch (qsa_trace_scan).
+thread_local KernelEvents g_scan_events;
 
 int fail(int code, const char *fmt, ...)
 {
@@ -210,6 +212,9 @@ int decode_impl(const char *fn, const qsa_config *cfg, const qsa_layer_bufs *Lb,
                 int32_t ld_scores, int32_t *blk_out, uint32_t flags, void *ws, size_t ws_bytes,
                 qsa_stream_t stream)
 {
+    // the events set by qsa_trace_scan are for this call only, whatever it returns
+    const KernelEvents ev = g_scan_events;
+    g_scan_events = KernelEvents{};
     int r = check_cfg(cfg);
     if (r)
         return r;
@@ -279,7 +284,7 @@ int decode_impl(const char *fn, const qsa_config *cfg, const qsa_layer_bufs *Lb,
     const CandLists cl = cand_lists(ws, L);
     int32_t n_lists = 0;
     HIP_CHECK(launch_score_decode(H(q_idx), n_q, H(Lb->k_pool), ap.b_lo, (int32_t)row, scores, ld,
-                                  &ap, &cl, &n_lists, s));
+                                  &ap, &cl, &n_lists, s, ev));
 
     if (flags == QSA_STEP_FUSED_GATHER) {
         // 3-5. top-k from the candidate lists and attention over the chosen
@@ -914,6 +919,15 @@ int qsa_mla_list_status(const int32_t *n_list, int32_t list_cap, int32_t *n_list
         return fail(QSA_ERR_CAPACITY,
                     "qsa_mla_sparse_attn: %d positions visible, list_cap is %d (out is NaN)", n,
                     list_cap);
+    return QSA_OK;
+}
+
+int qsa_trace_scan(void *start_event, void *stop_event)
+{
+    if (!start_event != !stop_event)
+        return fail(QSA_ERR_INVALID, "qsa_trace_scan: give both events or neither");
+    g_scan_events.start = (hipEvent_t)start_event;
+    g_scan_events.stop = (hipEvent_t)stop_event;
     return QSA_OK;
 }
 

@@ -49,15 +49,21 @@ struct CandLists {
 };
 
 // ---- scores (k_score.hip) ---------------------------------------------------
+// Events that a launch records with its kernel's own start and end times
+// (hipExtLaunchKernelGGL); both NULL: a plain launch.
+struct KernelEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
 // Stand-alone scan (qsa_index_score, ap NULL, n_q = 1): scores[0, nb).
 // Decode-step scan (ap non-NULL): the append work runs in the same launch (at
 // most one completed block, block nb; its scores are written too); n_q queries
 // (rows of q) score every row read once, query i into scores[i * ld ..]; with
 // cl (n_q = 1 only) every work group also writes its candidate list and
-// *n_lists gets the list count.
+// *n_lists gets the list count.  ev: the decode-step launch records them.
 hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb,
                                int32_t row_elems, float *scores, int32_t ld, const AppendArgs *ap,
-                               const CandLists *cl, int32_t *n_lists, hipStream_t s);
+                               const CandLists *cl, int32_t *n_lists, hipStream_t s,
+                               KernelEvents ev = {});
 hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h16 *pool,
                                 int32_t row_elems, float *scores, int32_t ld, hipStream_t s);
 

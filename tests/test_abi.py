@@ -182,3 +182,16 @@ def test_mla_preconditions(lib):
     # the capacity check after a list call rejects bad arguments on the host
     assert lib.qsa_mla_list_status(None, 2048, None, None) == qb.QSA_ERR_INVALID
     assert lib.qsa_mla_list_status(FAKE, 0, None, None) == qb.QSA_ERR_INVALID
+
+
+def test_trace_scan_arguments(lib):
+    # both events or neither; a decode step that fails on the host clears the
+    # setting, so a later step does not record stale events
+    assert lib.qsa_trace_scan(FAKE, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_trace_scan(None, FAKE) == qb.QSA_ERR_INVALID
+    assert lib.qsa_trace_scan(None, None) == qb.QSA_OK
+    assert lib.qsa_trace_scan(FAKE, FAKE) == qb.QSA_OK
+    c = cfg(cap_tokens=4096).c()
+    assert lib.qsa_decode_step(C.byref(c), None, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               None, 0, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
+    assert lib.qsa_trace_scan(None, None) == qb.QSA_OK

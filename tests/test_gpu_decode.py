@@ -132,6 +132,44 @@ def test_speculative_rollback_needs_no_rebuild(gpu):
                           host(clean.k_pool[:nb]).view(np.uint16))
 
 
+def test_trace_scan_events_leave_the_step_unchanged(gpu):
+    # events handed to the scoring launch of a step: the step's results are bit for
+    # bit those of an untraced step at the same position, the events carry a
+    # positive kernel time within the whole step's, and the next step is untraced
+    w = small(4 * 20000 + 3)
+    L, cfg, g, _ = setup_decode(w, with_oracle=False)
+    n0 = L["n_prefix"]
+    ws = qb.workspace(cfg, 1, w.cap_tokens)
+    nb = (n0 + 1) // 4
+    res = []
+    for traced in (True, False, True):
+        out = torch.empty((w.hq, w.dv), device="cuda")
+        scores = torch.empty(nb, device="cuda")
+        blk = torch.full((512,), -1, dtype=torch.int32, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in ev:
+            e.record()  # creates the events
+        if traced:
+            qb.qsa_trace_scan(ev[0], ev[1])
+        ev[2].record()
+        qb.qsa_decode_step(cfg, g, n0, dev(L["q_idx"]), dev(L["k_idx_new"][0]), dev(L["q"]),
+                           dev(L["k_new"][0]), dev(L["v_new"][0]), out, ws, scores_out=scores,
+                           blk_out=blk)
+        ev[3].record()
+        torch.cuda.synchronize()
+        step_ms = ev[2].elapsed_time(ev[3])
+        if traced:
+            scan_ms = ev[0].elapsed_time(ev[1])
+            assert 0.0 < scan_ms < step_ms, (scan_ms, step_ms)
+        res.append((host(out), host(scores), host(blk)))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for a, b in zip(res[0], res[2]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    b = host(blk)
+    assert np.array_equal(b, O.topk_sort(res[0][1], 512))
+
+
 # ------------------------------------------------------------------ a2 scores
 @pytest.mark.parametrize("H,d,nb", [(16, 128, 3001), (4, 64, 1024), (16, 128, 1), (2, 64, 333),
                                     (8, 128, 2047), (32, 128, 100)])
@@ -419,10 +457,11 @@ def clustered_values(pattern, nb, r):
     exactly 2048 * v_b, on the GPU and in the oracle."""
     v = (np.round(r.standard_normal(nb) * 6.4) / 64).astype(np.float16)  # no subnormals
     if pattern == "one_scan_group":
-        # the blocks b with b mod 4092 in [20, 24) on top: the decode scan's 1023 work
-        # groups read runs of 4 neighbouring rows, so these all belong to one work
-        # group, whose 8-entry candidate list cannot hold them (full-row fallback)
-        sel = (np.arange(nb) % 4092 >= 20) & (np.arange(nb) % 4092 < 24)
+        # the blocks b with b mod 3068 in [20, 24) on top: the decode scan's 767 scan
+        # work groups read runs of 4 neighbouring rows (row b in work group
+        # (b mod 3068) / 4), so these all belong to one work group, whose 8-entry
+        # candidate list cannot hold them (full-row fallback)
+        sel = (np.arange(nb) % 3068 >= 20) & (np.arange(nb) % 3068 < 24)
         v[sel] = (4.0 + np.arange(sel.sum()) / 64).astype(np.float16)
     elif pattern == "recent_window":
         v[-700:] = np.linspace(1.0, 2.0, 700).astype(np.float16)
