@@ -73,6 +73,8 @@ extern "C" {
 #define QSA_PREFILL_GROUPED_UNION 1u  /* groups of 128 / (hq/hkv) consecutive rows read the
                                          union of their chosen blocks once (see
                                          qsa_prefill_attn) */
+#define QSA_PREFILL_UNION_ALL 2u      /* with QSA_PREFILL_GROUPED_UNION: every group takes
+                                         the union form, however large its union */
 
 /* A hipStream_t; NULL is the null stream. */
 typedef void *qsa_stream_t;
@@ -215,15 +217,19 @@ QSA_API int qsa_sparse_attn(const qsa_config *cfg, const uint16_t *q, const uint
  * 「Vulkan版のプロファイリングでTGが遅くなった原因を調べる」; its steps are not given,
  * and the reading here keeps the result: groups of 128 / (hq/hkv) consecutive rows
  * stream the union of their chosen blocks and their tails once, on the matrix
- * cores, with a per-row mask so that every row attends to exactly its own cells;
- * the output equals the per-row form up to fp32 summation order and binary16
- * rounding of the softmax weights; on an MI355X, for 1,024 rows at depth 126,253,
- * it takes 0.15 ms when neighbouring rows share most of their blocks and 0.78 ms
- * when they share almost none, against 0.92-0.94 ms per row).  The union form
- * needs hq/hkv in {4, 8, 16}, d = dv = 128 and (128 / (hq/hkv)) * topk_blocks <=
- * 16384 (else QSA_ERR_UNSUPPORTED) and a workspace of
- * qsa_workspace_size(cfg, n_q, pos0 + n_q).  Both forms drop a chosen id outside
- * the row's [0, nb_r).
+ * cores, with a per-row mask so that every row attends to exactly its own cells).
+ * A group whose union holds more than 3/8 of its rows x k blocks (rows that share
+ * few blocks) is attended per row instead, where that is cheaper; adding
+ * QSA_PREFILL_UNION_ALL makes every group take the union form.  All forms give the
+ * per-row result up to fp32 summation order and binary16 rounding of the softmax
+ * weights.  On an MI355X, for 1,024 rows at depth 126,253: 0.15 ms by the union
+ * when neighbouring rows share most of their blocks, 0.40 ms per row when they
+ * share almost none (the union alone: 0.78 ms).  The union form needs hq/hkv in
+ * {4, 8, 16}, d = dv = 128 and (128 / (hq/hkv)) * topk_blocks <= 16384 (else
+ * QSA_ERR_UNSUPPORTED) and a workspace of qsa_workspace_size(cfg, n_q, pos0 + n_q).
+ * Every form drops a chosen id outside the row's [0, nb_r).
+ * Errors: INVALID (unknown flags, QSA_PREFILL_UNION_ALL without
+ * QSA_PREFILL_GROUPED_UNION, bad pointers), UNSUPPORTED, CAPACITY (workspace).
  */
 QSA_API int qsa_prefill_attn(const qsa_config *cfg, const uint16_t *q, int32_t n_q, int32_t pos0,
                      const int32_t *blk, int32_t ldb, const uint16_t *k_cache,
@@ -299,7 +305,7 @@ QSA_API int qsa_decode_multi(const qsa_config *cfg, const qsa_layer_bufs *L, int
  * steps 2-5 causally (row r sees N_r = n_before + r + 1 tokens).
  * q_idx [n_new][h_idx][d_idx], q [n_new][hq][d], out [n_new][hq][dv].
  * Optional outputs: scores_out [n_new][ld_scores], blk_out [n_new][k].
- * flags: QSA_PREFILL_PER_ROW or QSA_PREFILL_GROUPED_UNION, as for qsa_prefill_attn.
+ * flags: as for qsa_prefill_attn.
  */
 QSA_API int qsa_prefill_step(const qsa_config *cfg, const qsa_layer_bufs *L, int32_t n_before,
                      int32_t n_new, const uint16_t *q_idx, const uint16_t *k_idx_new,

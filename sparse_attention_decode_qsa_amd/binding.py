@@ -27,6 +27,7 @@ QSA_STEP_FUSED_GATHER = 0
 QSA_STEP_COMPACT_GATHER = 1
 QSA_PREFILL_PER_ROW = 0
 QSA_PREFILL_GROUPED_UNION = 1
+QSA_PREFILL_UNION_ALL = 2
 
 EXPORTS = [
     "qsa_status_string", "qsa_last_error", "qsa_config_check", "qsa_workspace_size",

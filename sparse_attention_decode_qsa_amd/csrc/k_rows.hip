@@ -1,0 +1,278 @@
+// Per-row attention of a prefill chunk on the matrix cores (Qiita part 10,
+// "selected QSA K/V gather（COMMON-005）": a query row attends over the cells of
+// its own chosen blocks plus its tail, exactly as a decode step at that row's
+// length would; "QSAとQSA indexerについて": every row of a prefill chunk is such
+// a decode at its own length).
+//
+// rows_attn_kernel<G>: one work group per (KV head, row), 4 waves; wave w takes
+// tiles w, w + 4, ... of 32 cells.  Each tile goes from the caches straight into
+// the matrix operands (v_mfma_f32_16x16x32_f16), nothing staged in LDS:
+//   S^T = K Q^T     A = 16 cells x 32 dims of K (64-byte pieces of each K row),
+//                   B = the G query heads of the group, zero-padded to 16;
+//   O^T += V^T P^T  A = 16 value dims x 32 cells: a lane reads the 16-byte piece
+//                   8m .. 8m+7 of 8 V rows (each read instruction covers whole
+//                   256-byte rows) and transposes the 8 x 8 halves in registers,
+//                   so MFMA r of the tile holds value dims 8m + r;
+//                   B = P^T as the score product leaves it in the lane (cells
+//                   16t + 4j + e of tile half t): the k slots of the PV product
+//                   are those cells, and the V rows a lane reads are the same
+//                   cells, two whole 4-token blocks.
+// A lane therefore holds the scores, the softmax state and 32 output dims of one
+// head (its column of S^T and O^T), and no value crosses lanes except the maximum
+// over the 4 lane rows of the head.  Online softmax in the log2 domain; P is
+// rounded to binary16 for the PV product.  At the end the four waves' (m, l, O)
+// are merged through LDS.
+//
+// With a union-size array (grouped-union prefill) the kernel leaves out the rows
+// whose group the union kernel takes (union size at most u_limit blocks).
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kRThreads = 256;
+constexpr int kRWaves = kRThreads / kWave;
+constexpr int kRTile = 32;   // cells per tile
+constexpr int kRDim = 128;   // D = DV
+constexpr int kROPitch = kRDim + 4;  // LDS pitch of a head's merged outputs (floats)
+constexpr float kLog2e = 1.4426950408889634f;
+// chosen blocks, the tail's block, -1 up to a whole tile (8 blocks)
+constexpr int kRMaxBlocks = kMaxTopk + 1 + 8;
+
+// Sum over lanes l, l ^ 16, l ^ 32, l ^ 48, in the same order in all four (the
+// row swaps leave a lane's own value and its partner's; fp addition of two terms
+// commutes).
+__device__ __forceinline__ float sum_across_rows(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 4 waves per SIMD (at most 128 registers): with two loads per lane in flight that
+// is the ~32 KiB per CU the gather runs best at
+template <int G>
+__global__ __launch_bounds__(kRThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
+rows_attn_kernel(RowsArgs a)
+{
+    static_assert(G == 4 || G == 8 || G == 16, "query heads per KV head");
+    __shared__ int32_t bl[kRMaxBlocks];
+    __shared__ __attribute__((aligned(16))) float om[kRWaves][G][kROPitch];
+    __shared__ float mm[kRWaves][G], ll[kRWaves][G];
+
+    const int g = blockIdx.x;
+    const int32_t row = blockIdx.y;
+    if (a.n_u && a.n_u[row / a.group_rows] <= a.u_limit)
+        return;  // this row's group is the union kernel's (uniform over the group)
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    const int n = lane & 15, j4 = lane >> 4;
+
+    const int32_t N = a.pos0 + row + 1;  // tokens this row sees
+    const int32_t nbr = N / kBlockTokens, nsel = min(a.k, nbr);
+    const int32_t tail = N - kBlockTokens * nbr;
+    const int32_t count = kBlockTokens * nsel + tail;
+    const int32_t ntile = (count + kRTile - 1) / kRTile;
+    // block list: the chosen ids (an id outside [0, nbr) can only come from a broken
+    // selection: its cells are dropped), then the tail's block
+    const int32_t *br = a.blk + (int64_t)row * a.ldb;
+    for (int32_t i = t; i < ntile * 8; i += kRThreads) {
+        int32_t id = -1;
+        if (i < nsel) {
+            const int32_t b = br[i];
+            id = ((uint32_t)b < (uint32_t)nbr) ? b : -1;
+        } else if (i == nsel && tail > 0) {
+            id = nbr;
+        }
+        bl[i] = id;
+    }
+
+    const int64_t kt = (int64_t)a.hkv * kRDim;  // elements per token row, K and V
+    const h16 *kg = a.k_cache + (int64_t)g * kRDim;
+    const h16 *vg = a.v_cache + (int64_t)g * kRDim;
+    // B of the score product: head n of the group, dims 32 kk + 8 j4 .. + 8
+    h16x8 qf[4];
+    const h16 *qr = a.q + ((int64_t)row * a.hq + (int64_t)g * G + (n < G ? n : 0)) * kRDim;
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++)
+        qf[kk] = (n < G) ? *(const h16x8 *)(qr + 32 * kk + 8 * j4) : h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+
+    f32x4 oacc[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++)
+        oacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = a.scale * kLog2e;
+    __syncthreads();
+
+    // Few loads in flight: a gather from the caches keeps ~0.5 us latency only while
+    // a CU has about 32 KiB of loads outstanding (4 waves per SIMD x 2 pieces of
+    // 1 KiB per wave); with more in flight the latency grows faster than the bytes
+    // and the rate falls to about half.  So each step below issues two 16-byte
+    // pieces per lane and uses them before the next step's loads go out (the
+    // compiler barriers keep it from hoisting loads across steps).
+    auto fence = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int32_t tile = wave; tile < ntile; tile += kRWaves) {
+        const int32_t c0 = tile * kRTile;
+        // S^T = K Q^T over 4 k-steps; step kk reads dims 32 kk + 8 j4 of cells
+        // c0 + n and c0 + 16 + n (the A rows of the two cell halves)
+        int32_t ktok[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++) {
+            const int32_t c = c0 + 16 * tt + n;
+            const int32_t b = bl[c >> 2];
+            ktok[tt] = (b >= 0 && c < count) ? kBlockTokens * b + (c & 3) : 0;
+        }
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            h16x8 kf[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; tt++)
+                kf[tt] = *(const h16x8 *)(kg + (int64_t)ktok[tt] * kt + 32 * kk + 8 * j4);
+#pragma unroll
+            for (int tt = 0; tt < 2; tt++)
+                sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[tt], qf[kk], sacc[tt], 0, 0, 0);
+            fence();
+        }
+
+        // the lane's cells in the score layout: c0 + 16 tt + 4 j4 + e, i.e. the
+        // 4-token blocks 8 tile + 4 tt + j4 (also the V rows it reads below)
+        int32_t vb[2];
+        uint32_t vm = 0u;
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++) {
+            vb[tt] = bl[8 * tile + 4 * tt + j4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int32_t c = c0 + 16 * tt + 4 * j4 + e;
+                vm |= (vb[tt] >= 0 && c < count) ? 1u << (4 * tt + e) : 0u;
+            }
+        }
+
+        // V pieces of the first half's first two cells go out before the softmax;
+        // a cell that is not there reads token 0 (a real, finite row: its p is 0)
+        auto vaddr = [&](int tt, int e) {
+            const int32_t tok = ((vm >> (4 * tt + e)) & 1u) ? kBlockTokens * vb[tt] + e : 0;
+            return (const h16x8 *)(vg + (int64_t)tok * kt + 8 * n);
+        };
+        h16x8 vin[4];
+        vin[0] = *vaddr(0, 0);
+        vin[1] = *vaddr(0, 1);
+
+        // online softmax of head n over the tile's cells (order 4 tt + e)
+        float s[8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            s[i] = (((vm >> i) & 1u) && n < G) ? sacc[i / 4][i % 4] : -INFINITY;
+            tmax = fmaxf(tmax, s[i]);
+        }
+        tmax = max_across_rows(tmax);
+        const float mnew = fmaxf(m_run, tmax * sl2);
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
+        const bool moved = mnew != m_run;
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -mref));
+            psum += s[i];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = mnew;
+        if (__any(moved)) {
+#pragma unroll
+            for (int r = 0; r < 8; r++)
+                oacc[r] *= alpha;
+        }
+
+        // O^T += V^T P^T, one 16-cell half at a time (v_mfma_f32_16x16x16_f16: the
+        // lane's k slots are its 4 cells of the half, one 4-token block); the V
+        // pieces are dims 8 n .. + 8 of those 4 rows, two per step, transposed so
+        // that MFMA r takes dims 8 n + r
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++) {
+            if (tt == 1) {
+                vin[0] = *vaddr(1, 0);
+                vin[1] = *vaddr(1, 1);
+            }
+            // the pair in flight is used before the next pair goes out
+            asm volatile("" : "+v"(vin[0]), "+v"(vin[1]));
+            fence();
+            vin[2] = *vaddr(tt, 2);
+            vin[3] = *vaddr(tt, 3);
+            const h16x4 pf = h16x4{(h16)s[4 * tt], (h16)s[4 * tt + 1], (h16)s[4 * tt + 2],
+                                   (h16)s[4 * tt + 3]};
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                const h16x4 vt = h16x4{vin[0][r], vin[1][r], vin[2][r], vin[3][r]};
+                oacc[r] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt, pf, oacc[r], 0, 0, 0);
+            }
+            fence();
+        }
+    }
+
+    // merge of the four waves: head n's dims 32 j4 + 8 e + r from this lane
+    const float lsum = sum_across_rows(l_run);
+    if (n < G) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            float *op = &om[wave][n][32 * j4 + 8 * e];
+            *(f32x4 *)op = f32x4{oacc[0][e], oacc[1][e], oacc[2][e], oacc[3][e]};
+            *(f32x4 *)(op + 4) = f32x4{oacc[4][e], oacc[5][e], oacc[6][e], oacc[7][e]};
+        }
+        if (j4 == 0) {
+            mm[wave][n] = m_run;
+            ll[wave][n] = lsum;
+        }
+    }
+    __syncthreads();
+    float *orow = a.out + ((int64_t)row * a.hq + (int64_t)g * G) * kRDim;
+    for (int i = t; i < G * kRDim; i += kRThreads) {
+        const int h = i / kRDim, d = i - h * kRDim;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kRWaves; w++)
+            M = fmaxf(M, mm[w][h]);
+        const float Mref = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kRWaves; w++) {
+            const float sc = __builtin_amdgcn_exp2f(mm[w][h] - Mref);
+            L += sc * ll[w][h];
+            o += sc * om[w][h][d];
+        }
+        orow[i] = o / L;
+    }
+}
+
+}  // namespace
+
+bool rows_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k)
+{
+    if (hkv <= 0 || hq % hkv || d != kRDim || dv != kRDim || k > kMaxTopk)
+        return false;
+    const int32_t G = hq / hkv;
+    return G == 4 || G == 8 || G == 16;
+}
+
+hipError_t launch_rows_attn(const RowsArgs &a, hipStream_t s)
+{
+    if (a.n_q <= 0)
+        return hipSuccess;
+    if (!rows_supported(a.hq, a.hkv, kRDim, kRDim, a.k) || (a.n_u && a.group_rows <= 0))
+        return hipErrorInvalidValue;
+    const dim3 grid((uint32_t)a.hkv, (uint32_t)a.n_q);
+    switch (a.hq / a.hkv) {
+    case 4: hipLaunchKernelGGL(rows_attn_kernel<4>, grid, dim3(kRThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(rows_attn_kernel<8>, grid, dim3(kRThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(rows_attn_kernel<16>, grid, dim3(kRThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qsa

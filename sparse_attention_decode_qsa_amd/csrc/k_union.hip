@@ -166,6 +166,7 @@ struct UnionAttnArgs {
     const uint32_t *umask;  // [groups][cap_u]
     const int32_t *n_u;     // [groups]
     int32_t cap_u;
+    int32_t u_limit;        // groups with more union blocks are the per-row kernel's
     int32_t n_q, pos0, hq, hkv;
     float scale;
     int32_t splits;
@@ -191,6 +192,8 @@ __global__ __launch_bounds__(kSetThreads * SETS, 3 - SETS) void union_attn_kerne
 
     // virtual block list: the union, then the blocks of the tail span [t0, t1)
     const int32_t nu = a.n_u[g];
+    if (nu > a.u_limit)
+        return;  // the per-row kernel takes this group (uniform over the work group)
     const int32_t t0 = ((a.pos0 + r0 + 1) / kBlockTokens) * kBlockTokens;
     const int32_t t1 = a.pos0 + r0 + nr;
     const int32_t ntb = t1 > t0 ? (t1 - 1) / kBlockTokens - t0 / kBlockTokens + 1 : 0;
@@ -493,9 +496,14 @@ __global__ __launch_bounds__(kSetThreads * SETS, 3 - SETS) void union_attn_kerne
 constexpr int kUCombThreads = 256;
 __global__ __launch_bounds__(kUCombThreads) void union_combine_kernel(const float *__restrict__ part,
                                                                      int32_t hq, int32_t S,
+                                                                     const int32_t *__restrict__ n_u,
+                                                                     int32_t group_rows,
+                                                                     int32_t u_limit,
                                                                      float *__restrict__ out)
 {
     const int64_t row = blockIdx.x;
+    if (n_u[row / group_rows] > u_limit)
+        return;  // a per-row group: its output is the per-row kernel's
     for (int idx = threadIdx.x; idx < hq * (kDim / 4); idx += kUCombThreads) {
         const int h = idx / (kDim / 4), c = idx % (kDim / 4);
         const float *pb = part + (row * hq + h) * S * kPartStride;
@@ -555,6 +563,7 @@ hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s)
     a.umask = u.umask;
     a.n_u = u.n_u;
     a.cap_u = cap_u;
+    a.u_limit = u.u_limit;
     a.n_q = u.n_q;
     a.pos0 = u.pos0;
     a.hq = u.hq;
@@ -572,11 +581,44 @@ hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();
-    if (e != hipSuccess || u.splits == 1)
+    if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(union_combine_kernel, dim3((uint32_t)u.n_q), dim3(kUCombThreads), 0, s,
-                       u.part, u.hq, u.splits, u.out);
-    return hipGetLastError();
+    if (u.splits > 1) {
+        hipLaunchKernelGGL(union_combine_kernel, dim3((uint32_t)u.n_q), dim3(kUCombThreads), 0, s,
+                           u.part, u.hq, u.splits, u.n_u, G, u.u_limit, u.out);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    if (u.u_limit >= cap_u)
+        return hipSuccess;  // no group can exceed the limit
+    // the groups whose union is too large for the union form to pay: per row
+    RowsArgs ra;
+    ra.q = u.q;
+    ra.blk = u.blk;
+    ra.ldb = u.ldb;
+    ra.k_cache = u.k_cache;
+    ra.v_cache = u.v_cache;
+    ra.n_q = u.n_q;
+    ra.pos0 = u.pos0;
+    ra.k = u.k;
+    ra.hq = u.hq;
+    ra.hkv = u.hkv;
+    ra.scale = u.scale;
+    ra.out = u.out;
+    ra.n_u = u.n_u;
+    ra.group_rows = G;
+    ra.u_limit = u.u_limit;
+    return launch_rows_attn(ra, s);
+}
+
+int32_t union_limit(int32_t hq, int32_t hkv, int32_t k)
+{
+    // A union block costs the union kernel about 8/3 of what one row's block costs
+    // the per-row kernel (measured at depth 126,253: 1.7-2.2 ns against 0.76 ns per
+    // block, whole chip), so the union pays while it holds at most 3/8 of the
+    // group's rows x k blocks (6 k for groups of 16 rows).
+    return (int32_t)(((int64_t)union_group_rows(hq, hkv) * k * 3) / 8);
 }
 
 }  // namespace qsa

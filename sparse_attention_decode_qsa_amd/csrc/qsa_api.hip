@@ -642,12 +642,34 @@ static hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32
         u.hkv = cfg->hkv;
         u.scale = cfg->attn_scale;
         u.splits = union_splits(n_q, cfg->hq, cfg->hkv);
+        u.u_limit = (flags & QSA_PREFILL_UNION_ALL) ? INT32_MAX
+                                                    : union_limit(cfg->hq, cfg->hkv,
+                                                                  cfg->topk_blocks);
         u.uid = at<int32_t>(ws, L.uid);
         u.umask = at<uint32_t>(ws, L.umask);
         u.n_u = at<int32_t>(ws, L.nu);
         u.part = at<float>(ws, L.upart);
         u.out = out;
         return launch_union_attn(u, s);
+    }
+    if (rows_supported(cfg->hq, cfg->hkv, cfg->d, cfg->dv, cfg->topk_blocks)) {
+        RowsArgs ra;
+        ra.q = q;
+        ra.blk = blk;
+        ra.ldb = ldb;
+        ra.k_cache = kc;
+        ra.v_cache = vc;
+        ra.n_q = n_q;
+        ra.pos0 = pos0;
+        ra.k = cfg->topk_blocks;
+        ra.hq = cfg->hq;
+        ra.hkv = cfg->hkv;
+        ra.scale = cfg->attn_scale;
+        ra.out = out;
+        ra.n_u = nullptr;
+        ra.group_rows = 1;
+        ra.u_limit = 0;
+        return launch_rows_attn(ra, s);
     }
     AttnArgs a = attn_base(cfg);
     a.q = q;
@@ -666,8 +688,11 @@ static hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32
 
 static int check_prefill_flags(const qsa_config *cfg, uint32_t flags, const char *fn)
 {
-    if (flags & ~QSA_PREFILL_GROUPED_UNION)
+    if (flags & ~(QSA_PREFILL_GROUPED_UNION | QSA_PREFILL_UNION_ALL))
         return fail(QSA_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+    if ((flags & QSA_PREFILL_UNION_ALL) && !(flags & QSA_PREFILL_GROUPED_UNION))
+        return fail(QSA_ERR_INVALID, "%s: QSA_PREFILL_UNION_ALL needs QSA_PREFILL_GROUPED_UNION",
+                    fn);
     if ((flags & QSA_PREFILL_GROUPED_UNION) &&
         !union_supported(cfg->hq, cfg->hkv, cfg->d, cfg->dv, cfg->topk_blocks))
         return fail(QSA_ERR_UNSUPPORTED,

@@ -169,6 +169,8 @@ struct UnionArgs {
     int32_t n_q, pos0, k, hq, hkv;
     float scale;
     int32_t splits;         // union_splits()
+    int32_t u_limit;        // groups of more union blocks go to the per-row kernel
+                            // (union_limit(); at least rows * k: every group here)
     int32_t *uid;           // [groups][rows * k]
     uint32_t *umask;        // [groups][rows * k]
     int32_t *n_u;           // [groups]
@@ -178,7 +180,25 @@ struct UnionArgs {
 bool union_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k);
 int32_t union_group_rows(int32_t hq, int32_t hkv);
 int32_t union_splits(int32_t n_q, int32_t hq, int32_t hkv);
+int32_t union_limit(int32_t hq, int32_t hkv, int32_t k);
 hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s);
+
+// ---- per-row prefill attention on the matrix cores (k_rows.hip) ---------------
+// One work group per (KV head, row); d = dv = 128, hq / hkv in {4, 8, 16}.
+struct RowsArgs {
+    const h16 *q;           // [n_q][hq][128]
+    const int32_t *blk;     // [n_q][ldb] chosen ids per row
+    int32_t ldb;
+    const h16 *k_cache, *v_cache;  // token-major [tok][hkv][128]
+    int32_t n_q, pos0, k, hq, hkv;
+    float scale;
+    float *out;             // [n_q][hq][128]
+    const int32_t *n_u;     // union blocks per row group (NULL: every row here)
+    int32_t group_rows;     // rows per group of n_u
+    int32_t u_limit;        // rows of a group with n_u <= u_limit are left out
+};
+bool rows_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k);
+hipError_t launch_rows_attn(const RowsArgs &a, hipStream_t s);
 
 // ---- MLA list (k_mla.hip) ---------------------------------------------------
 constexpr int kListSeg = 1024;     // positions per list-building work group

@@ -167,7 +167,13 @@ def test_entry_points_reject_bad_arguments_on_the_host(lib):
                                     FAKE, None, 0, None, U, FAKE, 1 << 30, None) == \
             qb.QSA_ERR_UNSUPPORTED, kw
     assert lib.qsa_prefill_step(cp, C.byref(b), 100, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                                0, None, 2, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
+                                0, None, 4, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
+    # the union-for-every-group flag needs the grouped-union flag
+    assert lib.qsa_prefill_step(cp, C.byref(b), 100, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                0, None, qb.QSA_PREFILL_UNION_ALL, FAKE, 1 << 30, None) == \
+        qb.QSA_ERR_INVALID
+    assert lib.qsa_prefill_attn(cp, FAKE, 8, 100, FAKE, 512, FAKE, FAKE, FAKE,
+                                qb.QSA_PREFILL_UNION_ALL, FAKE, 1 << 30, None) == qb.QSA_ERR_INVALID
 
 
 def test_mla_preconditions(lib):

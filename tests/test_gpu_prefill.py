@@ -223,6 +223,7 @@ def test_prefill_step_full_size_sampled(gpu):
 
 # ---------------------------------------------------------------- grouped-union form
 UNION = qb.QSA_PREFILL_GROUPED_UNION
+UNION_ALL = qb.QSA_PREFILL_GROUPED_UNION | qb.QSA_PREFILL_UNION_ALL  # no per-row groups
 
 
 @pytest.mark.parametrize("q_corr", [0.0, 0.99])
@@ -233,10 +234,13 @@ def test_prefill_step_union_small(gpu, q_corr):
     check_prefill_rows(w, I, g, out, scores, blk, range(w.n_q))
 
 
-def union_direct(hq, hkv, k, pos0, n_q, seed, shared=0.5, ldb_pad=0):
-    """qsa_prefill_attn on chosen-block lists drawn here (a share of each group's
-    blocks common to its rows), union form against the oracle for every row."""
-    d = dv = 128
+def union_direct(hq, hkv, k, pos0, n_q, seed, shared=0.5, ldb_pad=0, flags=None, d=128):
+    """qsa_prefill_attn on chosen-block lists drawn here (a share of the blocks common
+    to each run of 8 rows; `shared` may also be a function of the row), against the
+    oracle for every row: with `flags`, else the grouped-union form both with its
+    per-group choice and with the union for every group."""
+    dv = d
+    share = shared if callable(shared) else (lambda i: shared)
     n_all = pos0 + n_q
     cap = (n_all + 64) // 4 * 4
     cfg = qb.Config(topk_blocks=k, hq=hq, hkv=hkv, d=d, dv=dv, cap_tokens=cap)
@@ -254,7 +258,7 @@ def union_direct(hq, hkv, k, pos0, n_q, seed, shared=0.5, ldb_pad=0):
             ids = np.arange(nb)
         else:
             if common is None or i % 8 == 0:
-                common = r.choice(nb, size=int(ns * shared), replace=False)
+                common = r.choice(nb, size=int(ns * share(i)), replace=False)
             rest = np.setdiff1d(np.arange(nb), common)
             ids = np.concatenate([common, r.choice(rest, size=ns - common.size, replace=False)])
         B[i, :ns] = np.sort(ids)
@@ -262,15 +266,17 @@ def union_direct(hq, hkv, k, pos0, n_q, seed, shared=0.5, ldb_pad=0):
     vc = torch.zeros((cap, hkv, dv), dtype=torch.float16, device="cuda")
     kc[:n_all], vc[:n_all] = dev(K), dev(V)
     ws = qb.workspace(cfg, n_q, n_all)
-    out = torch.full((n_q, hq, dv), 5.0, device="cuda")
-    qb.qsa_prefill_attn(cfg, dev(Q), pos0, dev(B), ldb, kc, vc, out, ws, flags=UNION)
-    got = host(out)
     scale = 1.0 / np.sqrt(d)
+    refs = []
     for i in range(n_q):
         nb = (pos0 + i + 1) // 4
-        cl = O.cells(B[i, :min(k, nb)], pos0 + i + 1)
-        ref = O.attn_cells(Q[i], K, V, cl, scale)
-        assert_attn_close(got[i], ref, f"row {i}")
+        refs.append(O.attn_cells(Q[i], K, V, O.cells(B[i, :min(k, nb)], pos0 + i + 1), scale))
+    for f in ([UNION, UNION_ALL] if flags is None else [flags]):
+        out = torch.full((n_q, hq, dv), 5.0, device="cuda")
+        qb.qsa_prefill_attn(cfg, dev(Q), pos0, dev(B), ldb, kc, vc, out, ws, flags=f)
+        got = host(out)
+        for i in range(n_q):
+            assert_attn_close(got[i], refs[i], f"flags {f} row {i}")
     return B
 
 
@@ -284,6 +290,22 @@ def union_direct(hq, hkv, k, pos0, n_q, seed, shared=0.5, ldb_pad=0):
 ])
 def test_prefill_attn_union_shapes(gpu, hq, hkv, k, pos0, n_q):
     union_direct(hq, hkv, k, pos0, n_q, 70 + n_q, ldb_pad=3)
+
+
+@pytest.mark.parametrize("hq,hkv,k,pos0,n_q,d", [
+    (32, 4, 64, 3, 70, 128),      # first rows see every block (nb <= k), empty and full tails
+    (32, 4, 64, 257, 33, 128),    # 8 query heads per KV head
+    (16, 4, 64, 1001, 45, 128),   # 4 query heads per KV head
+    (32, 2, 64, 2002, 20, 128),   # 16 query heads per KV head
+    (8, 1, 512, 9000, 17, 128),   # k = 512, one KV head
+    (32, 4, 1024, 5000, 5, 128),  # k = 1024: 4,099 cells, a ragged last tile
+    (32, 4, 512, 5000, 1, 128),   # a single row
+    (32, 4, 64, 1001, 9, 64),     # d = 64: the vector-unit per-row kernel
+    (8, 4, 64, 1001, 9, 128),     # 2 query heads per KV head: the vector-unit kernel
+])
+def test_prefill_attn_per_row_shapes(gpu, hq, hkv, k, pos0, n_q, d):
+    union_direct(hq, hkv, k, pos0, n_q, 170 + n_q, shared=0.0, ldb_pad=5,
+                 flags=qb.QSA_PREFILL_PER_ROW, d=d)
 
 
 def test_prefill_attn_union_past_one_bitmap_window(gpu):
@@ -327,8 +349,16 @@ def test_prefill_attn_broken_ids_are_dropped(gpu):
 
 
 def test_prefill_attn_union_no_overlap(gpu):
-    # rows with disjoint choices: the union holds rows x k blocks
+    # rows with disjoint choices: the union holds rows x k blocks (per row, unless
+    # every group is made to take the union)
     union_direct(32, 4, 64, 40000, 16, 91, shared=0.0)
+
+
+def test_prefill_attn_union_mixed_groups(gpu):
+    # 6 groups of 16 rows, sharing 90% of their blocks in even groups (unions of
+    # about 3.4 k: the union kernel) and nothing in odd ones (16 k: per row), so one
+    # call runs both kernels, each on its own groups; a ragged last group
+    union_direct(32, 4, 128, 30000, 90, 92, shared=lambda i: 0.9 if (i // 16) % 2 == 0 else 0.0)
 
 
 @pytest.mark.parametrize("name", ["prefill_1024_at_126253", "prefill_1024_at_126253_corr"])
@@ -344,4 +374,11 @@ def test_prefill_step_union_full_size_sampled(gpu, name):
                         None)
     ref = host(ref)
     err = np.max(np.abs(out - ref), axis=(1, 2))
+    assert np.all(err <= 2e-3 * np.max(np.abs(ref), axis=(1, 2))), int(np.argmax(err))
+    # and the union for every group, on the same chosen blocks
+    alls = torch.empty_like(dev(out))
+    ws = qb.workspace(cfg, w.n_q, I["depth"] + w.n_q)
+    qb.qsa_prefill_attn(cfg, dev(I["q"]), I["depth"], dev(blk), w.topk, g.k_cache, g.v_cache,
+                        alls, ws, flags=UNION_ALL)
+    err = np.max(np.abs(host(alls) - ref), axis=(1, 2))
     assert np.all(err <= 2e-3 * np.max(np.abs(ref), axis=(1, 2))), int(np.argmax(err))
