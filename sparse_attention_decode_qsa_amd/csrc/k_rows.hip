@@ -36,8 +36,9 @@ constexpr int kRTile = 32;   // cells per tile
 constexpr int kRDim = 128;   // D = DV
 constexpr int kROPitch = kRDim + 4;  // LDS pitch of a head's merged outputs (floats)
 constexpr float kLog2e = 1.4426950408889634f;
-// chosen blocks, the tail's block, -1 up to a whole tile (8 blocks)
-constexpr int kRMaxBlocks = kMaxTopk + 1 + 8;
+// cells of a row: 4 per chosen block and up to 3 of the tail, up to a whole tile;
+// a multiple of 64 (the table is filled a wave, i.e. two tiles, at a time)
+constexpr int kRMaxCells = ((kBlockTokens * kMaxTopk + 3 + 63) / 64) * 64;
 
 // Sum over lanes l, l ^ 16, l ^ 32, l ^ 48, in the same order in all four (the
 // row swaps leave a lane's own value and its partner's; fp addition of two terms
@@ -50,6 +51,48 @@ __device__ __forceinline__ float sum_across_rows(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS of a work group: the byte offset of every cell's row from the head's base
+// (token 0 for a cell that is not there) and a validity mask per tile of 32 cells;
+// after the tiles the same bytes hold the four waves' partial outputs.
+template <int G>
+struct RowsLds {
+    union {
+        struct {
+            uint32_t coff[kRMaxCells];
+            int32_t bl[kRMaxCells / kBlockTokens];  // the row's block ids, -1 dropped
+        };
+        float om[kRWaves][G][kROPitch];
+    };
+    uint32_t tmask[kRMaxCells / kRTile];
+    float mm[kRWaves][G], ll[kRWaves][G];
+};
+
+// A row of a union group: merge of the union kernel's split partials for the
+// group's heads (p = [row][hq][splits][kUnionPartStride]: m, l, -, -, then the
+// outputs), o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+template <int G>
+__device__ void combine_union_row(const RowsArgs &a, int32_t row, int g)
+{
+    const int S = a.splits;
+    for (int i = threadIdx.x; i < G * (kRDim / 4); i += kRThreads) {
+        const int h = g * G + i / (kRDim / 4), c = i % (kRDim / 4);
+        const float *pb = a.part + ((int64_t)row * a.hq + h) * S * kUnionPartStride;
+        float M = -INFINITY;
+        for (int sp = 0; sp < S; sp++)
+            M = fmaxf(M, pb[sp * kUnionPartStride]);
+        const float mref = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f;
+        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < S; sp++) {
+            const f32x4 ml = *(const f32x4 *)(pb + sp * kUnionPartStride);
+            const float w = __builtin_amdgcn_exp2f(ml[0] - mref);
+            L += w * ml[1];
+            o += w * *(const f32x4 *)(pb + sp * kUnionPartStride + 4 + 4 * c);
+        }
+        *(f32x4 *)(a.out + ((int64_t)row * a.hq + h) * kRDim + 4 * c) = o * (1.f / L);
+    }
+}
+
 // 4 waves per SIMD (at most 128 registers): with two loads per lane in flight that
 // is the ~32 KiB per CU the gather runs best at
 template <int G>
@@ -57,14 +100,17 @@ __global__ __launch_bounds__(kRThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
 rows_attn_kernel(RowsArgs a)
 {
     static_assert(G == 4 || G == 8 || G == 16, "query heads per KV head");
-    __shared__ int32_t bl[kRMaxBlocks];
-    __shared__ __attribute__((aligned(16))) float om[kRWaves][G][kROPitch];
-    __shared__ float mm[kRWaves][G], ll[kRWaves][G];
+    __shared__ __attribute__((aligned(16))) RowsLds<G> sm;
 
     const int g = blockIdx.x;
     const int32_t row = blockIdx.y;
-    if (a.n_u && a.n_u[row / a.group_rows] <= a.u_limit)
-        return;  // this row's group is the union kernel's (uniform over the group)
+    if (a.n_u && a.n_u[row / a.group_rows] <= a.u_limit) {
+        // this row's group is the union kernel's (uniform over the group): only the
+        // merge of its split partials, if it has several
+        if (a.splits > 1)
+            combine_union_row<G>(a, row, g);
+        return;
+    }
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
     const int n = lane & 15, j4 = lane >> 4;
 
@@ -73,23 +119,45 @@ rows_attn_kernel(RowsArgs a)
     const int32_t tail = N - kBlockTokens * nbr;
     const int32_t count = kBlockTokens * nsel + tail;
     const int32_t ntile = (count + kRTile - 1) / kRTile;
-    // block list: the chosen ids (an id outside [0, nbr) can only come from a broken
-    // selection: its cells are dropped), then the tail's block
+    const uint32_t rowb = (uint32_t)a.hkv * kRDim * sizeof(h16);  // bytes per token row
+    // the row's blocks: its chosen ids (an id outside [0, nbr) can only come from a
+    // broken selection: its cells are dropped), then the tail's block, read with
+    // all loads in flight at once
     const int32_t *br = a.blk + (int64_t)row * a.ldb;
-    for (int32_t i = t; i < ntile * 8; i += kRThreads) {
-        int32_t id = -1;
-        if (i < nsel) {
-            const int32_t b = br[i];
-            id = ((uint32_t)b < (uint32_t)nbr) ? b : -1;
-        } else if (i == nsel && tail > 0) {
-            id = nbr;
+    constexpr int kBPer = (kRMaxCells / kBlockTokens + kRThreads - 1) / kRThreads;
+    int32_t ids[kBPer];
+#pragma unroll
+    for (int j = 0; j < kBPer; j++) {
+        const int32_t i = t + j * kRThreads;
+        ids[j] = (i < nsel) ? br[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kBPer; j++) {
+        const int32_t i = t + j * kRThreads;
+        if (i < ntile * (kRTile / kBlockTokens)) {
+            int32_t id = -1;
+            if (i < nsel)
+                id = ((uint32_t)ids[j] < (uint32_t)nbr) ? ids[j] : -1;
+            else if (i == nsel && tail > 0)
+                id = nbr;
+            sm.bl[i] = id;
         }
-        bl[i] = id;
+    }
+    __syncthreads();
+    // cells: 4 tokens per block; the tail block's cells past the row's count are not there
+    for (int32_t c = t; c < ntile * kRTile; c += kRThreads) {
+        const int32_t b = sm.bl[c / kBlockTokens];
+        const int32_t tok = (b >= 0 && c < count) ? kBlockTokens * b + (c & 3) : -1;
+        sm.coff[c] = tok >= 0 ? (uint32_t)tok * rowb : 0u;
+        const uint64_t there = __ballot(tok >= 0);  // cells of two tiles per wave
+        if (lane == 0) {
+            sm.tmask[c / kRTile] = (uint32_t)there;
+            sm.tmask[c / kRTile + 1] = (uint32_t)(there >> 32);
+        }
     }
 
-    const int64_t kt = (int64_t)a.hkv * kRDim;  // elements per token row, K and V
-    const h16 *kg = a.k_cache + (int64_t)g * kRDim;
-    const h16 *vg = a.v_cache + (int64_t)g * kRDim;
+    const char *kg = (const char *)(a.k_cache + (int64_t)g * kRDim);
+    const char *vg = (const char *)(a.v_cache + (int64_t)g * kRDim);
     // B of the score product: head n of the group, dims 32 kk + 8 j4 .. + 8
     h16x8 qf[4];
     const h16 *qr = a.q + ((int64_t)row * a.hq + (int64_t)g * G + (n < G ? n : 0)) * kRDim;
@@ -115,60 +183,55 @@ rows_attn_kernel(RowsArgs a)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
+    auto piece = [](const char *base, uint32_t off) { return *(const h16x8 *)(base + off); };
     for (int32_t tile = wave; tile < ntile; tile += kRWaves) {
         const int32_t c0 = tile * kRTile;
         // S^T = K Q^T over 4 k-steps; step kk reads dims 32 kk + 8 j4 of cells
         // c0 + n and c0 + 16 + n (the A rows of the two cell halves)
-        int32_t ktok[2];
+        uint32_t koff[2];
 #pragma unroll
-        for (int tt = 0; tt < 2; tt++) {
-            const int32_t c = c0 + 16 * tt + n;
-            const int32_t b = bl[c >> 2];
-            ktok[tt] = (b >= 0 && c < count) ? kBlockTokens * b + (c & 3) : 0;
-        }
+        for (int tt = 0; tt < 2; tt++)
+            koff[tt] = sm.coff[c0 + 16 * tt + n] + 16u * j4;
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kk = 0; kk < 4; kk++) {
             h16x8 kf[2];
 #pragma unroll
             for (int tt = 0; tt < 2; tt++)
-                kf[tt] = *(const h16x8 *)(kg + (int64_t)ktok[tt] * kt + 32 * kk + 8 * j4);
+                kf[tt] = piece(kg + 64 * kk, koff[tt]);
 #pragma unroll
             for (int tt = 0; tt < 2; tt++)
                 sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[tt], qf[kk], sacc[tt], 0, 0, 0);
             fence();
         }
 
-        // the lane's cells in the score layout: c0 + 16 tt + 4 j4 + e, i.e. the
-        // 4-token blocks 8 tile + 4 tt + j4 (also the V rows it reads below)
-        int32_t vb[2];
-        uint32_t vm = 0u;
+        // the lane's cells in the score layout: c0 + 16 tt + 4 j4 + e (two whole
+        // 4-token blocks, also the V rows it reads below); bit 4 tt + e of vm says
+        // the cell is there (none for a padding head)
+        const uint32_t tm = sm.tmask[tile];
+        const uint32_t vm = (n < G) ? (((tm >> (4 * j4)) & 0xfu) | (((tm >> (16 + 4 * j4)) & 0xfu) << 4))
+                                    : 0u;
+        uint32_t voff[2][4];
 #pragma unroll
         for (int tt = 0; tt < 2; tt++) {
-            vb[tt] = bl[8 * tile + 4 * tt + j4];
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int32_t c = c0 + 16 * tt + 4 * j4 + e;
-                vm |= (vb[tt] >= 0 && c < count) ? 1u << (4 * tt + e) : 0u;
-            }
+            const uint4 o = *(const uint4 *)&sm.coff[c0 + 16 * tt + 4 * j4];
+            voff[tt][0] = o.x + 16u * n;
+            voff[tt][1] = o.y + 16u * n;
+            voff[tt][2] = o.z + 16u * n;
+            voff[tt][3] = o.w + 16u * n;
         }
-
-        // V pieces of the first half's first two cells go out before the softmax;
-        // a cell that is not there reads token 0 (a real, finite row: its p is 0)
-        auto vaddr = [&](int tt, int e) {
-            const int32_t tok = ((vm >> (4 * tt + e)) & 1u) ? kBlockTokens * vb[tt] + e : 0;
-            return (const h16x8 *)(vg + (int64_t)tok * kt + 8 * n);
-        };
+        // the first half's first two V pieces go out before the softmax (a cell that
+        // is not there reads token 0: a real, finite row, and its p is 0)
         h16x8 vin[4];
-        vin[0] = *vaddr(0, 0);
-        vin[1] = *vaddr(0, 1);
+        vin[0] = piece(vg, voff[0][0]);
+        vin[1] = piece(vg, voff[0][1]);
 
         // online softmax of head n over the tile's cells (order 4 tt + e)
         float s[8];
         float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            s[i] = (((vm >> i) & 1u) && n < G) ? sacc[i / 4][i % 4] : -INFINITY;
+            s[i] = ((vm >> i) & 1u) ? sacc[i / 4][i % 4] : -INFINITY;
             tmax = fmaxf(tmax, s[i]);
         }
         tmax = max_across_rows(tmax);
@@ -197,14 +260,14 @@ rows_attn_kernel(RowsArgs a)
 #pragma unroll
         for (int tt = 0; tt < 2; tt++) {
             if (tt == 1) {
-                vin[0] = *vaddr(1, 0);
-                vin[1] = *vaddr(1, 1);
+                vin[0] = piece(vg, voff[1][0]);
+                vin[1] = piece(vg, voff[1][1]);
             }
             // the pair in flight is used before the next pair goes out
             asm volatile("" : "+v"(vin[0]), "+v"(vin[1]));
             fence();
-            vin[2] = *vaddr(tt, 2);
-            vin[3] = *vaddr(tt, 3);
+            vin[2] = piece(vg, voff[tt][2]);
+            vin[3] = piece(vg, voff[tt][3]);
             const h16x4 pf = h16x4{(h16)s[4 * tt], (h16)s[4 * tt + 1], (h16)s[4 * tt + 2],
                                    (h16)s[4 * tt + 3]};
 #pragma unroll
@@ -216,18 +279,20 @@ rows_attn_kernel(RowsArgs a)
         }
     }
 
-    // merge of the four waves: head n's dims 32 j4 + 8 e + r from this lane
+    // merge of the four waves: head n's dims 32 j4 + 8 e + r from this lane (the
+    // cell offsets are dead once every wave is past its tiles)
     const float lsum = sum_across_rows(l_run);
+    __syncthreads();
     if (n < G) {
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            float *op = &om[wave][n][32 * j4 + 8 * e];
+            float *op = &sm.om[wave][n][32 * j4 + 8 * e];
             *(f32x4 *)op = f32x4{oacc[0][e], oacc[1][e], oacc[2][e], oacc[3][e]};
             *(f32x4 *)(op + 4) = f32x4{oacc[4][e], oacc[5][e], oacc[6][e], oacc[7][e]};
         }
         if (j4 == 0) {
-            mm[wave][n] = m_run;
-            ll[wave][n] = lsum;
+            sm.mm[wave][n] = m_run;
+            sm.ll[wave][n] = lsum;
         }
     }
     __syncthreads();
@@ -237,14 +302,14 @@ rows_attn_kernel(RowsArgs a)
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kRWaves; w++)
-            M = fmaxf(M, mm[w][h]);
+            M = fmaxf(M, sm.mm[w][h]);
         const float Mref = (M == -INFINITY) ? 0.f : M;
         float L = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < kRWaves; w++) {
-            const float sc = __builtin_amdgcn_exp2f(mm[w][h] - Mref);
-            L += sc * ll[w][h];
-            o += sc * om[w][h][d];
+            const float sc = __builtin_amdgcn_exp2f(sm.mm[w][h] - Mref);
+            L += sc * sm.ll[w][h];
+            o += sc * sm.om[w][h][d];
         }
         orow[i] = o / L;
     }
@@ -252,9 +317,12 @@ rows_attn_kernel(RowsArgs a)
 
 }  // namespace
 
-bool rows_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k)
+bool rows_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k, int64_t n_tokens)
 {
     if (hkv <= 0 || hq % hkv || d != kRDim || dv != kRDim || k > kMaxTopk)
+        return false;
+    // cell offsets are 32-bit byte offsets into the caches
+    if (n_tokens * hkv * kRDim * (int64_t)sizeof(h16) > (int64_t)UINT32_MAX)
         return false;
     const int32_t G = hq / hkv;
     return G == 4 || G == 8 || G == 16;
@@ -264,7 +332,8 @@ hipError_t launch_rows_attn(const RowsArgs &a, hipStream_t s)
 {
     if (a.n_q <= 0)
         return hipSuccess;
-    if (!rows_supported(a.hq, a.hkv, kRDim, kRDim, a.k) || (a.n_u && a.group_rows <= 0))
+    if (!rows_supported(a.hq, a.hkv, kRDim, kRDim, a.k, (int64_t)a.pos0 + a.n_q) ||
+        (a.n_u && a.group_rows <= 0) || (a.splits > 1 && (!a.n_u || !a.part)))
         return hipErrorInvalidValue;
     const dim3 grid((uint32_t)a.hkv, (uint32_t)a.n_q);
     switch (a.hq / a.hkv) {

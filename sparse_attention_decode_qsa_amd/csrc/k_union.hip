@@ -55,7 +55,7 @@ struct UnionBuildLds {
 
 __global__ __launch_bounds__(kUBThreads) void union_build_kernel(
     const int32_t *__restrict__ blk, int32_t ldb, int32_t pos0, int32_t n_q, int32_t k, int32_t G,
-    int32_t cap_u, int32_t *__restrict__ uid, uint32_t *__restrict__ umask,
+    int32_t cap_u, int32_t u_limit, int32_t *__restrict__ uid, uint32_t *__restrict__ umask,
     int32_t *__restrict__ n_u)
 {
     __shared__ UnionBuildLds sm;
@@ -103,6 +103,15 @@ __global__ __launch_bounds__(kUBThreads) void union_build_kernel(
         for (int32_t w = wa; w < wb; w++)
             c += __popc(sm.bits[w]);
         uint32_t pos = base + wg_exclusive_scan<kUBThreads>(c, sm.S);
+        if (t == kUBThreads - 1)
+            sm.total = pos + c;
+        __syncthreads();
+        if (sm.total > (uint32_t)u_limit) {
+            // past the limit: the group goes per row, only its count is needed
+            if (t == 0)
+                n_u[g] = (int32_t)sm.total;
+            return;
+        }
         for (int32_t w = wa; w < wb; w++) {
             sm.pre[w] = pos;
             uint32_t m = sm.bits[w];
@@ -551,7 +560,7 @@ hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s)
     const int32_t groups = (u.n_q + G - 1) / G;
     const int32_t cap_u = G * u.k;
     hipLaunchKernelGGL(union_build_kernel, dim3((uint32_t)groups), dim3(kUBThreads), 0, s, u.blk,
-                       u.ldb, u.pos0, u.n_q, u.k, G, cap_u, u.uid, u.umask, u.n_u);
+                       u.ldb, u.pos0, u.n_q, u.k, G, cap_u, u.u_limit, u.uid, u.umask, u.n_u);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -583,16 +592,16 @@ hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s)
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    if (u.splits > 1) {
+    if (u.u_limit >= cap_u) {
+        // no group can exceed the limit: the union kernel's partials, if split
+        if (u.splits == 1)
+            return hipSuccess;
         hipLaunchKernelGGL(union_combine_kernel, dim3((uint32_t)u.n_q), dim3(kUCombThreads), 0, s,
                            u.part, u.hq, u.splits, u.n_u, G, u.u_limit, u.out);
-        e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
+        return hipGetLastError();
     }
-    if (u.u_limit >= cap_u)
-        return hipSuccess;  // no group can exceed the limit
-    // the groups whose union is too large for the union form to pay: per row
+    // the groups whose union is too large for the union form to pay go per row; the
+    // same launch merges the other groups' split partials
     RowsArgs ra;
     ra.q = u.q;
     ra.blk = u.blk;
@@ -609,6 +618,8 @@ hipError_t launch_union_attn(const UnionArgs &u, hipStream_t s)
     ra.n_u = u.n_u;
     ra.group_rows = G;
     ra.u_limit = u.u_limit;
+    ra.part = u.part;
+    ra.splits = u.splits;
     return launch_rows_attn(ra, s);
 }
 

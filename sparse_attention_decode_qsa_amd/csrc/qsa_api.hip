@@ -642,9 +642,13 @@ static hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32
         u.hkv = cfg->hkv;
         u.scale = cfg->attn_scale;
         u.splits = union_splits(n_q, cfg->hq, cfg->hkv);
-        u.u_limit = (flags & QSA_PREFILL_UNION_ALL) ? INT32_MAX
-                                                    : union_limit(cfg->hq, cfg->hkv,
-                                                                  cfg->topk_blocks);
+        // the union for every group when asked, or when the per-row kernel cannot
+        // take this shape
+        const bool rows_ok = rows_supported(cfg->hq, cfg->hkv, cfg->d, cfg->dv,
+                                            cfg->topk_blocks, (int64_t)pos0 + n_q);
+        u.u_limit = ((flags & QSA_PREFILL_UNION_ALL) || !rows_ok)
+                        ? INT32_MAX
+                        : union_limit(cfg->hq, cfg->hkv, cfg->topk_blocks);
         u.uid = at<int32_t>(ws, L.uid);
         u.umask = at<uint32_t>(ws, L.umask);
         u.n_u = at<int32_t>(ws, L.nu);
@@ -652,7 +656,8 @@ static hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32
         u.out = out;
         return launch_union_attn(u, s);
     }
-    if (rows_supported(cfg->hq, cfg->hkv, cfg->d, cfg->dv, cfg->topk_blocks)) {
+    if (rows_supported(cfg->hq, cfg->hkv, cfg->d, cfg->dv, cfg->topk_blocks,
+                       (int64_t)pos0 + n_q)) {
         RowsArgs ra;
         ra.q = q;
         ra.blk = blk;
@@ -669,6 +674,8 @@ static hipError_t prefill_attn_launch(const qsa_config *cfg, const h16 *q, int32
         ra.n_u = nullptr;
         ra.group_rows = 1;
         ra.u_limit = 0;
+        ra.part = nullptr;
+        ra.splits = 0;
         return launch_rows_attn(ra, s);
     }
     AttnArgs a = attn_base(cfg);

@@ -195,9 +195,12 @@ struct RowsArgs {
     float *out;             // [n_q][hq][128]
     const int32_t *n_u;     // union blocks per row group (NULL: every row here)
     int32_t group_rows;     // rows per group of n_u
-    int32_t u_limit;        // rows of a group with n_u <= u_limit are left out
+    int32_t u_limit;        // rows of a group with n_u <= u_limit are the union's:
+    const float *part;      // their split partials (splits > 1), merged here
+    int32_t splits;
 };
-bool rows_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k);
+// n_tokens: tokens in the caches the rows read (pos0 + n_q)
+bool rows_supported(int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t k, int64_t n_tokens);
 hipError_t launch_rows_attn(const RowsArgs &a, hipStream_t s);
 
 // ---- MLA list (k_mla.hip) ---------------------------------------------------
