@@ -518,6 +518,7 @@ def bench_prefill(args):
         "groups": len(ublocks),
         "kv_bytes_streamed": u_bytes,
         "kv_achieved_gbps": round(u_bytes / (attn_union_all_us * 1e-6) / 1e9, 1),
+        "counter_traffic_bytes": traffic_for("union_attn_kernel", "k_union.hip", w.name),
         "mfma_flop": u_flop,
         "mfma_achieved_tflops": round(u_flop / (attn_union_all_us * 1e-6) / 1e12, 2),
         "mfma_frac": round(u_flop / (attn_union_all_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,

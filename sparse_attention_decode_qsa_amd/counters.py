@@ -37,11 +37,21 @@ def per_dispatch(path: str, counter: str) -> dict:
     return vals
 
 
-def mean_kib(path: str, counter: str, sub: str):
-    v = [x for (_, name), x in per_dispatch(path, counter).items() if sub in name]
+def mean_kib(path: str, counter: str, sub: str, ids=None):
+    """Mean over the dispatches whose name contains `sub` (and whose id is in `ids`,
+    when given), and their count."""
+    v = [x for (d, name), x in per_dispatch(path, counter).items()
+         if sub in name and (ids is None or d in ids)]
     if not v:
         raise SystemExit(f"no dispatch matching {sub!r} in {path}")
     return sum(v) / len(v), len(v)
+
+
+def ids_with_fetch(path: str, sub: str, min_kib: float) -> set:
+    """Dispatch ids of the kernel whose FETCH_SIZE is at least min_kib (the runs of
+    one command give the same ids, so the WRITE_SIZE run is read for the same ones)."""
+    return {d for (d, name), x in per_dispatch(path, "FETCH_SIZE").items()
+            if sub in name and x >= min_kib}
 
 
 def src_hash(name: str) -> str:
@@ -60,14 +70,21 @@ def main():
     ap.add_argument("--key", required=True)
     ap.add_argument("--workload", required=True, help="the bench.py workload the runs used")
     ap.add_argument("--source", default="k_score.hip")
+    ap.add_argument("--min-fetch-kib", type=float, default=None,
+                    help="only the dispatches that fetch at least this much (e.g. to leave "
+                         "out launches whose work groups all exit at once)")
     ap.add_argument("--json", default=None)
     a = ap.parse_args()
     cb = float(a.calib_mib << 20)
     out = {"workload": a.workload, "source_hash": src_hash(a.source), "kernel_match": a.kernel}
     total = 0.0
+    ids = None
+    if a.min_fetch_kib is not None:
+        ids = ids_with_fetch(a.fetch, a.kernel, a.min_fetch_kib)
+        out["min_fetch_kib"] = a.min_fetch_kib
     for name, kpath, cpath, counter in (("fetch", a.fetch, a.calib_fetch, "FETCH_SIZE"),
                                         ("write", a.write, a.calib_write, "WRITE_SIZE")):
-        kib, n = mean_kib(kpath, counter, a.kernel)
+        kib, n = mean_kib(kpath, counter, a.kernel, ids)
         ckib, cn = mean_kib(cpath, counter, "copyBuffer")
         factor = cb / (ckib * 1024.0)
         out[name] = dict(counter=counter, kib_per_dispatch=round(kib, 1), dispatches=n,
