@@ -272,24 +272,25 @@ def bench_decode(args):
     rowc = w.h_idx * w.d_idx // 8
     step_kernel = f"score_decode_kernel<{rowc},{2 if rowc >= 128 else 4},512,{rows},true,true>"
 
-    # the stand-alone scan (qsa_index_score), back-to-back launches between two
-    # events (dispatch gaps included)
+    # the stand-alone scan (qsa_index_score), back to back over the layers' caches,
+    # each launch's own start and end times
     nb = w.n_tokens // 4
     scores = torch.empty(nb + 64, dtype=torch.float32, device=dev)
     sreps = 12 * max(1, args.kernel_reps // 12)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * sreps)]
     with torch.cuda.stream(stream):
+        for e in sev:
+            e.record(stream)
         for r in range(12):
             st = layers[r % n_layers]
             qb.qsa_index_score(cfg, st["q_idx"], w.n_tokens - 1, st["layer"].k_pool, scores)
-        k0 = torch.cuda.Event(enable_timing=True)
-        k1 = torch.cuda.Event(enable_timing=True)
-        k0.record(stream)
+        torch.cuda._sleep(hold_cycles(stream, args.trace_hold_ms))
         for r in range(sreps):
             st = layers[r % n_layers]
+            qb.qsa_trace_scan(sev[2 * r], sev[2 * r + 1])
             qb.qsa_index_score(cfg, st["q_idx"], w.n_tokens - 1, st["layer"].k_pool, scores)
-        k1.record(stream)
-    k1.synchronize()
-    alone_us = k0.elapsed_time(k1) * 1e3 / sreps
+    stream.synchronize()
+    alone_us = sum(sev[2 * r].elapsed_time(sev[2 * r + 1]) for r in range(sreps)) * 1e3 / sreps
     alone_bytes = nb * row
     alone_gbps = alone_bytes / (alone_us * 1e-6) / 1e9
 
@@ -345,7 +346,8 @@ def bench_decode(args):
                 "traffic": traffic_for("score_decode_kernel", "k_score.hip", w.name),
                 "algorithmic_bytes_per_launch": alone_bytes,
                 "avg_launch_us": round(alone_us, 3),
-                "timing": f"{sreps} back-to-back qsa_index_score launches between two events",
+                "timing": f"kernel start/end events of {sreps} back-to-back qsa_index_score "
+                          f"launches (qsa_trace_scan)",
             },
         },
         "step_hbm": {
@@ -450,6 +452,8 @@ def bench_prefill(args):
         qb.qsa_index_score(cfg, q_idx, depth, pools[turn[0] % len(pools)], scores, ld=ld)
         turn[0] += 1
 
+    # plain launches back to back (a scoring launch takes ~150 us, the gaps ~1%): with
+    # start/stop events on the launch this kernel itself runs ~7% slower
     score_us = _timed(stream, score_once, args.steps)
     topk_us = _timed(stream, lambda: qb.qsa_topk_blocks(cfg, scores, n_q, ld, depth, blk, nsel,
                                                         ws), args.steps)

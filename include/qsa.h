@@ -347,15 +347,15 @@ QSA_API int qsa_mla_list_status(const int32_t *n_list, int32_t list_cap, int32_t
                         qsa_stream_t stream);
 
 /*
- * Kernel timing of one decode step's scoring launch, for tracing (no part of the
- * method; the step's results do not change).  start_event and stop_event are
- * hipEvent_t handles that the caller created, with timing enabled, on the device
- * of the step's stream.  The calling thread's next qsa_decode_step,
- * qsa_decode_step_noalloc or qsa_decode_multi launches its scoring kernel (the
- * appends, the block scores and the candidate lists) so that the two events take
- * that kernel's own start and end times (hipEventElapsedTime then gives its
- * duration); that call clears the setting, whatever it returns.  Both NULL clear
- * it.  The events stay the caller's.  The step must not be under stream capture.
+ * Kernel timing of one scoring launch, for tracing (no part of the method; results
+ * do not change).  start_event and stop_event are hipEvent_t handles that the
+ * caller created, with timing enabled, on the device of the call's stream.  The
+ * calling thread's next qsa_decode_step, qsa_decode_step_noalloc, qsa_decode_multi
+ * or qsa_index_score launches its scoring kernel (in a decode step: the appends,
+ * the block scores and the candidate lists) so that the two events take that
+ * kernel's own start and end times (hipEventElapsedTime then gives its duration);
+ * that call clears the setting, whatever it returns.  Both NULL clear it.  The
+ * events stay the caller's.  The call must not be under stream capture.
  * Errors: INVALID (exactly one of the two is NULL).
  */
 QSA_API int qsa_trace_scan(void *start_event, void *stop_event);

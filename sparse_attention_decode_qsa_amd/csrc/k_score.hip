@@ -23,8 +23,6 @@
 // query row, the kListLen best of their union (in any order) and writes them, so
 // the top-k reads a few thousand candidates per query row instead of the whole
 // score row.
-#include <hip/hip_ext.h>
-
 #include "qsa_append.h"
 
 namespace qsa {
@@ -277,21 +275,9 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
     }
 }
 
-// A launch of kern with the events of ev (kernel start and end times), else plain.
-template <typename F, typename... Args>
-void launch_ev(F kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, KernelEvents ev,
-               Args... args)
-{
-    if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
-    else
-        hipLaunchKernelGGL(kern, grid, block, lds, s, args...);
-}
-
-// Work groups of the decode-step scan, besides the append's.  Two of them are
-// resident per CU (8 waves each; the append's fp64 RoPE angles set the register
-// count), so 767 is one and a half rounds over 256 CUs; measured at 256k tokens it
-// beat a full two rounds (1,023) by 1% per step and one round (511) by 4%.
+// Work groups of the decode-step scan, besides the append's: with the append work
+// group, three per CU (8 waves each, 78 registers: the append's fp64 RoPE angles set
+// the count), so every work group starts in the first round.
 constexpr int64_t kStepScanWgs = 767;
 static_assert(kStepScanWgs < kListWgs, "one list per thread of the top-k selection");
 
@@ -338,16 +324,20 @@ hipError_t launch_rowc(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb, f
         constexpr int RPW = kWave / LPR;
         constexpr int NW = kThreads / kWave;
         const int64_t groups = ((int64_t)nb + RPW - 1) / RPW;
-        int64_t grid = (groups + (int64_t)NW * U - 1) / ((int64_t)NW * U);
-        if (grid > 2048)
-            grid = 2048;
+        // about 8 row groups per wave, 512 to 2,048 work groups (fewer when there are
+        // fewer row groups than waves): measured at 31,898 to 255,181 tokens, 512
+        // groups beat 2,048 by 1-2% on the short caches and lose 0.5-1% on the long
+        int64_t grid = (groups + (int64_t)NW * 8 - 1) / ((int64_t)NW * 8);
+        grid = grid > 2048 ? 2048 : (grid < 512 ? 512 : grid);
+        const int64_t gmax = (groups + (int64_t)NW - 1) / NW;
+        if (grid > gmax)
+            grid = gmax;
         if (grid < 1)
             grid = 1;
         const AppendArgs none{};
         const CandLists nol{};
-        hipLaunchKernelGGL((score_decode_kernel<ROWC, U, kThreads, 1, false, false>),
-                           dim3((uint32_t)grid), dim3(kThreads), 0, s, q, pool, nb, scores, ld,
-                           none, nol);
+        launch_ev(score_decode_kernel<ROWC, U, kThreads, 1, false, false>, dim3((uint32_t)grid),
+                  dim3(kThreads), 0, s, ev, q, pool, nb, scores, ld, none, nol);
         return hipGetLastError();
     }
     switch (n_q) {

@@ -152,7 +152,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_prefill_kernel(const h16 *_
 }  // namespace
 
 hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h16 *pool,
-                                int32_t row_elems, float *scores, int32_t ld, hipStream_t s)
+                                int32_t row_elems, float *scores, int32_t ld, hipStream_t s,
+                                KernelEvents ev)
 {
     const int32_t nb_max = (pos0 + n_q) / kBlockTokens;
     if (nb_max <= 0)
@@ -162,8 +163,8 @@ hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h
     const int32_t ncol = (nb_max + TN - 1) / TN, nrow = (n_q + TM - 1) / TM;
     // every XCD gets whole columns (all their row tiles); columns past ncol exit
     const int64_t wgs = (int64_t)((ncol + kXcds - 1) / kXcds) * kXcds * nrow;
-    hipLaunchKernelGGL(score_prefill_kernel, dim3((uint32_t)wgs), dim3(kThreads), 0, s, q, n_q,
-                       pos0, pool, row_elems, scores, ld, ncol, nrow);
+    launch_ev(score_prefill_kernel, dim3((uint32_t)wgs), dim3(kThreads), 0, s, ev, q, n_q, pos0,
+              pool, row_elems, scores, ld, ncol, nrow);
     return hipGetLastError();
 }
 

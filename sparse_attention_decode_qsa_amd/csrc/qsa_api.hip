@@ -514,6 +514,9 @@ int qsa_kv_append(const qsa_config *cfg, const uint16_t *k_new, const uint16_t *
 int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, int32_t pos0,
                     const uint16_t *k_pool, float *scores, int32_t ld, qsa_stream_t stream)
 {
+    // the events set by qsa_trace_scan are for this call only, whatever it returns
+    const KernelEvents ev = g_scan_events;
+    g_scan_events = KernelEvents{};
     int r = check_cfg(cfg);
     if (r)
         return r;
@@ -530,13 +533,14 @@ int qsa_index_score(const qsa_config *cfg, const uint16_t *q_idx, int32_t n_q, i
     const int32_t row = cfg->h_idx * cfg->d_idx;
     if (n_q == 1) {
         HIP_CHECK(launch_score_decode(H(q_idx), 1, H(k_pool), (pos0 + 1) / kBlockTokens, row,
-                                      scores, 0, nullptr, nullptr, nullptr, (hipStream_t)stream));
+                                      scores, 0, nullptr, nullptr, nullptr, (hipStream_t)stream,
+                                      ev));
         return QSA_OK;
     }
     if (ld % 4)
         return fail(QSA_ERR_INVALID, "qsa_index_score: ld must be a multiple of 4 for n_q > 1");
     HIP_CHECK(launch_score_prefill(H(q_idx), n_q, pos0, H(k_pool), row, scores, ld,
-                                   (hipStream_t)stream));
+                                   (hipStream_t)stream, ev));
     return QSA_OK;
 }
 

@@ -33,11 +33,13 @@ __device__ void append_pool(const AppendArgs &a, int32_t b0, int32_t nbk, f32x2 
 {
     const int32_t d = a.d, H = a.H, half = d / 2;
     const int64_t row = (int64_t)H * d;
-    // RoPE angles of pair i at block position 4b: 4b * base^(-2i/d), in fp64.
+    // RoPE angles of pair i at block position 4b: 4b * base^(-2i/d), in fp64; the
+    // power as 2^(-2i/d * log2(base)) (the fused decode scan's register count, and so
+    // its occupancy, is set by this code: pow takes 16 more registers than exp2)
     for (int e = threadIdx.x; e < nbk * half; e += NT) {
         const int bl = e / half, i = e - bl * half;
         const double pos = (double)kBlockTokens * (double)(b0 + bl);
-        const double inv = pow((double)a.base, -2.0 * (double)i / (double)d);
+        const double inv = exp2(-2.0 * (double)i / (double)d * log2((double)a.base));
         double sn, cn;
         sincos(pos * inv, &sn, &cn);
         cs[e] = f32x2{(float)cn, (float)sn};

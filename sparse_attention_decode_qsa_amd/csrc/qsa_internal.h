@@ -2,6 +2,7 @@
 // kernel files.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -54,18 +55,29 @@ struct CandLists {
 struct KernelEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
+// A launch of kern with the events of ev, else plain.
+template <typename F, typename... Args>
+void launch_ev(F kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, KernelEvents ev,
+               Args... args)
+{
+    if (ev.start || ev.stop)
+        hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kern, grid, block, lds, s, args...);
+}
 // Stand-alone scan (qsa_index_score, ap NULL, n_q = 1): scores[0, nb).
 // Decode-step scan (ap non-NULL): the append work runs in the same launch (at
 // most one completed block, block nb; its scores are written too); n_q queries
 // (rows of q) score every row read once, query i into scores[i * ld ..]; with
 // cl (n_q = 1 only) every work group also writes its candidate list and
-// *n_lists gets the list count.  ev: the decode-step launch records them.
+// *n_lists gets the list count.  ev: the scoring launch records them.
 hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb,
                                int32_t row_elems, float *scores, int32_t ld, const AppendArgs *ap,
                                const CandLists *cl, int32_t *n_lists, hipStream_t s,
                                KernelEvents ev = {});
 hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h16 *pool,
-                                int32_t row_elems, float *scores, int32_t ld, hipStream_t s);
+                                int32_t row_elems, float *scores, int32_t ld, hipStream_t s,
+                                KernelEvents ev = {});
 
 // ---- top-k (k_topk.hip) -----------------------------------------------------
 // One decode row: candidate lists built from the scores (in cl), then the list
