@@ -351,6 +351,12 @@ hipError_t launch_rowc(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb, f
 
 }  // namespace
 
+int32_t scan_rows_per_group(int32_t row_elems)
+{
+    const int32_t rowc = row_elems / 8;  // 16-byte chunks per row
+    return rowc >= kWave ? 1 : kWave / rowc;
+}
+
 hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb,
                                int32_t row_elems, float *scores, int32_t ld, const AppendArgs *ap,
                                const CandLists *cl, int32_t *n_lists, hipStream_t s,

@@ -47,6 +47,7 @@ struct TailArgs {
     int32_t splits;       // ceil(cells / (64 chunks)) of the row with the most cells
     float *part;          // [rows][hq][splits][DV + 2]
     int32_t *blk_out;     // optional, [rows][k]
+    int32_t scan_rpw;     // rows per row group of the decode scan (its list layout)
 };
 
 template <int G, int D, int DV>
@@ -80,6 +81,86 @@ __device__ __forceinline__ float row_group_sum(float x)
     if (W == 16)
         x += dpp<kDppRowMirror>(x);
     return x;
+}
+
+// Places the chosen blocks once the lists hold the top-k exactly (every key >= rs):
+// an exclusive prefix over the work group (wave scans, one barrier, then the
+// totals of the waves below) gives each thread the positions of its keys, and
+// place(pos, id) is called for positions below k.
+template <typename Place>
+__device__ __forceinline__ void place_chosen(const uint64_t (&R)[kListLen], uint64_t rs,
+                                             uint32_t k, uint32_t nb, uint32_t *wsum,
+                                             Place place)
+{
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kListLen; j++)
+        c += R[j] >= rs ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan(c);
+    if (lane == kWave - 1)
+        wsum[wave] = incl;
+    __syncthreads();
+    uint32_t pos = incl - c;
+#pragma unroll
+    for (int i = 0; i < kNT / kWave; i += 4) {
+        const uint4 v = *(const uint4 *)&wsum[i];
+        pos += (i < wave ? v.x : 0u) + (i + 1 < wave ? v.y : 0u) +
+               (i + 2 < wave ? v.z : 0u) + (i + 3 < wave ? v.w : 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < kListLen; j++)
+        if (R[j] >= rs) {
+            uint32_t id = rank_id(R[j]);
+            id = id < nb ? id : 0u;
+            if (pos < k)
+                place((int32_t)pos, (int32_t)id);
+            pos++;
+        }
+}
+
+// Where the chosen blocks of one split go: position i to cells 4i .. 4i + 3 of the
+// split's token table (positions b_lo .. b_hi - 1), and to ids[i] when want_ids.
+struct SplitPlace {
+    int32_t *toks;
+    int32_t *ids;
+    uint32_t *wsum;
+    int32_t b_lo, b_hi;
+    bool want_ids;
+    __device__ void operator()(int32_t pos, int32_t id) const
+    {
+        if (pos >= b_lo && pos < b_hi) {
+#pragma unroll
+            for (int e = 0; e < kBlockTokens; e++)
+                toks[(pos - b_lo) * kBlockTokens + e] = kBlockTokens * id + e;
+        }
+        if (want_ids)
+            ids[pos] = id;
+    }
+};
+
+struct ListKeys {
+    uint64_t v[kListLen];
+};
+
+// The lists hide chosen rows (rs = R* of the lists): widen them with their work
+// groups' rows (widen_lists), select again and, when that is exact, place the
+// chosen blocks.  Returns false if the lists are still not enough (the caller then
+// selects from the whole score row).  Out of line, so that the step's usual path
+// carries none of this code.  All kNT threads call it.
+__device__ __noinline__ bool widen_select_place(ListKeys keys, uint32_t nrows, int32_t W,
+                                                uint64_t rs, const float *scores,
+                                                ListLayout lay, uint32_t k, uint32_t nb,
+                                                ListSelLds &L, SplitPlace pl)
+{
+    uint64_t(&R)[kListLen] = keys.v;
+    if (!widen_lists(R, &nrows, W, rs, scores, lay, L))
+        return false;
+    __syncthreads();
+    if (lists_select(R, nrows, (int)threadIdx.x < W, k, L, &rs) != kListsExact)
+        return false;
+    place_chosen(R, rs, k, nb, pl.wsum, pl);
+    return true;
 }
 
 template <int G, int D, int DV>
@@ -163,37 +244,24 @@ __global__ __launch_bounds__(kNT) void step_tail_kernel(TailArgs a)
         }
     } else {
         uint64_t rs = 0;
-        if (lists_select_rest(R, (uint32_t)a.k, sm.L, &rs)) {
-            uint32_t c = 0;
+        const int sel = lists_select_rest(R, (uint32_t)a.k, sm.L, &rs);
+        const SplitPlace pl{sm.toks, sm.ids, sm.wsum, b_lo, b_hi, want_blk};
+        bool placed = false;
+        if (sel == kListsExact) {
+            place_chosen(R, rs, (uint32_t)a.k, (uint32_t)nb, sm.wsum, pl);
+            placed = true;
+        } else if (sel == kListsHide) {
+            // the scan's row layout: list 0 is the append's, scan work group
+            // b = list - 1 of n_lists - 1 owns runs of 4 row groups
+            ListKeys keys;
 #pragma unroll
             for (int j = 0; j < kListLen; j++)
-                c += R[j] >= rs ? 1u : 0u;
-            // exclusive prefix over the work group: wave scans, one barrier, then
-            // the totals of the waves below (sm.wsum is written only here)
-            const uint32_t incl = wave_incl_scan(c);
-            if (lane == kWave - 1)
-                sm.wsum[wave] = incl;
-            __syncthreads();
-            uint32_t pos = incl - c;
-#pragma unroll
-            for (int i = 0; i < kNT / kWave; i += 4) {
-                const uint4 v = *(const uint4 *)&sm.wsum[i];
-                pos += (i < wave ? v.x : 0u) + (i + 1 < wave ? v.y : 0u) +
-                       (i + 2 < wave ? v.z : 0u) + (i + 3 < wave ? v.w : 0u);
-            }
-#pragma unroll
-            for (int j = 0; j < kListLen; j++)
-                if (R[j] >= rs) {
-                    uint32_t id = rank_id(R[j]);
-                    id = id < (uint32_t)nb ? id : 0u;
-                    if (pos < (uint32_t)a.k) {
-                        place((int32_t)pos, (int32_t)id);
-                        if (want_blk)
-                            sm.ids[pos] = (int32_t)id;
-                    }
-                    pos++;
-                }
-        } else {
+                keys.v[j] = R[j];
+            const ListLayout lay{1, a.n_lists - 1, a.scan_rpw, (uint32_t)(a.pos0 / kBlockTokens)};
+            placed = widen_select_place(keys, nrows, a.n_lists, rs, scores, lay, (uint32_t)a.k,
+                                        (uint32_t)nb, sm.L, pl);
+        }
+        if (!placed) {
             __syncthreads();
             select_row_global<kNT>(scores, (uint32_t)nb, a.k, sm.ids, sm.L.hist[0],
                                    sm.u.sel.cand, sm.u.sel.bitmap, sm.L.S);
@@ -334,7 +402,7 @@ hipError_t launch_step_tail(const StepTail &st, hipStream_t s)
     const int32_t n_last = st.pos0 + st.rows;  // tokens seen by the last row
     if (st.rows < 1 || st.pos0 < 0 || st.k < 1 || st.k > kMaxTopk ||
         n_last / kBlockTokens > kMaxBlocks || st.n_lists < 1 || st.n_lists > kListWgs ||
-        st.hq % st.hkv)
+        st.hq % st.hkv || st.scan_rpw < 1)
         return hipErrorInvalidValue;
     TailArgs a;
     a.cl = st.cl;
@@ -369,6 +437,7 @@ hipError_t launch_step_tail(const StepTail &st, hipStream_t s)
         return hipErrorInvalidValue;
     a.part = st.part;
     a.blk_out = st.blk_out;
+    a.scan_rpw = st.scan_rpw;
     const int G = st.hq / st.hkv;
     hipError_t e;
     if (st.d == 128 && st.dv == 128)

@@ -372,6 +372,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
 __global__ __launch_bounds__(kSelThreads) void topk_lists_kernel(const float *__restrict__ scores,
                                                                  int32_t nb, int32_t k,
                                                                  CandLists cl, int32_t W,
+                                                                 ListLayout lay,
                                                                  int32_t *__restrict__ blk,
                                                                  int32_t *__restrict__ n_sel)
 {
@@ -386,7 +387,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_lists_kernel(const float *__
     load_list(cl, W, R, &nrows);
     zero_words<NT>(bitmap, ((uint32_t)nb + 31) / 32);
     uint64_t rs = 0;
-    if (lists_select(R, nrows, t < W, (uint32_t)k, L, &rs)) {
+    int sel;
+    // at most two passes, the second after widening (one copy of the selection)
+#pragma clang loop unroll(disable)
+    for (int pass = 0;; pass++) {
+        sel = lists_select(R, nrows, t < W, (uint32_t)k, L, &rs);
+        if (sel != kListsHide || pass > 0 || !widen_lists(R, &nrows, W, rs, scores, lay, L))
+            break;
+        __syncthreads();
+    }
+    if (sel == kListsExact) {
 #pragma unroll
         for (int j = 0; j < kListLen; j++)
             if (R[j] >= rs) {
@@ -523,7 +533,8 @@ hipError_t launch_score_lists(const float *scores, int32_t rows, int32_t ld, int
 }
 
 hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,
-                             int32_t n_lists, int32_t *blk, int32_t *n_sel, hipStream_t s)
+                             int32_t n_lists, int32_t *blk, int32_t *n_sel, hipStream_t s,
+                             int32_t scan_rpw, int32_t n_scan)
 {
     if (nb > kMaxBlocks || n_lists < 1 || n_lists > kListWgs)
         return hipErrorInvalidValue;
@@ -532,8 +543,12 @@ hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLis
         hipLaunchKernelGGL(iota_kernel, dim3(grid), dim3(kThreads), 0, s, blk, nb, n_sel);
         return hipGetLastError();
     }
+    // the rows behind the lists: the decode scan's layout, or launch_score_lists'
+    // (list w owns runs of 4 rows at stride 4 n_lists: row groups of one row)
+    const ListLayout lay = scan_rpw > 0 ? ListLayout{1, n_lists - 1, scan_rpw, (uint32_t)n_scan}
+                                        : ListLayout{0, n_lists, 1, (uint32_t)nb};
     hipLaunchKernelGGL(topk_lists_kernel, dim3(1), dim3(kSelThreads), 0, s, scores, nb, k, cl,
-                       n_lists, blk, n_sel);
+                       n_lists, lay, blk, n_sel);
     return hipGetLastError();
 }
 

@@ -308,6 +308,7 @@ int decode_impl(const char *fn, const qsa_config *cfg, const qsa_layer_bufs *Lb,
         st.part = at<float>(ws, L.part);
         st.out = out;
         st.blk_out = blk_out;
+        st.scan_rpw = scan_rows_per_group((int32_t)row);
         HIP_CHECK(launch_step_tail(st, s));
         return QSA_OK;
     }
@@ -316,7 +317,8 @@ int decode_impl(const char *fn, const qsa_config *cfg, const qsa_layer_bufs *Lb,
     const int32_t nsel = nb < k ? nb : k;
     const int32_t cells = kBlockTokens * nsel + N % kBlockTokens;
     int32_t *blk = blk_out ? blk_out : at<int32_t>(ws, L.blk);
-    HIP_CHECK(launch_topk_lists(scores, nb, k, cl, n_lists, blk, at<int32_t>(ws, L.nsel), s));
+    HIP_CHECK(launch_topk_lists(scores, nb, k, cl, n_lists, blk, at<int32_t>(ws, L.nsel), s,
+                                scan_rows_per_group((int32_t)row), ap.b_lo));
 
     // 4-5. compact gather, then attention over the compact rows
     AttnArgs a = attn_base(cfg);

@@ -75,6 +75,10 @@ hipError_t launch_score_decode(const h16 *q, int32_t n_q, const h16 *pool, int32
                                int32_t row_elems, float *scores, int32_t ld, const AppendArgs *ap,
                                const CandLists *cl, int32_t *n_lists, hipStream_t s,
                                KernelEvents ev = {});
+// The decode-step scan's list layout: list 0 is the append work group's; scan work
+// group b = list - 1 (of n_lists - 1) owns the runs of 4 consecutive row groups
+// 4 b + 4 (n_lists - 1) m .. + 3, a row group being this many consecutive rows.
+int32_t scan_rows_per_group(int32_t row_elems);
 hipError_t launch_score_prefill(const h16 *q, int32_t n_q, int32_t pos0, const h16 *pool,
                                 int32_t row_elems, float *scores, int32_t ld, hipStream_t s,
                                 KernelEvents ev = {});
@@ -91,8 +95,11 @@ hipError_t launch_score_lists(const float *scores, int32_t rows, int32_t ld, int
                               CandLists cl, int32_t *n_lists, hipStream_t s);
 // Top-k of one row from the scan's candidate lists (n_lists of them); selects
 // from the whole score row when the lists cannot be shown to hold the top-k.
+// scan_rpw: the lists come from the decode-step scan (scan_rows_per_group() of its
+// rows; they cover rows < n_scan); 0: from launch_score_lists (rows < nb).
 hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,
-                             int32_t n_lists, int32_t *blk, int32_t *n_sel, hipStream_t s);
+                             int32_t n_lists, int32_t *blk, int32_t *n_sel, hipStream_t s,
+                             int32_t scan_rpw = 0, int32_t n_scan = 0);
 hipError_t launch_topk_rows(const float *scores, int32_t n_q, int32_t ld, int32_t pos0,
                             int32_t k, int32_t *blk, int32_t *n_sel, hipStream_t s);
 int32_t topk_max_blocks();
@@ -162,6 +169,7 @@ struct StepTail {
     float *part;          // [rows][hq][splits][dv + 2]
     float *out;           // [rows][hq][dv]
     int32_t *blk_out;     // optional: [rows][k] chosen ids, ascending
+    int32_t scan_rpw;     // scan_rows_per_group() of the scan that wrote the lists
 };
 hipError_t launch_step_tail(const StepTail &st, hipStream_t s);
 

@@ -383,6 +383,7 @@ __device__ void select_row_global(const float *row, uint32_t nb, int32_t k, int3
 //      enough (returns false) and the caller selects from the whole score row.
 //      Otherwise every row outside the lists ranks below the smallest key of
 //      its own list, hence below R*, and the lists hold the top-k exactly.
+constexpr int kMaxWiden = 128;  // lists one widening may replace (k / 9 < 128 for k <= 1024)
 struct alignas(16) ListSelLds {
     alignas(16) uint32_t hist[2][kHistBins];
     uint64_t small[kSmallRank];
@@ -392,7 +393,11 @@ struct alignas(16) ListSelLds {
     alignas(16) uint32_t wkey[2][kSelThreads / kWave];
     uint64_t rstar;
     uint32_t hidden;
+    uint32_t widen[kMaxWiden];  // work groups whose rows replace their lists
 };
+
+// Outcome of lists_select_rest.
+enum ListSel : int { kListsExact = 0, kListsHide = 1, kListsShort = 2 };
 
 // The part of the selection before its first barrier: clears the histograms and
 // writes each wave's key range and largest full-list minimum.  All kSelThreads
@@ -434,9 +439,11 @@ __device__ void lists_prepare(const uint64_t (&R)[kListLen], uint32_t nrows, boo
 }
 
 // The rest of the selection, after lists_prepare and a barrier.  All kSelThreads
-// threads call it with the same R; on true, *rs = R*.  Leaves L.hist cleared.
-__device__ bool lists_select_rest(const uint64_t (&R)[kListLen], uint32_t k, ListSelLds &L,
-                                  uint64_t *rs)
+// threads call it with the same R.  Returns kListsExact (the lists hold the top-k;
+// *rs = R*), kListsHide (a full list may hide chosen rows; *rs = R* of the lists)
+// or kListsShort (fewer than k keys in the lists).  Leaves L.hist cleared.
+__device__ int lists_select_rest(const uint64_t (&R)[kListLen], uint32_t k, ListSelLds &L,
+                                 uint64_t *rs)
 {
     constexpr int NT = kSelThreads;
     const int t = threadIdx.x;
@@ -462,7 +469,7 @@ __device__ bool lists_select_rest(const uint64_t (&R)[kListLen], uint32_t k, Lis
     };
     uint32_t need = k, cnt = 0;
     if (hi_key < lo)  // no entry at all
-        return false;
+        return kListsShort;
     int p = 0;
     for (;;) {
         const int s = span >= (uint32_t)kHistBins ? 32 - __clz((int)span) - kHistBits : 0;
@@ -475,7 +482,7 @@ __device__ bool lists_select_rest(const uint64_t (&R)[kListLen], uint32_t k, Lis
         find_from_top_wg<NT>(h, need, S, L.wtot);
         const uint32_t d = S.res[0];
         if (d == 0xffffffffu)  // fewer than k keys in the lists
-            return false;
+            return kListsShort;
         need -= S.res[1];
         cnt = S.res[3];
         // nobody reads h again in this pass; the next pass uses the other one
@@ -540,16 +547,99 @@ __device__ bool lists_select_rest(const uint64_t (&R)[kListLen], uint32_t k, Lis
     }
     __syncthreads();
     *rs = L.rstar;
-    return L.hidden == 0u;
+    return L.hidden == 0u ? kListsExact : kListsHide;
 }
 
 // The whole selection: lists_prepare, a barrier, lists_select_rest.
-__device__ bool lists_select(const uint64_t (&R)[kListLen], uint32_t nrows, bool has_list,
-                             uint32_t k, ListSelLds &L, uint64_t *rs)
+__device__ int lists_select(const uint64_t (&R)[kListLen], uint32_t nrows, bool has_list,
+                            uint32_t k, ListSelLds &L, uint64_t *rs)
 {
     lists_prepare(R, nrows, has_list, L);
     __syncthreads();
     return lists_select_rest(R, k, L, rs);
+}
+
+// The rows behind a set of candidate lists: list li >= base was written by the
+// work group b = li - base, which owns the rows r < n_rows whose group g = r / rpw
+// lies in its runs of 4 groups, 4 b + 4 nwg m .. 4 b + 4 nwg m + 3 (m = 0, 1, ...);
+// lists below base own no such rows (the decode scan's list 0 is its append's).
+struct ListLayout {
+    int32_t base;
+    int32_t nwg;
+    int32_t rpw;
+    uint32_t n_rows;
+};
+
+// Targeted fallback, after lists_select_rest returned kListsHide with rs = R* of
+// the lists: every full list whose smallest key is >= R* is dropped, and all rows
+// of its work group (their scores re-read from the score row) go to the threads
+// past the W lists, kListLen rows each, as lists that hide nothing.  The top-k of
+// the widened set is the true top-k: adding candidates cannot lower the k-th key,
+// so a list that hid nothing before (not full, or its smallest key below R*) hides
+// nothing after, and the dropped lists' work groups are now complete.  Returns
+// false, leaving R as it was, when those rows do not fit the spare threads (the
+// caller then selects from the whole score row).  All kSelThreads threads call it;
+// lists_prepare (after a barrier) and lists_select_rest then run on the new R.
+__device__ bool widen_lists(uint64_t (&R)[kListLen], uint32_t *nrows, int32_t W, uint64_t rs,
+                            const float *scores, const ListLayout &lay, ListSelLds &L)
+{
+    constexpr int NT = kSelThreads;
+    const int t = threadIdx.x;
+    Scratch<NT> &S = L.S;
+    if (lay.nwg < 1 || lay.rpw < 1 || lay.n_rows == 0u)
+        return false;
+    // rows of one work group at most, and the threads that take them
+    const uint32_t rpw = (uint32_t)lay.rpw, nwg = (uint32_t)lay.nwg;
+    const uint32_t groups = (lay.n_rows + rpw - 1u) / rpw;
+    const uint32_t per = 4u * ((groups + 4u * nwg - 1u) / (4u * nwg)) * rpw;
+    const uint32_t P = (per + kListLen - 1u) / kListLen;
+    uint64_t mn = ~0ull;
+#pragma unroll
+    for (int j = 0; j < kListLen; j++)
+        mn = R[j] < mn ? R[j] : mn;
+    const bool hides = t < W && t >= lay.base && *nrows > (uint32_t)kListLen && mn >= rs;
+    // the dropped lists in list order (a prefix sum, not atomics: every work group
+    // that runs this selection must hand the same rows to the same threads, since
+    // the chosen blocks are placed in thread order)
+    const uint32_t o = wg_exclusive_scan<NT>(hides ? 1u : 0u, S);
+    if (t == NT - 1)
+        S.cnt = o + (hides ? 1u : 0u);
+    if (hides && o < (uint32_t)kMaxWiden)
+        L.widen[o] = (uint32_t)(t - lay.base);
+    __syncthreads();
+    const uint32_t n_off = S.cnt;
+    if (n_off == 0u || n_off > (uint32_t)kMaxWiden || W > NT ||
+        (uint64_t)n_off * P > (uint64_t)(NT - W))
+        return false;  // the same on every thread
+    if (hides) {
+#pragma unroll
+        for (int j = 0; j < kListLen; j++)
+            R[j] = 0ull;
+        *nrows = 0u;
+    }
+    const int sp = t - W;
+    if (sp >= 0 && (uint32_t)sp < n_off * P) {
+        const uint32_t b = L.widen[(uint32_t)sp / P], part = (uint32_t)sp % P;
+        uint32_t r[kListLen];
+        float v[kListLen];
+#pragma unroll
+        for (int e = 0; e < kListLen; e++) {
+            const uint32_t j = part * kListLen + (uint32_t)e;  // the work group's j-th row
+            const uint32_t jg = j / rpw;
+            const uint32_t g = 4u * b + (jg & 3u) + 4u * nwg * (jg >> 2);
+            r[e] = j < per ? g * rpw + j % rpw : 0xffffffffu;
+            v[e] = scores[r[e] < lay.n_rows ? r[e] : lay.n_rows - 1u];  // all loads in flight
+        }
+        uint32_t n = 0;
+#pragma unroll
+        for (int e = 0; e < kListLen; e++) {
+            const bool on = r[e] < lay.n_rows;
+            R[e] = on ? rank_key(v[e], r[e]) : 0ull;
+            n += on ? 1u : 0u;
+        }
+        *nrows = n;
+    }
+    return true;
 }
 
 // Issues the loads of list min(t, W - 1) and its row count (W >= 1): no branch,

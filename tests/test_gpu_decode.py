@@ -520,6 +520,75 @@ def test_decode_step_clustered_scores(gpu, pattern):
     assert_attn_close(host(out), ref_out)
 
 
+def scan_share_rows(b, nb, nwg, rpw):
+    """Rows of the decode scan's work group b (of nwg): runs of 4 row groups of rpw
+    rows at stride 4 nwg groups, in scan order."""
+    g = np.arange((nb + rpw - 1) // rpw)
+    rows = np.concatenate([np.arange(x * rpw, (x + 1) * rpw) for x in g if (x % (4 * nwg)) // 4 == b])
+    return rows[rows < nb]
+
+
+@pytest.mark.parametrize("H,d,nb0,n_groups,per_group", [
+    (16, 128, 20000, 1, 28),     # one work group's 26 rows all on top: its list is widened
+    (16, 128, 20000, 40, 12),    # 40 lists widened at once (160 spare threads)
+    (4, 64, 20000, 3, 20),       # row groups of 2 rows (a 4 x 64 indexer)
+    (4, 64, 200000, 20, 20),     # 20 work groups of 264 rows do not fit: whole-row selection
+])
+def test_decode_step_hidden_rows(gpu, H, d, nb0, n_groups, per_group):
+    # the top of the score row crowds the shares of n_groups scan work groups (more
+    # than 8 chosen rows each), so their 8-entry lists hide chosen rows: the tail
+    # replaces those lists by all their rows, or selects from the whole score row
+    # when the rows do not fit; the chosen ids equal the top-k of the GPU's scores
+    n_before = 4 * nb0 + 3  # the step completes block nb0
+    w = small(n_before + 1, h_idx=H, d_idx=d, hq=8, hkv=1, d=64, dv=64)
+    cfg = cfg_of(w)
+    r = np.random.default_rng(nb0 + n_groups)
+    v = (np.round(r.standard_normal(nb0) * 6.4) / 64).astype(np.float16)
+    # the scan's layout: row groups of rpw rows (one wave-wide load per group), one
+    # work group per 8 row groups, at most 767
+    rpw = 64 // min(64, H * d // 8)
+    nwg = min(767, -(-(-(-nb0 // rpw)) // 8))
+    hi = []
+    for b in r.choice(nwg, n_groups, replace=False):
+        rows = scan_share_rows(int(b), nb0, nwg, rpw)
+        assert rows.size > 8
+        hi.extend(rows[:per_group].tolist())
+    hi = np.array(hi)
+    v[hi] = (4.0 + np.arange(hi.size) / 64).astype(np.float16)
+    pooled = np.zeros((w.cap_tokens // 4, H, d), np.float16)
+    pooled[:nb0] = v[:, None, None]
+    raw = np.zeros((w.cap_tokens, H, d), np.float16)
+    raw[4 * nb0:n_before] = synth.normal_f16(80, (3, H, d))
+    K = synth.normal_f16(81, (w.cap_tokens, 1, 64))
+    V = synth.normal_f16(82, (w.cap_tokens, 1, 64))
+    K[n_before:] = 0
+    V[n_before:] = 0
+    q_idx = np.ones((H, d), np.float16)
+    q = synth.normal_f16(83, (8, 64))
+    k_idx_new = synth.normal_f16(84, (H, d))
+    k_new, v_new = synth.normal_f16(85, (1, 64)), synth.normal_f16(86, (1, 64))
+
+    g = qb.Layer(cfg)
+    g.k_pool.copy_(dev(pooled))
+    g.k_raw.copy_(dev(raw))
+    g.k_cache.copy_(dev(K))
+    g.v_cache.copy_(dev(V))
+    out = torch.empty((8, 64), device="cuda")
+    scores = torch.empty(nb0 + 1, device="cuda")
+    blk = torch.full((512,), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, 1, w.cap_tokens)
+    for flags in (qb.QSA_STEP_FUSED_GATHER, qb.QSA_STEP_COMPACT_GATHER):
+        qb.qsa_decode_step(cfg, g, n_before, dev(q_idx), dev(k_idx_new), dev(q), dev(k_new),
+                           dev(v_new), out, ws, scores_out=scores, blk_out=blk, flags=flags)
+        s_gpu = host(scores)
+        assert np.array_equal(s_gpu[:nb0], float(H * d) * v.astype(np.float32))
+        b_gpu = host(blk)
+        assert np.array_equal(b_gpu, O.topk_sort(s_gpu, 512)), flags
+        assert set(hi.tolist()) <= set(b_gpu.tolist())
+        ref_out = O.attn_cells(q, K, V, O.cells(b_gpu, n_before + 1), w.scale)
+        assert_attn_close(host(out), ref_out, f"flags {flags}")
+
+
 @pytest.mark.parametrize("pattern", ["one_scan_group", "recent_window", "all_equal",
                                      "few_values"])
 def test_decode_multi_clustered_scores(gpu, pattern):
