@@ -8,28 +8,30 @@
 //
 // Tiling: a work group computes a 256 (queries) x 256 (blocks) tile; its 8
 // waves each own 128 x 64 (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).
-// Every 32-feature step stages A (16 KiB) and B (16 KiB) in LDS with rows padded
-// to 80 bytes (conflict-free 16-byte fragment reads).  Two LDS buffers and four
-// register sets: while step s is multiplied, step s + 1 waits in registers to be
-// stored into the other buffer and the global loads of steps s + 2 .. s + 4 are
-// in flight, and a step needs one barrier.  Every load is issued unconditionally
-// (indexes clamped into the operands), so the compiler waits only for the oldest
-// register set: a load under a branch made it wait for all of them, which left one
-// step of work to cover a load.  Blocks at or past the last row's causal bound are
-// never written.
+// Every 64-feature step stages A (32 KiB) and B (32 KiB) in LDS with rows padded
+// to 144 bytes (conflict-free 16-byte fragment reads); 8 threads copy one row's 128
+// bytes, so each step fetches whole 128-byte lines (32-feature steps fetched half a
+// line per step and the other half one step later, 6% slower).  Two LDS buffers and
+// two register sets: while step s is multiplied (two MFMA substeps of 32 features),
+// step s + 1 waits in registers to be stored into the other buffer and the global
+// loads of step s + 2 are in flight, and a step needs one barrier.  Every load is
+// issued unconditionally (indexes clamped into the operands), so the compiler waits
+// only for the oldest register set: a load under a branch made it wait for all of
+// them.  Blocks at or past the last row's causal bound are never written.
 //
 // On this shape (1,024 queries x 31,819 blocks x 2,048 features) the kernel is
-// bound by LDS traffic, not by the matrix cores: a step moves 32 KiB into LDS and
-// 96 KiB out of it per CU, which at 128 bytes per clock takes as long as the
-// step's MFMA work; the score tile's fp32 stores (130 MB per chunk) add the rest.
+// bound by its LDS reads, not by the matrix cores: a step reads 192 KiB out of LDS
+// per CU, which at 128 bytes per clock takes three quarters of the step's MFMA time
+// and overlaps it only in part (every wave reads its fragments right after the
+// barrier); the score tile's fp32 stores (130 MB per chunk) add the rest.
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int TM = 256, TN = 256, TK = 32;
-constexpr int PITCH = TK + 8;  // halfs per LDS row (80 bytes)
+constexpr int TM = 256, TN = 256, TK = 64;
+constexpr int PITCH = TK + 8;  // halfs per LDS row (144 bytes)
 constexpr int WM = 128, WN = 64;
 constexpr int FI = WM / 16, FJ = WN / 16;
 
@@ -39,7 +41,7 @@ constexpr int FI = WM / 16, FJ = WN / 16;
 // block-column tile, c = 8 * (j / nrow) + (i mod 8) with j = i / 8: those tiles run
 // side by side on one L2, which then fetches the column's pooled rows once.
 constexpr int kXcds = 8;
-constexpr int NS = 4;  // register sets: a step's loads are issued NS steps ahead
+constexpr int NS = 2;  // register sets: a step's loads are issued NS steps ahead
 
 __global__ __launch_bounds__(kThreads, 1) void score_prefill_kernel(const h16 *__restrict__ Q,
                                                                  int32_t n_q, int32_t pos0,
@@ -61,34 +63,37 @@ __global__ __launch_bounds__(kThreads, 1) void score_prefill_kernel(const h16 *_
     const int32_t c0 = col * TN;
     const int32_t nb_max = (pos0 + n_q) / kBlockTokens;
 
-    // global -> register staging: A: 2 x 16B per thread, B: 2 x 16B per thread.
-    // Rows past the last query / last block are clamped to it (their products are
-    // never stored) and feature offsets past the end to the last step (the loads
-    // issued ahead of the last steps are never used).
-    const int lr = t >> 2, lk = (t & 3) * 8;
-    const h16 *qa[2], *pb[2];
+    // global -> register staging: each operand's 256 rows x 128 bytes as 4 x 16 bytes
+    // per thread, 8 threads per row.  Rows past the last query / last block are
+    // clamped to it (their products are never stored) and feature offsets past the
+    // end to the last step (the loads issued ahead of the last steps are never used).
+    constexpr int TPR = TK / 8;          // threads per row
+    constexpr int RPP = kThreads / TPR;  // rows per pass
+    constexpr int LPO = TM / RPP;        // loads per operand per thread
+    const int lr = t / TPR, lk = (t % TPR) * 8;
+    const h16 *qa[LPO], *pb[LPO];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        qa[i] = Q + (int64_t)min(r0 + lr + 128 * i, n_q - 1) * K + lk;
-        pb[i] = P + (int64_t)min(c0 + lr + 128 * i, nb_max - 1) * K + lk;
+    for (int i = 0; i < LPO; i++) {
+        qa[i] = Q + (int64_t)min(r0 + lr + RPP * i, n_q - 1) * K + lk;
+        pb[i] = P + (int64_t)min(c0 + lr + RPP * i, nb_max - 1) * K + lk;
     }
-    h16x8 ga[NS][2], gb[NS][2];
+    h16x8 ga[NS][LPO], gb[NS][LPO];
     auto gload = [&](int u, int k0) {
         k0 = min(k0, K - TK);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < LPO; i++)
             ga[u][i] = *(const h16x8 *)(qa[i] + k0);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < LPO; i++)
             gb[u][i] = *(const h16x8 *)(pb[i] + k0);
     };
     auto sstore = [&](int u, h16 *as, h16 *bs) {
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-            *(h16x8 *)&as[(lr + 128 * i) * PITCH + lk] = ga[u][i];
+        for (int i = 0; i < LPO; i++)
+            *(h16x8 *)&as[(lr + RPP * i) * PITCH + lk] = ga[u][i];
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-            *(h16x8 *)&bs[(lr + 128 * i) * PITCH + lk] = gb[u][i];
+        for (int i = 0; i < LPO; i++)
+            *(h16x8 *)&bs[(lr + RPP * i) * PITCH + lk] = gb[u][i];
     };
 
     f32x4 acc[FI][FJ];
@@ -100,16 +105,19 @@ __global__ __launch_bounds__(kThreads, 1) void score_prefill_kernel(const h16 *_
 
     const int fr = lane & 15, fk = (lane >> 4) * 8;
     auto mma = [&](const h16 *as, const h16 *bs) {
-        h16x8 b[FJ];
 #pragma unroll
-        for (int jj = 0; jj < FJ; jj++)
-            b[jj] = *(const h16x8 *)&bs[(wn * WN + jj * 16 + fr) * PITCH + fk];
-#pragma unroll
-        for (int i = 0; i < FI; i++) {
-            const h16x8 a = *(const h16x8 *)&as[(wm * WM + i * 16 + fr) * PITCH + fk];
+        for (int kk = 0; kk < TK; kk += 32) {
+            h16x8 b[FJ];
 #pragma unroll
             for (int jj = 0; jj < FJ; jj++)
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[jj], acc[i][jj], 0, 0, 0);
+                b[jj] = *(const h16x8 *)&bs[(wn * WN + jj * 16 + fr) * PITCH + kk + fk];
+#pragma unroll
+            for (int i = 0; i < FI; i++) {
+                const h16x8 a = *(const h16x8 *)&as[(wm * WM + i * 16 + fr) * PITCH + kk + fk];
+#pragma unroll
+                for (int jj = 0; jj < FJ; jj++)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[jj], acc[i][jj], 0, 0, 0);
+            }
         }
     };
 
