@@ -29,8 +29,13 @@ constexpr int kThreads = 256;
 constexpr int kRegThreads = 1024;
 constexpr int kListCap = 4096;  // keys in bins >= the lower bound, kept in LDS
 
+// Two work groups per CU (8 waves per SIMD, at most 64 registers, a few spilled
+// outside the key loops): one work group's row loads overlap the other's histogram
+// and ranking passes.  At one work group per CU (79-103 registers) the 1,024 rows
+// of a chunk took 42 / 66 / 105 us at 15,000 / 31,800 / 62,800 blocks per row,
+// against 31 / 48 / 84 us.
 template <int KPT>
-__global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__restrict__ scores,
+__global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_reg_kernel(const float *__restrict__ scores,
                                                                int32_t ld, int32_t pos0,
                                                                int32_t k, int32_t *__restrict__ blk,
                                                                int32_t *__restrict__ n_sel)
