@@ -6,7 +6,8 @@
 //
 // Grid: (split, KV head, query row), 1024 threads.  Every work group first selects the
 // same top-k blocks from the decode scan's candidate lists (lists_select; the
-// whole score row if the lists are not enough), in the deterministic order of
+// lists that may hide chosen rows are widened with their work groups' rows, and
+// the whole score row is the last resort), in the deterministic order of
 // the selection (attention does not depend on the order of its cells); the
 // threads holding the chosen blocks of this work group's split write its 64
 // cell tokens to LDS.  Then all 16 waves attend those 64 cells for one KV head:

@@ -93,8 +93,9 @@ hipError_t launch_topk_decode(const float *scores, int32_t nb, int32_t k, int32_
 // cl.list + r * kListWgs * kListLen; *n_lists gets the lists per row.
 hipError_t launch_score_lists(const float *scores, int32_t rows, int32_t ld, int32_t pos0,
                               CandLists cl, int32_t *n_lists, hipStream_t s);
-// Top-k of one row from the scan's candidate lists (n_lists of them); selects
-// from the whole score row when the lists cannot be shown to hold the top-k.
+// Top-k of one row from the scan's candidate lists (n_lists of them); when the
+// lists cannot be shown to hold the top-k, the lists that may hide chosen rows are
+// widened with their work groups' rows, else it selects from the whole score row.
 // scan_rpw: the lists come from the decode-step scan (scan_rows_per_group() of its
 // rows; they cover rows < n_scan); 0: from launch_score_lists (rows < nb).
 hipError_t launch_topk_lists(const float *scores, int32_t nb, int32_t k, CandLists cl,

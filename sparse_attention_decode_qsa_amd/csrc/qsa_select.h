@@ -380,10 +380,14 @@ __device__ void select_row_global(const float *row, uint32_t nb, int32_t k, int3
 //   2. a full list (its work group scored more than kListLen rows) whose
 //      smallest key is >= R* may hide chosen rows of that work group (checked
 //      on the per-wave maxima of those smallest keys); then the lists are not
-//      enough (returns false) and the caller selects from the whole score row.
-//      Otherwise every row outside the lists ranks below the smallest key of
-//      its own list, hence below R*, and the lists hold the top-k exactly.
-constexpr int kMaxWiden = 128;  // lists one widening may replace (k / 9 < 128 for k <= 1024)
+//      enough (kListsHide): the caller widens those lists with their work
+//      groups' rows (widen_lists) and selects again, or, when the rows do not
+//      fit, selects from the whole score row.  Otherwise every row outside the
+//      lists ranks below the smallest key of its own list, hence below R*, and
+//      the lists hold the top-k exactly.
+// A list that may hide rows holds kListLen keys >= R*, and only k keys are, so at
+// most k / kListLen lists need widening: 128 at k = 1024.
+constexpr int kMaxWiden = 128;
 struct alignas(16) ListSelLds {
     alignas(16) uint32_t hist[2][kHistBins];
     uint64_t small[kSmallRank];
