@@ -528,17 +528,23 @@ def scan_share_rows(b, nb, nwg, rpw):
     return rows[rows < nb]
 
 
-@pytest.mark.parametrize("H,d,nb0,n_groups,per_group", [
-    (16, 128, 20000, 1, 28),     # one work group's 26 rows all on top: its list is widened
-    (16, 128, 20000, 40, 12),    # 40 lists widened at once (160 spare threads)
-    (4, 64, 20000, 3, 20),       # row groups of 2 rows (a 4 x 64 indexer)
-    (4, 64, 200000, 20, 20),     # 20 work groups of 264 rows do not fit: whole-row selection
+@pytest.mark.parametrize("H,d,nb0,n_groups,per_group,edges", [
+    (16, 128, 20000, 1, 28, False),    # one work group's 26 rows all on top: widened
+    (16, 128, 20000, 40, 12, False),   # 40 lists widened at once (160 spare threads)
+    (4, 64, 20000, 3, 20, False),      # row groups of 2 rows (a 4 x 64 indexer)
+    (2, 64, 20000, 5, 30, False),      # row groups of 4 rows (a 2 x 64 indexer)
+    (2, 64, 20001, 4, 30, True),       # the first and last work groups; a partial last group
+    (32, 128, 20000, 3, 24, False),    # rows of 512 16-byte pieces (a 32 x 128 indexer)
+    (4, 64, 200000, 20, 20, False),    # 20 work groups of 264 rows do not fit: whole-row selection
 ])
-def test_decode_step_hidden_rows(gpu, H, d, nb0, n_groups, per_group):
+def test_decode_step_hidden_rows(gpu, H, d, nb0, n_groups, per_group, edges):
     # the top of the score row crowds the shares of n_groups scan work groups (more
     # than 8 chosen rows each), so their 8-entry lists hide chosen rows: the tail
     # replaces those lists by all their rows, or selects from the whole score row
-    # when the rows do not fit; the chosen ids equal the top-k of the GPU's scores
+    # when the rows do not fit; the chosen ids equal the top-k of the GPU's scores.
+    # edges: the chosen work groups include the first and the last two (whose
+    # second run ends in the partial last row group when nb0 is not a multiple of
+    # the group size)
     n_before = 4 * nb0 + 3  # the step completes block nb0
     w = small(n_before + 1, h_idx=H, d_idx=d, hq=8, hkv=1, d=64, dv=64)
     cfg = cfg_of(w)
@@ -549,7 +555,13 @@ def test_decode_step_hidden_rows(gpu, H, d, nb0, n_groups, per_group):
     rpw = 64 // min(64, H * d // 8)
     nwg = min(767, -(-(-(-nb0 // rpw)) // 8))
     hi = []
-    for b in r.choice(nwg, n_groups, replace=False):
+    if edges:
+        groups = [0, nwg - 1, nwg - 2] + r.choice(np.arange(1, nwg - 2), n_groups - 3,
+                                                  replace=False).tolist()
+        assert nb0 - 1 in scan_share_rows(nwg - 2, nb0, nwg, rpw)  # the partial group
+    else:
+        groups = r.choice(nwg, n_groups, replace=False).tolist()
+    for b in groups:
         rows = scan_share_rows(int(b), nb0, nwg, rpw)
         assert rows.size > 8
         hi.extend(rows[:per_group].tolist())
