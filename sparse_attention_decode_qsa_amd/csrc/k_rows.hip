@@ -174,11 +174,11 @@ rows_attn_kernel(RowsArgs a)
     __syncthreads();
 
     // Few loads in flight: a gather from the caches keeps ~0.5 us latency only while
-    // a CU has about 32 KiB of loads outstanding (4 waves per SIMD x 2 pieces of
-    // 1 KiB per wave); with more in flight the latency grows faster than the bytes
-    // and the rate falls to about half.  So each step below issues two 16-byte
-    // pieces per lane and uses them before the next step's loads go out (the
-    // compiler barriers keep it from hoisting loads across steps).
+    // a CU has about 32-64 KiB of loads outstanding (4 waves per SIMD x 2-4 pieces
+    // of 1 KiB per wave); with more in flight the latency grows faster than the
+    // bytes and the rate falls to about half.  So each step below issues two to four
+    // 16-byte pieces per lane and uses them before the next step's loads go out
+    // (the compiler barriers keep it from hoisting loads across steps).
     auto fence = [] {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
@@ -187,21 +187,29 @@ rows_attn_kernel(RowsArgs a)
     for (int32_t tile = wave; tile < ntile; tile += kRWaves) {
         const int32_t c0 = tile * kRTile;
         // S^T = K Q^T over 4 k-steps; step kk reads dims 32 kk + 8 j4 of cells
-        // c0 + n and c0 + 16 + n (the A rows of the two cell halves)
+        // c0 + n and c0 + 16 + n (the A rows of the two cell halves).  Steps go out
+        // in pairs: steps 2p and 2p + 1 read bytes 128p .. 128p + 127 of each K row,
+        // one whole line per round trip (a line read in two halves a step apart took
+        // 2-4% longer; all four steps at once, 6% longer)
         uint32_t koff[2];
 #pragma unroll
         for (int tt = 0; tt < 2; tt++)
             koff[tt] = sm.coff[c0 + 16 * tt + n] + 16u * j4;
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            h16x8 kf[2];
+        for (int kp = 0; kp < 2; kp++) {
+            h16x8 kf[2][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; tt++)
-                kf[tt] = piece(kg + 64 * kk, koff[tt]);
+            for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
-            for (int tt = 0; tt < 2; tt++)
-                sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[tt], qf[kk], sacc[tt], 0, 0, 0);
+                for (int tt = 0; tt < 2; tt++)
+                    kf[k2][tt] = piece(kg + 64 * (2 * kp + k2), koff[tt]);
+#pragma unroll
+            for (int k2 = 0; k2 < 2; k2++)
+#pragma unroll
+                for (int tt = 0; tt < 2; tt++)
+                    sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[k2][tt], qf[2 * kp + k2],
+                                                                      sacc[tt], 0, 0, 0);
             fence();
         }
 
