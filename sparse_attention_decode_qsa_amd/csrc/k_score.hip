@@ -77,6 +77,71 @@ __device__ __forceinline__ uint64_t lane_list_insert(uint64_t v, uint64_t x, int
     return x > v ? (x > above ? above : x) : v;
 }
 
+// A 64-bit value moved across lanes by a DPP pattern (both halves).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+constexpr int kDppRowRor4 = 0x124;   // lane i takes lane i - 4 of its row
+constexpr int kDppRowRor12 = 0x12C;  // lane i takes lane i + 4 of its row
+constexpr int kDppRowMirrorC = 0x140;
+constexpr int kDppRowHalfMirrorC = 0x141;
+constexpr int kDppQuadXor1C = 0xb1, kDppQuadXor2C = 0x4e;
+
+// The value of lane l ^ 16 (l ^ 32): the 16- (32-) lane swaps return, in every lane,
+// its own value and its partner's; which is which depends on the lane's row (half).
+__device__ __forceinline__ uint64_t lane_xor16_u64(uint64_t v, int lane)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    const auto b =
+        __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    const bool odd_row = (lane & 16) != 0;
+    return ((uint64_t)(odd_row ? b[0] : b[1]) << 32) | (odd_row ? a[0] : a[1]);
+}
+__device__ __forceinline__ uint64_t lane_xor32_u64(uint64_t v, int lane)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    const auto b =
+        __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    const bool upper = (lane & 32) != 0;
+    return ((uint64_t)(upper ? b[0] : b[1]) << 32) | (upper ? a[0] : a[1]);
+}
+
+// Sorts each 8-lane group of a bitonic sequence into descending order (compare-
+// exchange at distances 4, 2, 1; the lower lane of a pair keeps the larger key).
+__device__ __forceinline__ uint64_t bitonic8_desc(uint64_t e, int lane)
+{
+    const uint64_t dn = dpp_u64<kDppRowRor4>(e), up = dpp_u64<kDppRowRor12>(e);
+    uint64_t p = (lane & 4) ? dn : up;
+    e = ((lane & 4) == 0) == (e > p) ? e : p;
+    p = dpp_u64<kDppQuadXor2C>(e);
+    e = ((lane & 2) == 0) == (e > p) ? e : p;
+    p = dpp_u64<kDppQuadXor1C>(e);
+    e = ((lane & 1) == 0) == (e > p) ? e : p;
+    return e;
+}
+
+// The 8 largest of 64 keys held one per lane, each 8-lane group sorted descending:
+// three rounds of merging two sorted groups (each key against its partner group's
+// key in mirrored position keeps the 8 largest of the two, as a bitonic sequence),
+// the first two followed by a bitonic sort.  Lanes 0-7 end with the 8 largest, in
+// no particular order.  All 64 lanes take part.
+__device__ __forceinline__ uint64_t top8_of_64(uint64_t e, int lane)
+{
+    uint64_t p = dpp_u64<kDppRowMirrorC>(e);  // the other group of the row, reversed
+    e = e > p ? e : p;
+    e = bitonic8_desc(e, lane);
+    p = dpp_u64<kDppRowHalfMirrorC>(lane_xor16_u64(e, lane));  // the paired row's, reversed
+    e = e > p ? e : p;
+    e = bitonic8_desc(e, lane);
+    p = dpp_u64<kDppRowHalfMirrorC>(lane_xor32_u64(e, lane));  // the other half's, reversed
+    return e > p ? e : p;
+}
+
 // NQ queries (rows of q, ROWC 16-byte chunks each) score every row read once;
 // query i's scores go to scores[i * ld + b].  APPEND: work group 0 runs the
 // append.  LISTS: candidate lists in the epilogue, one per query row (row i's at
@@ -231,43 +296,20 @@ __global__ __launch_bounds__(NT) void score_decode_kernel(const h16 *__restrict_
         prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
         if (prev == NW - 1) {
             // per query row, the kListLen largest of the NW * kListLen entries, one
-            // per lane: each lane counts the entries that outrank its own (LDS
-            // broadcast reads; keys are distinct, empty entries are 0), so the
-            // kListLen best have ranks 0 .. kListLen - 1 and take those slots
+            // per lane (each wave's list sorted, descending), by a merge network in
+            // registers
             constexpr int NE = NW * kListLen;
             static_assert(!LISTS || NE == kWave, "one entry per lane");
             uint32_t n = 0;
 #pragma unroll
             for (int w = 0; w < NW; w++)
                 n += wrows[w];
-            uint64_t mine[NQ];
-            uint32_t rk[NQ];
 #pragma unroll
             for (int qi = 0; qi < NQ; qi++) {
-                mine[qi] = wtop[qi][lane];
-                rk[qi] = 0;
-            }
-            // the query rows' counts in one pass, so their LDS reads overlap
-#pragma unroll 4
-            for (int j = 0; j < NE; j += 2) {
-#pragma unroll
-                for (int qi = 0; qi < NQ; qi++) {
-                    const uint64_t a0 = wtop[qi][j], a1 = wtop[qi][j + 1];
-                    rk[qi] += (a0 > mine[qi] ? 1u : 0u) + (a1 > mine[qi] ? 1u : 0u);
-                }
-            }
-#pragma unroll
-            for (int qi = 0; qi < NQ; qi++) {
-                const uint64_t me = mine[qi];
-                const uint32_t rank = rk[qi];
-                const bool pick = me != 0ull && rank < (uint32_t)kListLen;
-                const uint32_t npick = (uint32_t)__popcll(__ballot(pick));
+                const uint64_t best = top8_of_64(wtop[qi][lane], lane);
                 const int64_t li = (int64_t)qi * kListWgs + blockIdx.x;
-                uint64_t *dst = cl.list + li * kListLen;
-                if (pick)
-                    dst[rank] = me;
-                if ((uint32_t)lane >= npick && lane < kListLen)
-                    dst[lane] = 0ull;
+                if (lane < kListLen)
+                    cl.list[li * kListLen + lane] = best;
                 if (lane == 0)
                     cl.rows[li] = n;
             }
