@@ -112,10 +112,12 @@ def test_topk_rows_bit_exact(gpu, kind):
         assert np.array_equal(b[i, :ns[i]], O.topk_sort(S[i, :nb], k)), i
 
 
-@pytest.mark.parametrize("n_q,pos0", [(24, 127253), (6, 262150), (5, 300001)])
+@pytest.mark.parametrize("n_q,pos0", [(24, 127253), (8, 200000), (4, 262140), (6, 262150),
+                                     (5, 300001)])
 def test_topk_rows_large_rows(gpu, n_q, pos0):
-    # rows of the 128k prefill size (~31.8k blocks each), and rows past the
-    # register-resident limit of 65,536 blocks
+    # rows of the 128k prefill size (~31.8k blocks each), of 50,000 blocks and up to
+    # exactly 65,536 (the register-resident form's largest rows, 64 keys a thread),
+    # and rows past that limit
     k = 512
     cfg = qb.Config(topk_blocks=k, cap_tokens=(pos0 + n_q + 64) // 4 * 4)
     nb_max = (pos0 + n_q) // 4
