@@ -679,8 +679,8 @@ def main():
                          "calibration kernel of known size for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("this build runs on one GPU only: the QSA layer step has no multi-GPU path here "
-              "(see the sharding notes); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the QSA layer step has no multi-GPU path "
+              "(its sharding is a design note); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.calib_copy_mib:
         import torch
