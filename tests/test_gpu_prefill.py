@@ -67,7 +67,10 @@ def run_prefill_scores(H, d, n_q, pos0, seed, rows_to_check):
 
 
 @pytest.mark.parametrize("H,d,n_q,pos0", [(16, 128, 300, 1000), (16, 128, 257, 3), (4, 64, 100, 999),
-                                          (8, 128, 1, 5000), (16, 128, 1024, 7)])
+                                          (8, 128, 1, 5000), (16, 128, 1024, 7),
+                                          # 128 features (two 64-feature steps), 1,024, 4,096
+                                          (2, 64, 70, 500), (1, 128, 130, 300), (8, 128, 2, 5000),
+                                          (32, 128, 64, 2000)])
 def test_index_score_prefill_mfma(gpu, H, d, n_q, pos0):
     if n_q == 1:
         pytest.skip("n_q == 1 is the decode kernel")
