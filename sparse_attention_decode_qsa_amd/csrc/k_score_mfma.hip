@@ -9,7 +9,7 @@
 // Tiling: a work group computes a 256 (queries) x 256 (blocks) tile; its 8
 // waves each own 128 x 64 (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).
 // Every 64-feature step stages A (32 KiB) and B (32 KiB) in LDS with rows padded
-// to 144 bytes (conflict-free 16-byte fragment reads); 8 threads copy one row's 128
+// to 144 bytes (16-byte fragment reads); 8 threads copy one row's 128
 // bytes, so each step fetches whole 128-byte lines (32-feature steps fetched half a
 // line per step and the other half one step later, 6% slower).  Two LDS buffers and
 // two register sets: while step s is multiplied (two MFMA substeps of 32 features),
@@ -19,11 +19,13 @@
 // only for the oldest register set: a load under a branch made it wait for all of
 // them.  Blocks at or past the last row's causal bound are never written.
 //
-// On this shape (1,024 queries x 31,819 blocks x 2,048 features) the kernel is
-// bound by its LDS reads, not by the matrix cores: a step reads 192 KiB out of LDS
-// per CU, which at 128 bytes per clock takes three quarters of the step's MFMA time
-// and overlaps it only in part (every wave reads its fragments right after the
-// barrier); the score tile's fp32 stores (130 MB per chunk) add the rest.
+// On this shape (1,024 queries x 31,819 blocks x 2,048 features) the matrix cores
+// are busy about 43% of the kernel's time.  What holds them back is the staging of
+// the operands, not the fragment reads: at this pitch the reads run into two-way
+// bank conflicts (128 bytes per clock per CU), yet a 160-byte pitch that removes
+// every conflict (and a third of the LDS's busy cycles) left the time unchanged,
+// while the same loop with the steps' global loads and LDS stores taken out ran
+// in about 0.8 of it; the score tile's fp32 stores (130 MB per chunk) add ~10%.
 #include "qsa_internal.h"
 
 namespace qsa {
