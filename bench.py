@@ -676,7 +676,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (a counter "
-                         "calibration kernel of known size for rocprofv3 --pmc runs)")
+                         "calibration kernel of known size for rocprofv3 --pmc runs), then a "
+                         "fill and a sum of the same size (cross-checks)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the QSA layer step has no multi-GPU path "
@@ -689,8 +690,14 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
+        # two more kernels of known traffic, to cross-check the copy's factors: a
+        # fill writes n bytes and reads none, a sum reads n bytes and writes a few
+        for _ in range(3):
+            dst.fill_(2)
+        tot = [src.view(torch.float32).sum() for _ in range(3)]
         torch.cuda.synchronize()
-        print(json.dumps({"calibration_copy_bytes": n, "copies": 3}), flush=True)
+        print(json.dumps({"calibration_copy_bytes": n, "copies": 3, "fills": 3, "sums": len(tot)}),
+              flush=True)
         return
     if args.workload.startswith("prefill"):
         res = bench_prefill(args)

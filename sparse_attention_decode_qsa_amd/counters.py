@@ -13,6 +13,12 @@ nothing else) give the scale factor per counter: the bytes the copy must read
 (or write) / what the counter reports for the copy dispatches.  The JSON file
 holds one entry per (key, workload): a figure is valid only for the workload it
 was taken on.
+
+    python -m sparse_attention_decode_qsa_amd.counters --cross-check \
+        --calib-fetch C_FETCH.csv --calib-write C_WRITE.csv --calib-mib 256
+
+prints the factors that the calibration run's fill and sum kernels imply, beside the
+copy's.
 """
 from __future__ import annotations
 
@@ -21,6 +27,7 @@ import csv
 import hashlib
 import json
 import os
+import sys
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,7 +66,37 @@ def src_hash(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def cross_check(fetch_csv: str, write_csv: str, mib: int) -> dict:
+    """Factors implied by the calibration run's other kernels of known traffic: the
+    fill writes mib MiB (reads none), the float32 sum reads mib MiB (writes a few
+    bytes).  They should agree with the copy's."""
+    n = float(mib << 20)
+    out = {}
+    for name, sub, counter, expect in (("fill_write", "FillFunctor", "WRITE_SIZE", n),
+                                       ("fill_fetch", "FillFunctor", "FETCH_SIZE", 0.0),
+                                       ("sum_fetch", "reduce_kernel", "FETCH_SIZE", n),
+                                       ("sum_write", "reduce_kernel", "WRITE_SIZE", 0.0),
+                                       ("copy_fetch", "copyBuffer", "FETCH_SIZE", n),
+                                       ("copy_write", "copyBuffer", "WRITE_SIZE", n)):
+        kib, cnt = mean_kib(fetch_csv if counter == "FETCH_SIZE" else write_csv, counter, sub)
+        e = dict(counter=counter, kib_per_dispatch=round(kib, 1), dispatches=cnt,
+                 expected_bytes=int(expect))
+        if expect:
+            e["factor"] = round(expect / (kib * 1024.0), 4)
+        out[name] = e
+    return out
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--cross-check":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--cross-check", action="store_true")
+        ap.add_argument("--calib-fetch", required=True)
+        ap.add_argument("--calib-write", required=True)
+        ap.add_argument("--calib-mib", type=int, default=256)
+        a = ap.parse_args()
+        print(json.dumps(cross_check(a.calib_fetch, a.calib_write, a.calib_mib), indent=1))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
