@@ -385,6 +385,36 @@ def test_decode_step_cycle(gpu, name, flags):
                           L["k_idx_new"].view(np.uint16))
 
 
+def random_decode_config(seed):
+    """A seeded draw over the configurations the step supports: indexer rows of
+    16..512 sixteen-byte pieces, 1..16 query heads per KV head, head dims 64 or 128,
+    k from 1 to 1,024, contexts from 2 to 24,000 tokens, either gather form."""
+    rng = np.random.default_rng(9000 + seed)
+    d_idx = int(rng.choice([16, 32, 64, 128, 256]))
+    rowc = int(rng.choice([r for r in (16, 32, 64, 128, 256, 512) if r * 8 >= d_idx]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([h for h in (1, 2, 4, 8) if h * G <= 64]))
+    d = int(rng.choice([64, 128]))
+    topk = int(rng.choice([1, 3, 64, 200, 512, 1024]))
+    n_tokens = int(rng.integers(2, 24000))
+    flags = qb.QSA_STEP_FUSED_GATHER if seed % 3 else qb.QSA_STEP_COMPACT_GATHER
+    w = synth.Workload(f"random_{seed}", 500 + seed, "decode", n_tokens, h_idx=rowc * 8 // d_idx,
+                       d_idx=d_idx, topk=topk, hq=hkv * G, hkv=hkv, d=d, dv=d)
+    return w, flags
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_decode_step_random_configs(gpu, seed):
+    # two consecutive steps of a drawn configuration (the second one completes a
+    # block in a quarter of the draws), each against the oracle
+    w, flags = random_decode_config(seed)
+    print(f"config {w}", flush=True)
+    L, cfg, g, o = setup_decode(w)
+    n0 = L["n_prefix"]
+    for step in range(2):
+        check_step(w, L, cfg, g, o, n0 + step, step, flags)
+
+
 def test_decode_step_small_contexts(gpu):
     # nb <= k (full attention), N < 4 (no complete block), k = nb - 1
     for n_tokens, k in [(1, 512), (3, 512), (4, 512), (2049, 512), (2053, 512), (401, 99)]:

@@ -198,6 +198,45 @@ def test_prefill_step_small(gpu):
                           I["v"][depth:].view(np.uint16))
 
 
+def random_prefill_config(seed):
+    """A seeded draw over the configurations a prefill chunk supports: indexer rows
+    of 16..512 sixteen-byte pieces, 1..16 query heads per KV head, head dims 64 or
+    128, k from 1 to 1,024, depths up to 12,000 tokens, chunks of 2..400 rows, and the
+    per-row, grouped-union and union-for-every-group forms."""
+    rng = np.random.default_rng(7000 + seed)
+    d_idx = int(rng.choice([16, 32, 64, 128, 256]))
+    rowc = int(rng.choice([r for r in (16, 32, 64, 128, 256, 512) if r * 8 >= d_idx]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([h for h in (1, 2, 4, 8) if h * G <= 64]))
+    d = int(rng.choice([64, 128]))
+    topk = int(rng.choice([1, 3, 64, 200, 512, 1024]))
+    depth = int(rng.integers(1, 12000))
+    n_q = int(rng.integers(2, 400))
+    flags = (qb.QSA_PREFILL_PER_ROW, UNION, UNION_ALL)[seed % 3]
+    w = synth.Workload(f"random_prefill_{seed}", 600 + seed, "prefill", depth,
+                       h_idx=rowc * 8 // d_idx, d_idx=d_idx, topk=topk, hq=hkv * G, hkv=hkv,
+                       d=d, dv=d, n_q=n_q, q_corr=float(rng.choice([0.0, 0.9])))
+    return w, flags
+
+
+@pytest.mark.parametrize("seed", range(18))
+def test_prefill_step_random_configs(gpu, seed):
+    # a drawn configuration: 24 sampled rows (first, last and 22 seeded) against the
+    # oracle, on the GPU's own pooled rows and the oracle's
+    w, flags = random_prefill_config(seed)
+    print(f"config {w} flags {flags}", flush=True)
+    G = w.hq // w.hkv
+    if flags != qb.QSA_PREFILL_PER_ROW and not (G in (4, 8, 16) and w.d == 128
+                                                 and (128 // G) * w.topk <= 16384):
+        # outside the grouped-union form's shapes the call refuses (status UNSUPPORTED)
+        with pytest.raises(qb.QsaError, match="grouped union"):
+            prefill_case(w, flags=flags)
+        flags = qb.QSA_PREFILL_PER_ROW
+    I, cfg, g, out, scores, blk = prefill_case(w, flags=flags)
+    oracle_pooled = O.pool_rebuild(I["raw"], I["depth"] + w.n_q)
+    check_prefill_rows(w, I, g, out, scores, blk, sample_rows(w.n_q, seed, 24), oracle_pooled)
+
+
 def test_prefill_step_is_decode_per_row(gpu):
     # a chunk row equals a decode step at that length (small chunk, every row)
     w = synth.Workload("prefill_vs_decode", 6, "prefill", 4 * 600 + 2, n_q=9, topk=64)
