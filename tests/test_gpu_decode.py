@@ -733,6 +733,44 @@ def test_decode_multi_equals_sequential_steps(gpu, n_tokens, n_q):
     assert np.array_equal(host(g.k_raw[n0:n0 + n_q]).view(np.uint16), k_idx_new.view(np.uint16))
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_multi_random_configs(gpu, seed):
+    # 2-4 verification rows of a drawn configuration (as for the single step), each
+    # row against the oracle's decode step at its position, in order
+    w, _ = random_decode_config(100 + seed)
+    n_q = 2 + seed % 3
+    print(f"config {w} rows {n_q}", flush=True)
+    L, cfg, g, o = setup_decode(w)
+    n0 = L["n_prefix"]
+    q_idx = synth.normal_f16(90 + seed, (n_q, w.h_idx, w.d_idx))
+    q = synth.normal_f16(120 + seed, (n_q, w.hq, w.d))
+    k_idx_new = synth.normal_f16(150 + seed, (n_q, w.h_idx, w.d_idx))
+    k_new = synth.normal_f16(180 + seed, (n_q, w.hkv, w.d))
+    v_new = synth.normal_f16(210 + seed, (n_q, w.hkv, w.dv))
+    ld = (n0 + n_q) // 4 + 3
+    out = torch.empty((n_q, w.hq, w.dv), device="cuda")
+    scores = torch.full((n_q, ld), 123.0, device="cuda")
+    blk = torch.full((n_q, w.topk), -1, dtype=torch.int32, device="cuda")
+    ws = qb.workspace(cfg, n_q, w.cap_tokens)
+    qb.qsa_decode_multi(cfg, g, n0, dev(q_idx), dev(k_idx_new), dev(q), dev(k_new), dev(v_new),
+                        out, ws, scores_out=scores, ld_scores=ld, blk_out=blk)
+    s_all, b_all, o_all = host(scores), host(blk), host(out)
+    for row in range(n_q):
+        ref = O.decode_step(shape_of(w), o.raw, o.pooled, o.k, o.v, n0 + row, q_idx[row],
+                            k_idx_new[row], q[row], k_new[row], v_new[row])
+        nb = (n0 + row + 1) // 4
+        s_gpu = s_all[row][:nb]
+        if nb:
+            assert np.max(np.abs(s_gpu - ref["scores64"])) <= \
+                SCORE_REL * np.max(np.abs(ref["scores64"])), row
+        b_gpu = b_all[row][:min(w.topk, nb)]
+        assert np.array_equal(b_gpu, O.topk_sort(s_gpu, w.topk)), row
+        ref_out = O.attn_cells(q[row], o.k, o.v, O.cells(b_gpu, n0 + row + 1), w.scale)
+        assert_attn_close(o_all[row], ref_out, f"row {row}")
+    nb = (n0 + n_q) // 4
+    assert_pool_close(host(g.k_pool[:nb]), o.pooled[:nb])
+
+
 def test_decode_multi_255181_planted(gpu):
     # the 256k workload with three rows: every row finds the planted blocks
     w = synth.WORKLOADS["decode_255181"]
