@@ -44,6 +44,7 @@ constexpr int kDim = 128;         // D = DV
 constexpr int KP = kDim + 8;      // K tile pitch (halfs)
 constexpr int VP = kTC + 4;       // V^T tile pitch (halfs)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMax = 8.f;  // log2 headroom of the softmax reference (see below)
 
 struct UnionBuildLds {
     uint32_t bits[kWinWords];
@@ -377,8 +378,13 @@ __global__ __launch_bounds__(kSetThreads * SETS, 3 - SETS) void union_attn_kerne
                 for (int e = 0; e < 4; e++)
                     tmax = fmaxf(tmax, s[mb][e]);
             tmax = max_across_rows(tmax);
-            // scores are scaled inside the exponent: p = 2^(s * sl2 - m)
-            const float mnew = fmaxf(m_run[nb], tmax * sl2);
+            // scores are scaled inside the exponent: p = 2^(s * sl2 - m).  The
+            // reference m moves only when the tile's maximum passes it by more than
+            // kLazyMax (p then stays below 2^kLazyMax; o and l share the reference,
+            // so o / l is unchanged up to rounding), which spares most tiles the
+            // rescale of the outputs
+            const float tm = tmax * sl2;
+            const float mnew = tm > m_run[nb] + kLazyMax ? tm : m_run[nb];
             const float mref = (mnew == -INFINITY) ? 0.f : mnew;
             alpha[nb] = __builtin_amdgcn_exp2f(m_run[nb] - mref);
             rescale |= mnew != m_run[nb];
