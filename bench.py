@@ -341,7 +341,7 @@ def bench_decode(args):
             "avg_launch_us": round(scan_us, 3),
             "timing": f"kernel start/end events of {reps} eager decode steps (qsa_trace_scan)",
             "standalone": {
-                "kernel": f"score_decode_kernel<{rowc},{2 if rowc >= 128 else 4},256,1,false,false>",
+                "kernel": f"score_decode_kernel<{rowc},{2 if rowc >= 128 else 4},512,1,false,false>",
                 "achieved": round(alone_gbps, 1), "frac": round(alone_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_for("score_decode_kernel", "k_score.hip", w.name),
                 "algorithmic_bytes_per_launch": alone_bytes,

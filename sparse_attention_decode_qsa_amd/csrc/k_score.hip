@@ -28,7 +28,7 @@
 namespace qsa {
 namespace {
 
-constexpr int kThreads = 256;   // stand-alone scan
+constexpr int kThreads = 512;   // stand-alone scan: 8 waves per work group
 constexpr int kStepThreads = 512;  // decode-step scan: 8 waves, so one list per 8 waves
 
 // Sum of a row's lane partials: a whole-wave row by DPP within the 16-lane rows
@@ -366,11 +366,12 @@ hipError_t launch_rowc(const h16 *q, int32_t n_q, const h16 *pool, int32_t nb, f
         constexpr int RPW = kWave / LPR;
         constexpr int NW = kThreads / kWave;
         const int64_t groups = ((int64_t)nb + RPW - 1) / RPW;
-        // about 8 row groups per wave, 512 to 2,048 work groups (fewer when there are
-        // fewer row groups than waves): measured at 31,898 to 255,181 tokens, 512
-        // groups beat 2,048 by 1-2% on the short caches and lose 0.5-1% on the long
+        // about 8 row groups per wave, 256 to 1,024 work groups of 8 waves (fewer when
+        // there are fewer row groups than waves): measured at 31,898 to 255,181
+        // tokens, the fewest beat the most by 1-2% on the short caches and lose
+        // 0.5-1% on the long; 8-wave groups beat twice as many 4-wave ones by 1.5-2%
         int64_t grid = (groups + (int64_t)NW * 8 - 1) / ((int64_t)NW * 8);
-        grid = grid > 2048 ? 2048 : (grid < 512 ? 512 : grid);
+        grid = grid > 1024 ? 1024 : (grid < 256 ? 256 : grid);
         const int64_t gmax = (groups + (int64_t)NW - 1) / NW;
         if (grid > gmax)
             grid = gmax;
